@@ -1,0 +1,182 @@
+/*
+ * pda.h - paged split-K decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (vllm-rdna pull request #33, "perf(rocm): FA-RDNA2 decode,
+ * scores on every wave and 4 barriers per tile", section "Purpose"): for
+ * every new query token t of sequence b and every query head h,
+ *
+ *     out[t, h, :] = softmax_j(scale * q[t, h, :] . k_j) . v_j
+ *
+ * over the keys j the token can see. K and V live in fixed-size pages of a
+ * shared pool, reached through the sequence's block-table row; query head h
+ * reads KV head h / G with G = num_q_heads / num_kv_heads (consecutive query
+ * heads share a KV head). A sequence holds seq_lens[b] keys, its q_lens[b]
+ * new tokens included: token i sits at position p = seq_lens[b] - q_lens[b]
+ * + i and sees keys lo..p, with lo = 0, or lo = max(0, p - window + 1) under a
+ * sliding window of `window` keys. A token that sees no key (p < 0) gets an
+ * all-zero row. The behaviours named in the pull request's "Test Plan" (zero
+ * rows, a caller scale written into a caller `out`, sliding window,
+ * multi-token queries, split decode) are part of this contract.
+ *
+ * Work is split along the key axis into `num_splits` contiguous chunks per
+ * (sequence, KV head); each chunk yields a partial (m, l, o) and a second
+ * kernel merges the partials (the split-K combine of the same section).
+ *
+ * Conventions for every entry point
+ *  - All tensors are contiguous, row-major, and live in device memory of the
+ *    current HIP device; the caller owns them. The library never allocates,
+ *    frees or synchronizes, and keeps no device state.
+ *  - Every launch goes on the caller's `stream` (the pull request passes the
+ *    current stream to every launch); calls return after enqueueing.
+ *  - Arguments are validated on the host before any HIP call; a failure
+ *    returns a negative pda_status and sets pda_last_error(). Values that
+ *    live in device memory are a contract, not checked (checking would need
+ *    a synchronization): 0 <= seq_lens[b] <= max_pages_per_seq * page_size;
+ *    1 <= q_lens[b] <= max_q_len; sum(q_lens) == num_tokens; the block-table
+ *    entries of the first ceil(seq_lens[b] / page_size) columns of row b are
+ *    in [0, num_pages). Other table entries, and page slots past a
+ *    sequence's length, are never read and may hold anything (NaN included).
+ */
+#ifndef PDA_H_
+#define PDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pda_status {
+  PDA_OK = 0,
+  PDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PDA_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+  PDA_ERR_ALIGN = -3,       /* a data pointer is not 16-byte aligned */
+  PDA_ERR_UNSUPPORTED = -4, /* valid, but no compiled kernel covers it */
+  PDA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than needed */
+  PDA_ERR_DEVICE = -6       /* the HIP runtime reported an error */
+} pda_status;
+
+/* Element type of the KV cache. fp16 is IEEE binary16. fp8 is OCP E4M3
+ * ("fn": bias 7, no infinities, max 448). int8 is symmetric signed with no
+ * zero point. For fp8 and int8 the value of a code is code_value * scale with
+ * one fp32 scale per KV head for K and one for V (the pull request's fp8 and
+ * int8 decode wrappers, section "Purpose"). */
+typedef enum pda_kv_dtype {
+  PDA_KV_F16 = 0,
+  PDA_KV_FP8_E4M3 = 1,
+  PDA_KV_INT8 = 2
+} pda_kv_dtype;
+
+/* Sizes of one call. */
+typedef struct pda_decode_dims {
+  int32_t batch;             /* B: sequences (0: nothing to do) */
+  int32_t num_tokens;        /* T = sum(q_lens); B when q_lens is NULL */
+  int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;      /* Hkv */
+  int32_t head_dim;          /* D: 128 or 256 */
+  int32_t page_size;         /* P: keys per page; 16 */
+  int32_t num_pages;         /* pages in each of the K and V pools */
+  int32_t max_pages_per_seq; /* columns of block_table */
+  int32_t max_q_len;         /* bound on q_lens[b]; 1 when q_lens is NULL */
+  int32_t kv_dtype;          /* a pda_kv_dtype */
+} pda_decode_dims;
+
+/* Largest (num_q_heads / num_kv_heads) * max_q_len a call accepts. */
+#define PDA_MAX_ROWS 32
+/* Largest number of key splits. */
+#define PDA_MAX_SPLITS 256
+
+/*
+ * Decode attention, written into `out`.
+ *
+ *  q            fp16 [T, Hq, D]; the tokens of sequence b are rows
+ *               off_b .. off_b + q_lens[b] - 1, off_b = sum of q_lens[<b].
+ *  k_cache      [num_pages, P, Hkv, D] of kv_dtype elements (page, slot,
+ *  v_cache      KV head, dim): the cache writer's layout.
+ *  block_table  int32 [B, max_pages_per_seq]: key j of sequence b is slot
+ *               j % P of page block_table[b][j / P].
+ *  seq_lens     int32 [B]: keys held by each sequence, new tokens included.
+ *  q_lens       int32 [B], or NULL: every sequence has one new token.
+ *  scale        multiplier of q.k (fp32), e.g. 1/sqrt(D).
+ *  window       sliding window in keys; <= 0: none.
+ *  num_splits   key splits per (sequence, KV head); 0: chosen by
+ *               pda_decode_resolve_splits; otherwise 1..PDA_MAX_SPLITS.
+ *  out          fp16 [T, Hq, D], fully overwritten.
+ *  k_scale      fp32 [Hkv] for fp8/int8 KV (NULL for fp16).
+ *  v_scale      fp32 [Hkv] for fp8/int8 KV (NULL for fp16).
+ *  workspace    device scratch for the split partials, at least
+ *               pda_decode_workspace_bytes(dims, window, num_splits) bytes,
+ *               16-byte aligned; may be NULL when that size is 0 (one split).
+ *
+ * Launches the decode kernel and, with more than one split, the combine
+ * kernel, both on `stream`.
+ */
+pda_status pda_paged_decode_attention(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+    float scale, int32_t window, int32_t num_splits, void* out,
+    const float* k_scale, const float* v_scale, const pda_decode_dims* dims,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The decode stage alone: writes the per-split partials of every row into
+ * `workspace` (always, also for one split) and launches nothing else.
+ * Arguments as for pda_paged_decode_attention, without `out`; `num_splits`
+ * 0 resolves as there. Partials layout, with S the resolved split count:
+ *
+ *   partial_o  = (float*)workspace                       [T, Hq, S, D]
+ *   partial_ml = (float*)workspace + T * Hq * S * D      [T, Hq, S, 2]
+ *
+ * For split s of row (t, h): m = partial_ml[..., 0] is the largest score of
+ * the split in base-2 units (scale * log2(e) * q.k), l = partial_ml[..., 1]
+ * = sum of 2^(score - m) over the split's visible keys, and partial_o =
+ * sum of 2^(score - m) * v (unnormalized, v dequantized). A split that sees
+ * no key has m = -inf, l = 0, o = 0.
+ */
+pda_status pda_paged_decode_partials(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+    float scale, int32_t window, int32_t num_splits,
+    const float* k_scale, const float* v_scale, const pda_decode_dims* dims,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Split-K combine: out[t, h, :] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+ * with M the largest m_s over splits with l_s > 0; a row whose splits are all
+ * empty is written as zeros. partial_o / partial_ml as laid out above
+ * (num_splits >= 1); out fp16 [T, Hq, D]. One launch on `stream`.
+ */
+pda_status pda_split_combine(const float* partial_o, const float* partial_ml,
+                             void* out, int32_t num_tokens, int32_t num_q_heads,
+                             int32_t head_dim, int32_t num_splits,
+                             hipStream_t stream);
+
+/* Split count a call with these sizes uses: `num_splits` itself when it is
+ * >= 1, otherwise the automatic choice for a device with `num_cus` compute
+ * units (num_cus <= 0: the current device's count). Host-only; no launch.
+ * Returns a value in 1..PDA_MAX_SPLITS, or a negative pda_status. */
+int32_t pda_decode_resolve_splits(const pda_decode_dims* dims, int32_t window,
+                                  int32_t num_splits, int32_t num_cus);
+
+/* Workspace bytes pda_paged_decode_attention needs (0 for one split) with
+ * the split count resolved as above; pda_paged_decode_partials needs
+ * pda_decode_partials_bytes. Host-only. Negative on invalid sizes. */
+int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
+                                   int32_t num_splits);
+int64_t pda_decode_partials_bytes(const pda_decode_dims* dims, int32_t window,
+                                  int32_t num_splits);
+
+/* Message of the calling thread's last non-OK status ("" if none). */
+const char* pda_last_error(void);
+
+/* Library version string. */
+const char* pda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDA_H_ */

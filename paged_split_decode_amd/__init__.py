@@ -1,0 +1,215 @@
+"""Paged split-K decode attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libpda.so`` (declared in
+``include/pda.h``). The functions here only marshal torch tensors into
+pointers and sizes; every step of the computation runs in the library's HIP
+kernels, on the current torch stream. torch supplies device memory and
+streams. There is no fallback: if the library is not built, every call raises.
+
+Build the library with ``python -m paged_split_decode_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "paged_decode_attention", "paged_decode_partials", "split_combine",
+    "resolve_splits", "workspace_bytes", "partials_bytes", "decode_dims",
+    "load_library", "library_path", "KV_DTYPES", "PDA_MAX_ROWS", "PDA_MAX_SPLITS",
+    "PdaError", "partials_views",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpda.so")
+
+KV_DTYPES = {"f16": 0, "fp8_e4m3": 1, "int8": 2}
+PDA_MAX_ROWS = 32
+PDA_MAX_SPLITS = 256
+STATUS = {0: "PDA_OK", -1: "PDA_ERR_NULL", -2: "PDA_ERR_SHAPE", -3: "PDA_ERR_ALIGN",
+          -4: "PDA_ERR_UNSUPPORTED", -5: "PDA_ERR_WORKSPACE", -6: "PDA_ERR_DEVICE"}
+
+
+class PdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_tokens", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
+        "num_pages", "max_pages_per_seq", "max_q_len", "kv_dtype")]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_VP, _I32P = ctypes.c_void_p, ctypes.c_void_p
+_DIMS = ctypes.POINTER(DecodeDims)
+
+_SIGNATURES = {
+    "pda_paged_decode_attention": (ctypes.c_int, [
+        _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+        _VP, _VP, _VP, _DIMS, _VP, ctypes.c_size_t, _VP]),
+    "pda_paged_decode_partials": (ctypes.c_int, [
+        _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+        _VP, _VP, _DIMS, _VP, ctypes.c_size_t, _VP]),
+    "pda_split_combine": (ctypes.c_int, [
+        _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP]),
+    "pda_decode_resolve_splits": (ctypes.c_int32, [_DIMS, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32]),
+    "pda_decode_workspace_bytes": (ctypes.c_int64, [_DIMS, ctypes.c_int32, ctypes.c_int32]),
+    "pda_decode_partials_bytes": (ctypes.c_int64, [_DIMS, ctypes.c_int32, ctypes.c_int32]),
+    "pda_last_error": (ctypes.c_char_p, []),
+    "pda_version": (ctypes.c_char_p, []),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpda.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m paged_split_decode_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PdaError(status, load_library().pda_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _kv_code(k_cache: torch.Tensor, kv_dtype: Optional[str]) -> int:
+    if kv_dtype is None:
+        kv_dtype = {torch.float16: "f16", torch.float8_e4m3fn: "fp8_e4m3",
+                    torch.int8: "int8"}.get(k_cache.dtype)
+        if kv_dtype is None:
+            raise ValueError(f"kv_dtype needed for a {k_cache.dtype} cache")
+    return KV_DTYPES[kv_dtype]
+
+
+def decode_dims(q, k_cache, block_table, seq_lens, q_lens=None, max_q_len=None,
+                kv_dtype=None) -> DecodeDims:
+    """Sizes of one call, read from tensor shapes. ``max_q_len`` defaults to
+    1 without q_lens; with q_lens it must be given (reading q_lens would need
+    a device synchronization)."""
+    T, Hq, D = q.shape
+    num_pages, P, Hkv, Dk = k_cache.shape
+    if q_lens is not None and max_q_len is None:
+        raise ValueError("max_q_len is required when q_lens is given")
+    return DecodeDims(batch=seq_lens.shape[0], num_tokens=T, num_q_heads=Hq,
+                      num_kv_heads=Hkv, head_dim=D, page_size=P, num_pages=num_pages,
+                      max_pages_per_seq=block_table.shape[1],
+                      max_q_len=1 if q_lens is None else int(max_q_len),
+                      kv_dtype=_kv_code(k_cache, kv_dtype))
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("every tensor must be contiguous")
+
+
+def resolve_splits(dims: DecodeDims, window: int = 0, num_splits: int = 0,
+                   num_cus: int = 0) -> int:
+    s = load_library().pda_decode_resolve_splits(ctypes.byref(dims), window, num_splits, num_cus)
+    if s < 0:
+        _check(s)
+    return s
+
+
+def workspace_bytes(dims: DecodeDims, window: int = 0, num_splits: int = 0) -> int:
+    n = load_library().pda_decode_workspace_bytes(ctypes.byref(dims), window, num_splits)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def partials_bytes(dims: DecodeDims, window: int = 0, num_splits: int = 0) -> int:
+    n = load_library().pda_decode_partials_bytes(ctypes.byref(dims), window, num_splits)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
+                           window, num_splits, out, k_scale=None, v_scale=None,
+                           kv_dtype=None, max_q_len=None, workspace=None, stream=None):
+    """out[t, h] = softmax(scale q.K^T) V over each token's visible keys (see
+    include/pda.h). Writes ``out`` (fp16 [T, Hq, D]) and returns None."""
+    lib = load_library()
+    _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, out, k_scale, v_scale)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype)
+    need = workspace_bytes(dims, window, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.pda_paged_decode_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(q_lens), float(scale), int(window), int(num_splits), _ptr(out),
+        _ptr(k_scale), _ptr(v_scale), ctypes.byref(dims), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def paged_decode_partials(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
+                          window, num_splits, workspace, k_scale=None, v_scale=None,
+                          kv_dtype=None, max_q_len=None, stream=None) -> int:
+    """The decode stage alone: writes split partials into ``workspace`` (a
+    float32 or uint8 tensor of at least partials_bytes(...) bytes). Returns
+    the split count used."""
+    lib = load_library()
+    _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, workspace, k_scale, v_scale)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype)
+    S = resolve_splits(dims, window, num_splits)
+    _check(lib.pda_paged_decode_partials(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(q_lens), float(scale), int(window), S, _ptr(k_scale), _ptr(v_scale),
+        ctypes.byref(dims), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return S
+
+
+def split_combine(partial_o, partial_ml, out, num_splits: int, stream=None):
+    """Merge split partials (float32 [T, Hq, S, D] and [T, Hq, S, 2]) into
+    ``out`` (fp16 [T, Hq, D])."""
+    lib = load_library()
+    _contig(partial_o, partial_ml, out)
+    T, Hq, D = out.shape
+    _check(lib.pda_split_combine(_ptr(partial_o), _ptr(partial_ml), _ptr(out), T, Hq, D,
+                                 int(num_splits), _stream(stream)))
+
+
+def partials_views(workspace: torch.Tensor, num_tokens: int, num_q_heads: int,
+                   num_splits: int, head_dim: int):
+    """(partial_o [T, Hq, S, D], partial_ml [T, Hq, S, 2]) float32 views of a
+    workspace written by paged_decode_partials (layout of include/pda.h)."""
+    f = workspace.view(torch.float32) if workspace.dtype != torch.float32 else workspace
+    n_o = num_tokens * num_q_heads * num_splits * head_dim
+    n_ml = num_tokens * num_q_heads * num_splits * 2
+    po = f[:n_o].view(num_tokens, num_q_heads, num_splits, head_dim)
+    pml = f[n_o:n_o + n_ml].view(num_tokens, num_q_heads, num_splits, 2)
+    return po, pml

@@ -1,0 +1,333 @@
+// Host layer of the C ABI declared in include/pda.h: argument validation,
+// split-count policy, launch shape, and the launches themselves on the
+// caller's stream. No allocation, no synchronization, no device state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "pda.h"
+#include "pda_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pda_status fail(pda_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device, queried once per device.
+int device_cu_count() {
+  static std::mutex mu;
+  static int counts[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return -1;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
+int kv_kind(int32_t kv_dtype) {
+  switch (kv_dtype) {
+    case PDA_KV_F16: return pda::kKvF16;
+    case PDA_KV_FP8_E4M3: return pda::kKvFp8;
+    case PDA_KV_INT8: return pda::kKvI8;
+    default: return -1;
+  }
+}
+
+// Launch shape for one call.
+struct Plan {
+  int rows;        // G * max_q_len query rows per (sequence, KV head)
+  int rows_per_wave;
+  int row_groups;
+  int key_waves;
+  int splits;
+  int threads;
+  size_t lds;
+};
+
+pda_status check_dims(const pda_decode_dims* d) {
+  if (!d) return fail(PDA_ERR_NULL, "dims is NULL");
+  if (d->batch < 0 || d->num_tokens < 0)
+    return fail(PDA_ERR_SHAPE, "batch (%d) and num_tokens (%d) must be >= 0", d->batch,
+                d->num_tokens);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads)
+    return fail(PDA_ERR_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->head_dim != 128 && d->head_dim != 256)
+    return fail(PDA_ERR_UNSUPPORTED, "head_dim %d: compiled for 128 and 256", d->head_dim);
+  if (d->page_size != pda::kPageSize)
+    return fail(PDA_ERR_UNSUPPORTED, "page_size %d: compiled for %d", d->page_size,
+                pda::kPageSize);
+  if (d->num_pages <= 0 || d->max_pages_per_seq <= 0)
+    return fail(PDA_ERR_SHAPE, "num_pages (%d) and max_pages_per_seq (%d) must be > 0",
+                d->num_pages, d->max_pages_per_seq);
+  if (d->max_q_len < 1) return fail(PDA_ERR_SHAPE, "max_q_len %d must be >= 1", d->max_q_len);
+  if (kv_kind(d->kv_dtype) < 0)
+    return fail(PDA_ERR_UNSUPPORTED, "kv_dtype %d is not a pda_kv_dtype", d->kv_dtype);
+  const int64_t rows = (int64_t)(d->num_q_heads / d->num_kv_heads) * d->max_q_len;
+  if (rows > PDA_MAX_ROWS)
+    return fail(PDA_ERR_UNSUPPORTED, "(num_q_heads/num_kv_heads)*max_q_len = %lld exceeds %d",
+                (long long)rows, PDA_MAX_ROWS);
+  if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX / 2)
+    return fail(PDA_ERR_SHAPE, "max_pages_per_seq * page_size too large");
+  return PDA_OK;
+}
+
+int auto_splits(const pda_decode_dims* d, int window, int key_waves, int num_cus) {
+  const int uk = pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype));
+  int64_t keys = (int64_t)d->max_pages_per_seq * d->page_size;
+  if (window > 0) keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + uk);
+  const int64_t units = (keys + uk - 1) / uk;
+  const int64_t work = std::max<int64_t>(1, (int64_t)d->batch * d->num_kv_heads);
+  const int64_t target = 2 * (int64_t)num_cus;  // workgroups wanted in flight
+  int64_t s = (target + work - 1) / work;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, units / (2 * key_waves)));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, PDA_MAX_SPLITS));
+}
+
+pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_splits, int num_cus,
+                     Plan* p) {
+  pda_status st = check_dims(d);
+  if (st != PDA_OK) return st;
+  if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
+    return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
+  p->rows = (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
+  const int cap = d->head_dim == 256 ? 6 : pda::kMaxRowsPerWave;
+  p->row_groups = (p->rows + cap - 1) / cap;
+  p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
+  p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
+  if (p->row_groups >= 4) p->key_waves = 1;
+  const int waves = p->row_groups * p->key_waves;
+  p->threads = 64 * waves;
+  p->lds = pda::decode_lds_bytes(waves, p->rows_per_wave, d->head_dim);
+  if (num_splits >= 1) {
+    p->splits = num_splits;
+  } else {
+    if (num_cus <= 0) num_cus = device_cu_count();
+    if (num_cus <= 0) return fail(PDA_ERR_DEVICE, "cannot query the device's compute units");
+    p->splits = auto_splits(d, window, p->key_waves, num_cus);
+  }
+  return PDA_OK;
+}
+
+int64_t partials_bytes(const pda_decode_dims* d, int splits) {
+  return (int64_t)d->num_tokens * d->num_q_heads * splits * (d->head_dim + 2) *
+         (int64_t)sizeof(float);
+}
+
+pda_status check_pointers(const void* q, const void* k, const void* v, const int32_t* bt,
+                          const int32_t* sl, const float* ks, const float* vs,
+                          const pda_decode_dims* d) {
+  if (!q || !k || !v || !bt || !sl)
+    return fail(PDA_ERR_NULL, "q, k_cache, v_cache, block_table and seq_lens must be non-NULL");
+  const bool quant = d->kv_dtype != PDA_KV_F16;
+  if (quant && (!ks || !vs))
+    return fail(PDA_ERR_NULL, "fp8/int8 KV needs k_scale and v_scale");
+  if (!quant && (ks || vs))
+    return fail(PDA_ERR_SHAPE, "k_scale/v_scale must be NULL for fp16 KV");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(PDA_ERR_ALIGN, "q, k_cache and v_cache must be 16-byte aligned");
+  return PDA_OK;
+}
+
+pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArgs& args,
+                         hipStream_t stream) {
+  const dim3 grid(p.splits, d->num_kv_heads, d->batch);
+  hipError_t e;
+  switch (kv_kind(d->kv_dtype)) {
+    case pda::kKvF16:
+      e = pda::launch_decode_f16(d->head_dim, p.rows_per_wave, grid, p.threads, p.lds, stream, args);
+      break;
+    case pda::kKvFp8:
+      e = pda::launch_decode_fp8(d->head_dim, p.rows_per_wave, grid, p.threads, p.lds, stream, args);
+      break;
+    default:
+      e = pda::launch_decode_i8(d->head_dim, p.rows_per_wave, grid, p.threads, p.lds, stream, args);
+      break;
+  }
+  if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+  return PDA_OK;
+}
+
+pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int32_t* bt,
+                          const int32_t* sl, const int32_t* ql, float scale, int32_t window,
+                          const float* ks, const float* vs, const pda_decode_dims* d,
+                          const Plan& p) {
+  pda::DecodeArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.block_table = bt;
+  a.seq_lens = sl;
+  a.q_lens = ql;
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.qk_mult = scale * 1.4426950408889634f;  // scores in base-2 units
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.group = d->num_q_heads / d->num_kv_heads;
+  a.max_pages = d->max_pages_per_seq;
+  a.max_q_len = d->max_q_len;
+  a.window = window;
+  a.num_splits = p.splits;
+  a.row_groups = p.row_groups;
+  a.key_waves = p.key_waves;
+  return a;
+}
+
+pda_status check_q_lens(const int32_t* q_lens, const pda_decode_dims* d) {
+  if (!q_lens && (d->num_tokens != d->batch || d->max_q_len != 1))
+    return fail(PDA_ERR_SHAPE,
+                "without q_lens every sequence has one token: num_tokens (%d) must equal "
+                "batch (%d) and max_q_len (%d) must be 1",
+                d->num_tokens, d->batch, d->max_q_len);
+  if (q_lens && (int64_t)d->num_tokens > (int64_t)d->batch * d->max_q_len)
+    return fail(PDA_ERR_SHAPE, "num_tokens %d exceeds batch * max_q_len", d->num_tokens);
+  return PDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      const int32_t* q_lens, float scale, int32_t window,
+                                      int32_t num_splits, void* out, const float* k_scale,
+                                      const float* v_scale, const pda_decode_dims* dims,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  pda_status st = check_dims(dims);
+  if (st != PDA_OK) return st;
+  if ((st = check_pointers(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, dims)))
+    return st;
+  if (!out) return fail(PDA_ERR_NULL, "out must be non-NULL");
+  if (!aligned16(out)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
+  if ((st = check_q_lens(q_lens, dims))) return st;
+  if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
+    return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
+  if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
+  Plan p;
+  if ((st = make_plan(dims, window, num_splits, 0, &p))) return st;
+  pda::DecodeArgs a = make_args(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
+                                window, k_scale, v_scale, dims, p);
+  if (p.splits == 1) {
+    a.direct = 1;
+    a.out = static_cast<uint16_t*>(out);
+    return launch_decode(p, dims, a, stream);
+  }
+  const int64_t need = partials_bytes(dims, p.splits);
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
+                workspace_bytes, workspace, (long long)need, p.splits);
+  if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  a.direct = 0;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)dims->num_tokens * dims->num_q_heads * p.splits * dims->head_dim;
+  if ((st = launch_decode(p, dims, a, stream))) return st;
+  const hipError_t e = pda::launch_combine(a.part_o, a.part_ml, static_cast<uint16_t*>(out),
+                                           dims->num_tokens * dims->num_q_heads,
+                                           dims->head_dim, p.splits, stream);
+  if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "combine launch: %s", hipGetErrorString(e));
+  return PDA_OK;
+}
+
+pda_status pda_paged_decode_partials(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const int32_t* q_lens, float scale, int32_t window,
+                                     int32_t num_splits, const float* k_scale,
+                                     const float* v_scale, const pda_decode_dims* dims,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  pda_status st = check_dims(dims);
+  if (st != PDA_OK) return st;
+  if ((st = check_pointers(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, dims)))
+    return st;
+  if ((st = check_q_lens(q_lens, dims))) return st;
+  if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
+    return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
+  if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
+  Plan p;
+  if ((st = make_plan(dims, window, num_splits, 0, &p))) return st;
+  const int64_t need = partials_bytes(dims, p.splits);
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
+                workspace_bytes, workspace, (long long)need, p.splits);
+  if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  pda::DecodeArgs a = make_args(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
+                                window, k_scale, v_scale, dims, p);
+  a.direct = 0;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)dims->num_tokens * dims->num_q_heads * p.splits * dims->head_dim;
+  return launch_decode(p, dims, a, stream);
+}
+
+pda_status pda_split_combine(const float* partial_o, const float* partial_ml, void* out,
+                             int32_t num_tokens, int32_t num_q_heads, int32_t head_dim,
+                             int32_t num_splits, hipStream_t stream) {
+  if (!partial_o || !partial_ml || !out)
+    return fail(PDA_ERR_NULL, "partial_o, partial_ml and out must be non-NULL");
+  if (num_tokens < 0 || num_q_heads <= 0)
+    return fail(PDA_ERR_SHAPE, "num_tokens %d / num_q_heads %d", num_tokens, num_q_heads);
+  if (head_dim != 128 && head_dim != 256)
+    return fail(PDA_ERR_UNSUPPORTED, "head_dim %d: compiled for 128 and 256", head_dim);
+  if (num_splits < 1 || num_splits > PDA_MAX_SPLITS)
+    return fail(PDA_ERR_SHAPE, "num_splits %d outside 1..%d", num_splits, PDA_MAX_SPLITS);
+  if (!aligned16(partial_o) || !aligned16(out))
+    return fail(PDA_ERR_ALIGN, "partial_o and out must be 16-byte aligned");
+  if (num_tokens == 0) return PDA_OK;
+  const int64_t rows = (int64_t)num_tokens * num_q_heads;
+  if (rows > INT32_MAX) return fail(PDA_ERR_SHAPE, "num_tokens * num_q_heads too large");
+  const hipError_t e = pda::launch_combine(partial_o, partial_ml, static_cast<uint16_t*>(out),
+                                           (int)rows, head_dim, num_splits, stream);
+  if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "combine launch: %s", hipGetErrorString(e));
+  return PDA_OK;
+}
+
+int32_t pda_decode_resolve_splits(const pda_decode_dims* dims, int32_t window,
+                                  int32_t num_splits, int32_t num_cus) {
+  Plan p;
+  const pda_status st = make_plan(dims, window, num_splits, num_cus, &p);
+  return st == PDA_OK ? p.splits : st;
+}
+
+int64_t pda_decode_partials_bytes(const pda_decode_dims* dims, int32_t window,
+                                  int32_t num_splits) {
+  Plan p;
+  const pda_status st = make_plan(dims, window, num_splits, 0, &p);
+  return st == PDA_OK ? partials_bytes(dims, p.splits) : st;
+}
+
+int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
+                                   int32_t num_splits) {
+  Plan p;
+  const pda_status st = make_plan(dims, window, num_splits, 0, &p);
+  if (st != PDA_OK) return st;
+  return p.splits == 1 ? 0 : partials_bytes(dims, p.splits);
+}
+
+const char* pda_last_error(void) { return g_last_error.c_str(); }
+
+const char* pda_version(void) { return "pda 0.1.0 gfx950"; }
+
+}  // extern "C"

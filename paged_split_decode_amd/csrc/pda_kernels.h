@@ -1,0 +1,73 @@
+// Internal interface between the host layer (pda_api.hip) and the gfx950
+// kernels (pda_decode_*.hip, pda_combine.hip). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pda {
+
+enum KvKind : int { kKvF16 = 0, kKvFp8 = 1, kKvI8 = 2 };
+
+constexpr int kPageSize = 16;     // keys per page (the only compiled size)
+constexpr int kLanesPerKey = 16;  // lanes sharing one key row in a wave
+constexpr int kMaxRowsPerWave = 8;
+
+// Keys one pipeline unit of a wave covers: 4 keys per wave instruction
+// (64 lanes / 16 lanes per key) times the key iterations per unit. A unit
+// keeps at most 32 dwords of K+V per lane in flight.
+constexpr int key_iters(int head_dim, int kv_kind) {
+  return (kv_kind == kKvF16 && head_dim == 256) ? 2 : 4;
+}
+constexpr int unit_keys(int head_dim, int kv_kind) {
+  return 4 * key_iters(head_dim, kv_kind);
+}
+
+struct DecodeArgs {
+  const uint8_t* q;       // fp16 [T, Hq, D]
+  const uint8_t* k;       // [num_pages, P, Hkv, D] elements
+  const uint8_t* v;
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* seq_lens;     // [B]
+  const int32_t* q_lens;       // [B] or nullptr
+  const float* k_scale;        // [Hkv] or nullptr
+  const float* v_scale;        // [Hkv] or nullptr
+  uint16_t* out;               // fp16 [T, Hq, D] (direct mode)
+  float* part_o;               // [T, Hq, S, D]   (partials mode)
+  float* part_ml;              // [T, Hq, S, 2]
+  float qk_mult;               // scale * log2(e)
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;               // G = Hq / Hkv
+  int32_t max_pages;
+  int32_t max_q_len;
+  int32_t window;
+  int32_t num_splits;
+  int32_t row_groups;          // waves of a workgroup sharing keys, split by rows
+  int32_t key_waves;           // waves of a workgroup splitting the key range
+  int32_t direct;              // 1: write out (one split); 0: write partials
+};
+
+// Launch the decode kernel for (head_dim, kv_kind, rows_per_wave) with
+// grid (num_splits, Hkv, B) and row_groups * key_waves waves per workgroup.
+// Returns hipErrorInvalidValue when no instantiation covers the request.
+hipError_t launch_decode_f16(int head_dim, int rows_per_wave, dim3 grid,
+                             int threads, size_t lds, hipStream_t stream,
+                             const DecodeArgs& args);
+hipError_t launch_decode_fp8(int head_dim, int rows_per_wave, dim3 grid,
+                             int threads, size_t lds, hipStream_t stream,
+                             const DecodeArgs& args);
+hipError_t launch_decode_i8(int head_dim, int rows_per_wave, dim3 grid,
+                            int threads, size_t lds, hipStream_t stream,
+                            const DecodeArgs& args);
+
+// Bytes of dynamic LDS the decode kernel needs for the final merge.
+inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
+  return (size_t)waves * rows_per_wave * (head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_combine(const float* part_o, const float* part_ml,
+                          uint16_t* out, int rows, int head_dim, int num_splits,
+                          hipStream_t stream);
+
+}  // namespace pda

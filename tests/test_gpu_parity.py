@@ -1,0 +1,314 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: max |gpu - oracle| <= 2e-3 for fp16 KV and <= 2e-2 against the
+dequantized-KV oracle for fp8-e4m3 / int8 KV. Rows that see no key must be
+exactly zero; every output must be finite. Cases mirror the decode cells the
+pages list (writer layout, empty rows, custom scale into out, sliding window,
+multi-token queries, split decode) plus page-permutation and uniform-V
+bit-exactness, and the benchmark workloads at full size on sampled
+(sequence, KV head) units.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_split_decode_amd as pda
+from synth import WORKLOADS, Workload, make_case, unit_subcase
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {"f16": 2e-3, "fp8_e4m3": 2e-2, "int8": 2e-2}
+
+
+def run_gpu(case, num_splits=None, scale=None, window=None, out=None, use_q_lens=True):
+    T, Hq, D = case.q.shape
+    if out is None:
+        out = torch.full((T, Hq, D), float("nan"), dtype=torch.float16, device=DEV)
+    ql = case.q_lens if use_q_lens else None
+    pda.paged_decode_attention(
+        case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens, ql,
+        case.scale if scale is None else scale,
+        case.window if window is None else window,
+        case.workload.num_splits if num_splits is None else num_splits, out,
+        k_scale=case.k_scale, v_scale=case.v_scale, kv_dtype=case.kv_dtype,
+        max_q_len=case.max_q_len if use_q_lens else None)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_full(case, **over):
+    h = case.host()
+    h.update(over)
+    return oracle.paged_decode_attention(**h)
+
+
+def assert_parity(got, want, kv, what=""):
+    g = got.detach().cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    zero_rows = np.all(want == 0, axis=-1)
+    assert np.all(g[zero_rows] == 0), f"{what}: rows that see no key are not zero"
+    err = np.abs(g - want).max() if g.size else 0.0
+    assert err <= TOL[kv], f"{what}: max |err| {err:.3g} > {TOL[kv]}"
+    return err
+
+
+def case_on_gpu(w):
+    return make_case(w, device=DEV)
+
+
+def small(seed, **kw):
+    base = dict(name="small", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                seq_lens=(1, 77, 300), seed=seed, pool_pages=48)
+    base.update(kw)
+    base["batch"] = len(base["seq_lens"])
+    return Workload(**base)
+
+
+# ---------------------------------------------------------------------------
+# The tiny workload and small random cases (full comparison)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_tiny_workload(splits):
+    c = case_on_gpu(WORKLOADS["tiny_d128"])
+    assert_parity(run_gpu(c, num_splits=splits), oracle_full(c), "f16", f"tiny S={splits}")
+
+
+def _random_case(seed):
+    r = np.random.default_rng(500 + seed)
+    D = int(r.choice([128, 256]))
+    kv = str(r.choice(["f16", "fp8_e4m3", "int8"]))
+    Hkv = int(r.choice([1, 2, 4]))
+    Q = int(r.choice([1, 1, 2, 3, 4]))
+    max_g = max(1, 32 // Q)
+    G = int(r.choice([g for g in (1, 2, 3, 4, 5, 6, 7, 8) if g <= max_g]))
+    B = int(r.integers(1, 5))
+    lens = tuple(int(x) for x in r.integers(0, 700, size=B))
+    W = int(r.choice([0, 0, 1, 17, 100, 5000]))
+    S = int(r.choice([0, 1, 2, 3, 5, 8, 32]))
+    return Workload("rand", batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                    kv_dtype=kv, q_len=Q, seq_lens=lens, window=W, num_splits=S,
+                    seed=seed, table_pad=int(r.integers(0, 3)))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_small_cases(seed):
+    w = _random_case(seed)
+    c = case_on_gpu(w)
+    assert_parity(run_gpu(c), oracle_full(c), w.kv_dtype, repr(w))
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("G,Q", [(1, 1), (4, 1), (6, 1), (8, 1), (7, 3), (8, 4), (5, 2)])
+def test_head_dims_dtypes_groups(kv, D, G, Q):
+    w = small(11, head_dim=D, kv_dtype=kv, num_q_heads=2 * G, num_kv_heads=2, q_len=Q,
+              num_splits=3)
+    c = case_on_gpu(w)
+    assert_parity(run_gpu(c), oracle_full(c), kv, repr(w))
+
+
+# ---------------------------------------------------------------------------
+# The pages' decode cells
+# ---------------------------------------------------------------------------
+
+
+def test_writer_layout_identity_and_permuted_tables():
+    # The kernel reads [page, slot, KV head, dim] pages through the table,
+    # whether the table is an identity (dense layout) or a permutation.
+    w = small(12, seq_lens=(64, 160), pool_pages=0, table_pad=0)
+    c = case_on_gpu(w)
+    want = oracle_full(c)
+    assert_parity(run_gpu(c), want, "f16", "permuted")
+    n = c.k_cache.shape[0]
+    bt = c.block_table.long()
+    order = torch.cat([bt[0, :4], bt[1, :10]])
+    rest = torch.tensor([p for p in range(n) if p not in set(order.tolist())], device=DEV)
+    order = torch.cat([order, rest])
+    c.k_cache = c.k_cache[order].contiguous()
+    c.v_cache = c.v_cache[order].contiguous()
+    c.block_table = torch.tensor([[0, 1, 2, 3] + [n - 1] * 6, list(range(4, 14))],
+                                 dtype=torch.int32, device=DEV)
+    assert_parity(run_gpu(c), want, "f16", "identity table")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_empty_rows_are_zero(D):
+    w = small(13, head_dim=D, q_len=3, seq_lens=(0, 2, 1, 40, 0), num_splits=4)
+    c = case_on_gpu(w)
+    got = run_gpu(c)
+    want = oracle_full(c)
+    assert_parity(got, want, "f16", "empty rows")
+    g = got.cpu().numpy()
+    # L=0: rows 0-2; L=2, q_len 3: row 3; L=1: rows 6-7 (row 8 sees key 0); L=0: rows 12-14
+    for t in (0, 1, 2, 3, 6, 7, 12, 13, 14):
+        assert np.all(g[t] == 0), t
+    assert np.any(g[8] != 0)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_custom_scale_into_out(splits):
+    c = case_on_gpu(small(14, num_splits=splits))
+    out = torch.full(tuple(c.q.shape), float("nan"), dtype=torch.float16, device=DEV)
+    got = run_gpu(c, scale=0.37, out=out)
+    assert got.data_ptr() == out.data_ptr()
+    assert_parity(out, oracle_full(c, scale=0.37), "f16", "scale 0.37")
+
+
+@pytest.mark.parametrize("W", [1, 2, 15, 16, 17, 64, 299, 300, 10000])
+@pytest.mark.parametrize("Q", [1, 3])
+def test_decode_paged_sliding_window(W, Q):
+    c = case_on_gpu(small(15, window=W, q_len=Q, num_q_heads=4, num_splits=0))
+    assert_parity(run_gpu(c), oracle_full(c), "f16", f"W={W} Q={Q}")
+
+
+@pytest.mark.parametrize("Q", [2, 3, 4])
+@pytest.mark.parametrize("D", [128, 256])
+def test_decode_multi_token_queries(Q, D):
+    c = case_on_gpu(small(16, q_len=Q, head_dim=D, seq_lens=(3, 50, 257, 2), num_splits=2))
+    assert_parity(run_gpu(c), oracle_full(c), "f16", f"Q={Q} D={D}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "int8"])
+def test_forward_split_decode_counts_agree(kv):
+    c = case_on_gpu(small(17, kv_dtype=kv, seq_lens=(5, 123, 700, 0), q_len=2, window=250))
+    want = oracle_full(c)
+    outs = {}
+    for S in (1, 2, 3, 8, 0, 64, 256):
+        outs[S] = run_gpu(c, num_splits=S)
+        assert_parity(outs[S], want, kv, f"S={S}")
+    base = outs[1].float()
+    for S, o in outs.items():
+        assert (o.float() - base).abs().max().item() <= 2 * TOL[kv]
+
+
+def test_page_permutation_is_bit_exact_on_gpu():
+    c = case_on_gpu(small(18, seq_lens=(40, 333), q_len=2, num_splits=3))
+    base = run_gpu(c).clone()
+    n = c.k_cache.shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(5)).to(DEV)
+    k2 = torch.empty_like(c.k_cache)
+    v2 = torch.empty_like(c.v_cache)
+    k2[perm] = c.k_cache
+    v2[perm] = c.v_cache
+    c.k_cache, c.v_cache = k2, v2
+    c.block_table = perm[c.block_table.long()].to(torch.int32)
+    got = run_gpu(c)
+    assert torch.equal(got.view(torch.int16), base.view(torch.int16))
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_uniform_v_returns_v_bit_exact(splits):
+    c = case_on_gpu(small(19, seq_lens=(9, 300), num_splits=splits))
+    c.v_cache = torch.full_like(c.v_cache, 0.7)
+    got = run_gpu(c)
+    assert torch.all(got == torch.tensor(0.7, dtype=torch.float16)).item()
+
+
+def test_q_lens_null_equals_ones():
+    c = case_on_gpu(small(20, num_splits=2))
+    a = run_gpu(c, use_q_lens=False)
+    b = run_gpu(c, use_q_lens=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+def test_partials_then_combine_equals_attention(kv):
+    c = case_on_gpu(small(21, kv_dtype=kv, q_len=2, seq_lens=(0, 90, 500), num_splits=6))
+    ref = run_gpu(c)
+    dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
+                           c.max_q_len, kv)
+    nbytes = pda.partials_bytes(dims, c.window, 6)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+    S = pda.paged_decode_partials(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                  c.q_lens, c.scale, c.window, 6, ws, c.k_scale, c.v_scale,
+                                  kv_dtype=kv, max_q_len=c.max_q_len)
+    T, Hq, D = c.q.shape
+    po, pml = pda.partials_views(ws, T, Hq, S, D)
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float16, device=DEV)
+    pda.split_combine(po, pml, out, S)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    # the partials themselves combine, in the oracle, to the oracle's answer
+    mixed = oracle.split_combine(po.cpu().numpy(), pml[..., 0].cpu().numpy(),
+                                 pml[..., 1].cpu().numpy(), base=2.0)
+    assert_parity(torch.from_numpy(mixed), oracle_full(c), kv, "oracle-combined partials")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("S", [1, 2, 7, 64])
+def test_split_combine_vs_oracle(D, S):
+    g = torch.Generator(device=DEV).manual_seed(S * D)
+    T, Hq = 5, 3
+    m = torch.randn(T, Hq, S, generator=g, device=DEV) * 4
+    l = torch.rand(T, Hq, S, generator=g, device=DEV) * 3 + 0.1
+    # o_s = l_s * (a softmax-weighted mean of N(0,1) values), as a split writes it
+    po = l[..., None] * torch.randn(T, Hq, S, D, generator=g, device=DEV)
+    empty = torch.rand(T, Hq, S, generator=g, device=DEV) < 0.3
+    empty[0, 0] = True  # a row with every split empty
+    m[empty] = float("-inf")
+    l[empty] = 0.0
+    po[empty] = float("nan")  # never read
+    pml = torch.stack([m, l], dim=-1).contiguous()
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float16, device=DEV)
+    pda.split_combine(po, pml, out, S)
+    torch.cuda.synchronize()
+    want = oracle.split_combine(po.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy(), base=2.0)
+    assert np.all(out[0, 0].cpu().numpy() == 0)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+    assert err <= 2e-3, err
+
+
+# ---------------------------------------------------------------------------
+# Benchmark workloads at full size, in the bench's launch configuration
+# ---------------------------------------------------------------------------
+
+
+def sampled_parity(c, units):
+    got = run_gpu(c)
+    assert torch.isfinite(got.float()).all()
+    G = c.q.shape[1] // c.k_cache.shape[2]
+    worst = 0.0
+    for b, g in units:
+        sub = unit_subcase(c, b, g)
+        want = oracle.paged_decode_attention(**sub)  # [Q, G, D]
+        off = int(c.q_lens_host[:b].sum())
+        Q = int(c.q_lens_host[b])
+        part = got[off:off + Q, g * G:(g + 1) * G]
+        worst = max(worst, assert_parity(part, want, c.kv_dtype, f"unit ({b},{g})"))
+    return got, worst
+
+
+def test_full_gqa4_d128_b8_l4096():
+    c = case_on_gpu(WORKLOADS["gqa4_d128_b8_l4096"])
+    got = run_gpu(c)
+    assert_parity(got, oracle_full(c), "f16", "gqa4 full")
+
+
+@pytest.mark.parametrize("window", [0, 4096])
+@pytest.mark.parametrize("B", [1, 2, 3, 8, 32])
+def test_full_gqa6_d256_l16384(B, window):
+    w = WORKLOADS["gqa6_d256_l16384"].with_(batch=B, window=window)
+    c = case_on_gpu(w)
+    units = sorted({(0, 0), (B - 1, 3), (B // 2, 1)})
+    sampled_parity(c, units)
+
+
+def test_full_verify_q3_d128_b32():
+    c = case_on_gpu(WORKLOADS["verify_q3_d128_b32"])
+    lens = c.seq_lens_host
+    zero = int(np.flatnonzero(lens == 0)[0])
+    units = [(int(np.argmax(lens)), 0), (zero, 1), (int(np.argmin(np.where(lens > 0, lens,
+                                                                             1 << 30))), 3),
+             (7, 2)]
+    sampled_parity(c, units)
+
+
+@pytest.mark.parametrize("name", ["quant_fp8_d256_b64_l32768", "quant_int8_d256_b64_l32768"])
+def test_full_quantized_d256_b64_l32768(name):
+    c = case_on_gpu(WORKLOADS[name])
+    sampled_parity(c, [(0, 0), (63, 3), (31, 2)])
