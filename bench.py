@@ -1,0 +1,313 @@
+"""Benchmark: paged split-K decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path (decode kernel + split combine) over
+one batch of synthetic input already resident in HBM. The headline workload
+is the fp16-KV D=128 case: 8 sequences of 4096 keys, 32 query heads over 8
+KV heads, page size 16, seeded random page permutation, automatic splits.
+Its KV pool (134 MB) fits in the 256 MiB Infinity Cache, so the timed loop
+rotates over enough replicas of the inputs (>= 1 GiB in total) that every step
+reads its KV from HBM.
+
+Reported (one JSON line):
+  value        algorithmic bytes (every visible K/V element once, q, out) per
+               step / measured step time, GB/s
+  roofline     the decode kernel alone: same bytes / its average launch
+               duration measured with HIP events on the launch stream, against
+               the 8 TB/s HBM peak; traffic = HBM bytes per launch from
+               rocprofv3 FETCH_SIZE + WRITE_SIZE counters when a counter
+               summary for the current kernel sources exists, else null
+  cpu_baseline the fp64 oracle on this host's cores, on a bounded sample of
+               the same workload
+  cells        the same measurement for the D=256 and other workloads
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+METRIC = "decode-attn achieved HBM GB/s (fraction of peak) + us/call, D=128 & D=256"
+HEADLINE = "gqa4_d128_b8_l4096"
+CELLS = [
+    ("gqa6_d256_l16384", dict(batch=8)),
+    ("gqa6_d256_l16384", dict(batch=32)),
+    ("gqa6_d256_l16384", dict(batch=32, window=4096)),
+    ("gqa6_d256_l16384", dict(batch=1)),
+    ("verify_q3_d128_b32", {}),
+    ("quant_fp8_d256_b64_l32768", {}),
+    ("quant_int8_d256_b64_l32768", {}),
+]
+KERNEL_SOURCES = ["pda_decode_impl.h", "pda_kernels.h", "pda_combine.hip", "pda_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_split_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per decode launch from a committed rocprofv3 counter summary
+    of the current kernel sources (profiles/traffic_<workload>.json), else
+    None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Runner:
+    """Pre-marshalled C-ABI calls for one case (no per-step Python work
+    beyond the ctypes call)."""
+
+    def __init__(self, case, device, replicas: int, num_splits: int):
+        import torch
+
+        import paged_split_decode_amd as pda
+
+        self.pda = pda
+        self.lib = pda.load_library()
+        self.case = case
+        c = case
+        self.dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
+                                    c.max_q_len, c.kv_dtype)
+        self.S = pda.resolve_splits(self.dims, c.window, num_splits)
+        T, Hq, D = c.q.shape
+        self.T, self.Hq, self.D = T, Hq, D
+        self.out = torch.empty((T, Hq, D), dtype=torch.float16, device=device)
+        nbytes = pda.partials_bytes(self.dims, c.window, self.S)
+        self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+        self.po, self.pml = pda.partials_views(self.ws, T, Hq, self.S, D)
+        # Replicas of everything a step reads, so consecutive steps do not
+        # hit in the Infinity Cache.
+        self.reps = [(c.q, c.k_cache, c.v_cache)]
+        for _ in range(replicas - 1):
+            self.reps.append((c.q.clone(), c.k_cache.clone(), c.v_cache.clone()))
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = ctypes.c_void_p
+        self.common = (P(c.block_table.data_ptr()), P(c.seq_lens.data_ptr()),
+                       P(c.q_lens.data_ptr()), ctypes.c_float(c.scale),
+                       ctypes.c_int32(c.window), ctypes.c_int32(self.S))
+        self.scales = (None if c.k_scale is None else P(c.k_scale.data_ptr()),
+                       None if c.v_scale is None else P(c.v_scale.data_ptr()))
+        self.dims_ref = ctypes.byref(self.dims)
+        self.ws_ptr, self.ws_bytes = P(self.ws.data_ptr()), nbytes
+        self.po_ptr, self.pml_ptr = P(self.po.data_ptr()), P(self.pml.data_ptr())
+        self.out_ptr = P(self.out.data_ptr())
+        self.rep_ptrs = [tuple(P(t.data_ptr()) for t in r) for r in self.reps]
+
+    def decode(self, i: int):
+        q, k, v = self.rep_ptrs[i % len(self.rep_ptrs)]
+        if self.S == 1:
+            st = self.lib.pda_paged_decode_attention(
+                q, k, v, *self.common, self.out_ptr, *self.scales, self.dims_ref, None, 0,
+                self.stream)
+        else:
+            st = self.lib.pda_paged_decode_partials(
+                q, k, v, *self.common, *self.scales, self.dims_ref, self.ws_ptr,
+                self.ws_bytes, self.stream)
+        if st != 0:
+            raise RuntimeError(self.lib.pda_last_error().decode())
+
+    def combine(self):
+        if self.S == 1:
+            return
+        st = self.lib.pda_split_combine(self.po_ptr, self.pml_ptr, self.out_ptr, self.T,
+                                        self.Hq, self.D, self.S, self.stream)
+        if st != 0:
+            raise RuntimeError(self.lib.pda_last_error().decode())
+
+
+def _hold_gpu():
+    """Keep the GPU busy for a few ms so that the timed launches that follow
+    are all queued before the first one runs (they then run back to back,
+    as a captured graph would)."""
+    import torch
+
+    torch.cuda._sleep(50_000_000)
+
+
+def measure(case, steps: int, warmup: int, num_splits: int, device):
+    """Time `steps` passes. Returns step time (device, launches queued ahead),
+    eager step time (launches paced by the host), and the decode kernel's
+    average launch duration from HIP events around each launch."""
+    import torch
+
+    from synth import algorithmic_bytes
+
+    nbytes = algorithmic_bytes(case)
+    pool = case.k_cache.numel() * case.k_cache.element_size() * 2
+    replicas = max(1, min(16, math.ceil((1 << 30) / max(pool, 1))))
+    r = Runner(case, device, replicas, num_splits)
+    for i in range(warmup):
+        r.decode(i)
+        r.combine()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    # Whole steps (decode + combine), queued ahead of the device.
+    _hold_gpu()
+    t0.record()
+    for i in range(steps):
+        r.decode(i)
+        r.combine()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # The same, paced by the host (no queue-ahead).
+    t0.record()
+    for i in range(steps):
+        r.decode(i)
+        r.combine()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_eager = t0.elapsed_time(t1) / steps
+
+    # The decode kernel alone, each launch bracketed by events on its stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    _hold_gpu()
+    for i in range(steps):
+        ev[i][0].record()
+        r.decode(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    dec = sorted(a.elapsed_time(b) for a, b in ev)
+    decode_ms = sum(dec) / len(dec)
+    return dict(ms_per_step=ms_step, ms_eager=ms_eager, decode_ms=decode_ms,
+                decode_ms_median=dec[len(dec) // 2], bytes=nbytes, splits=r.S,
+                replicas=replicas)
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The fp64 oracle on this host, on whole (sequence, KV head) units of the
+    same workload, repeated until about `budget_s` seconds of work."""
+    import numpy as np
+
+    import oracle
+    from synth import algorithmic_bytes
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    h = case.host()
+    nbytes = algorithmic_bytes(case)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_decode_attention(**h)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    np.asarray(0)
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the whole {case.workload.name} workload (all {len(h['seq_lens'])} "
+                      f"sequences x {h['k_cache'].shape[2]} KV heads), {reps} pass(es) in "
+                      f"{el:.1f} s"}
+
+
+def cell_record(name, w, m):
+    us = m["ms_per_step"] * 1e3
+    gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
+    dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
+    return {"workload": name, "batch": w.batch, "window": w.window, "kv_dtype": w.kv_dtype,
+            "head_dim": w.head_dim, "splits": m["splits"], "us_per_call": round(us, 2),
+            "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
+            "decode_us": round(m["decode_ms"] * 1e3, 2), "decode_GB_s": round(dec_gbs, 1),
+            "algorithmic_bytes": m["bytes"]}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cells", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this operator runs on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from synth import WORKLOADS, make_case
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    case = make_case(w, device=device)
+    m = measure(case, args.steps, args.warmup, w.num_splits, device)
+    gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
+    dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
+    traffic = traffic_for(args.workload)
+    rec = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "seq_len": w.seq_len,
+                   "q_len": w.q_len, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "page_size": w.page_size, "kv_dtype": w.kv_dtype, "num_splits": m["splits"],
+                   "us_per_call": round(m["ms_per_step"] * 1e3, 2),
+                   "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
+                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                   "algorithmic_bytes": m["bytes"], "input_replicas": m["replicas"],
+                   "accumulate": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "pda_decode_kernel",
+                     "decode_us": round(m["decode_ms"] * 1e3, 3),
+                     "decode_us_median": round(m["decode_ms_median"] * 1e3, 3)},
+    }
+    if not args.no_cells:
+        cells = []
+        del case
+        torch.cuda.empty_cache()
+        for name, over in CELLS:
+            wc = WORKLOADS[name].with_(**over)
+            c = make_case(wc, device=device)
+            mc = measure(c, max(10, args.steps // 4), 3, wc.num_splits, device)
+            cells.append(cell_record(name, wc, mc))
+            print(json.dumps({"cell": cells[-1]}), file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+        rec["cells"] = cells
+        case = make_case(w, device=device)
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(case)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -99,7 +99,7 @@ int auto_splits(const pda_decode_dims* d, int window, int key_waves, int num_cus
   if (window > 0) keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + uk);
   const int64_t units = (keys + uk - 1) / uk;
   const int64_t work = std::max<int64_t>(1, (int64_t)d->batch * d->num_kv_heads);
-  const int64_t target = 2 * (int64_t)num_cus;  // workgroups wanted in flight
+  const int64_t target = (int64_t)num_cus;  // about one workgroup per compute unit
   int64_t s = (target + work - 1) / work;
   s = std::min<int64_t>(s, std::max<int64_t>(1, units / (2 * key_waves)));
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, PDA_MAX_SPLITS));
@@ -112,7 +112,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
     return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
   p->rows = (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
-  const int cap = d->head_dim == 256 ? 6 : pda::kMaxRowsPerWave;
+  const int cap = d->head_dim == 256 ? 4 : pda::kMaxRowsPerWave;
   p->row_groups = (p->rows + cap - 1) / cap;
   p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
   p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
@@ -179,7 +179,7 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.v = static_cast<const uint8_t*>(v);
   a.block_table = bt;
   a.seq_lens = sl;
-  a.q_lens = ql;
+  a.q_lens = d->max_q_len == 1 ? nullptr : ql;  // every q_len is 1: offsets are b
   a.k_scale = ks;
   a.v_scale = vs;
   a.qk_mult = scale * 1.4426950408889634f;  // scores in base-2 units

@@ -62,6 +62,12 @@ struct Geom {
 };
 
 // Global dim of lane-local element e for the lane at key-chunk c.
+// Units of K+V kept in flight per wave (registers: 32 dwords per unit, 16
+// for 1-byte KV at D=128).
+constexpr int pipeline_stages(int D, int KV, int RW) {
+  return (D == 128 && RW <= 4) ? 3 : 2;
+}
+
 template <int D, int KV>
 __device__ __forceinline__ int dim_of(int c, int e) {
   if constexpr (KV == kKvF16 && D == 256) {
@@ -147,22 +153,29 @@ __device__ __forceinline__ void to_pairs(const uint32_t (&raw)[NR], h2_t (&out)[
   }
 }
 
-// Load this lane's slice of one key row (K or V) from `row`.
+// Byte offset of this lane's first 16-byte (8-byte for 1-byte KV at D=128)
+// piece within a key row; fp16 at D=256 has a second piece 256 bytes later.
+template <int D, int KV>
+__device__ __forceinline__ uint32_t lane_piece_offset(int c) {
+  return (uint32_t)(Geom<D, KV>::kLaneBytes == 8 ? 8 * c : 16 * c);
+}
+
+// Load this lane's slice of one key row (K or V); `p` points at its first piece.
 template <int D, int KV, int N>
-__device__ __forceinline__ void load_slice(uint32_t (&dst)[N], const uint8_t* row, int c) {
+__device__ __forceinline__ void load_slice(uint32_t (&dst)[N], const uint8_t* p) {
   using Gm = Geom<D, KV>;
   static_assert(N == Gm::kRawDwords, "slice size");
   if constexpr (Gm::kLaneBytes == 32) {  // fp16, D=256: two 256-byte halves
-    const u32x4 a = *reinterpret_cast<const u32x4*>(row + 16 * c);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(row + 256 + 16 * c);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 256);
 #pragma unroll
     for (int j = 0; j < 4; ++j) { dst[j] = a[j]; dst[4 + j] = b[j]; }
   } else if constexpr (Gm::kLaneBytes == 16) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(row + 16 * c);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) dst[j] = a[j];
   } else {  // 1-byte, D=128
-    const u32x2 a = *reinterpret_cast<const u32x2*>(row + 8 * c);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
     dst[0] = a[0];
     dst[1] = a[1];
   }
@@ -195,6 +208,7 @@ __device__ __forceinline__ void load_q(uint32_t (&dst)[N], const uint8_t* qrow, 
 
 template <int D, int KV, int RW>
 __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
+  constexpr int NB = pipeline_stages(D, KV, RW);
   using Gm = Geom<D, KV>;
   constexpr int DPL = Gm::kDimsPerLane;
   constexpr int NR = Gm::kRawDwords;
@@ -206,7 +220,7 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
   extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane >> 4;  // key group within the wave
   const int c = lane & 15;     // 16-byte chunk of the key row
   const int split = blockIdx.x;
@@ -246,15 +260,11 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
   int lo_r[RW], hi_r[RW];
   int lo_max = 0, hi_min = 0x7fffffff;
   bool any_active = false;
-  uint32_t qr[RW][NP];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int gr = rg * RW + r;
-    const int i = gr / G;
-    const int hh = gr - i * G;
+    const int i = (rg * RW + r) / G;
     const int pos = pos0 + i;
-    const bool exists = i < Qb;
-    const bool active = exists && pos >= 0;
+    const bool active = i < Qb && pos >= 0;
     lo_r[r] = active ? (a.window > 0 ? max(0, pos - a.window + 1) : 0) : 0;
     hi_r[r] = active ? pos : -1;
     if (active) {
@@ -262,43 +272,82 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
       hi_min = min(hi_min, hi_r[r]);
       any_active = true;
     }
-    if (exists) {
-      const uint8_t* qrow = a.q + ((size_t)(off + i) * Hq + g * G + hh) * (D * 2);
+  }
+  if (!any_active) w_hi = w_lo;
+  const int n = w_hi - w_lo;
+
+  // Addresses: a uniform (SGPR) page pointer per unit plus per-lane 32-bit
+  // offsets computed once.
+  const uint32_t key_stride = (uint32_t)a.num_kv_heads * Gm::kRowBytes;
+  const size_t page_bytes = (size_t)kPageSize * key_stride;
+  uint32_t loff[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i)
+    loff[i] = (uint32_t)(slot + 4 * i) * key_stride + (uint32_t)g * Gm::kRowBytes +
+              lane_piece_offset<D, KV>(c);
+  // Block-table row read through the constant address space: scalar loads,
+  // waited on with lgkmcnt, independent of the vector-load pipeline.
+  typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
+  const bt_ptr_t bt = (bt_ptr_t)(a.block_table + (size_t)b * a.max_pages);
+  // Page id of the wave's k-th unit (clamped to its last unit, whose
+  // repeated reads hit in cache).
+  auto pid_of = [&](int k) -> int { return bt[(w_lo + min(k, n - 1)) / UPP]; };
+
+  auto load_unit = [&](uint32_t (&kr)[KI][NR], uint32_t (&vr)[KI][NR], int pid, int u) {
+    const size_t base = (size_t)pid * page_bytes + (size_t)(u % UPP) * UK * key_stride;
+    const uint8_t* kp = a.k + base;
+    const uint8_t* vp = a.v + base;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      load_slice<D, KV>(kr[i], kp + loff[i]);
+      load_slice<D, KV>(vr[i], vp + loff[i]);
+    }
+  };
+
+  // First NB-1 units of K and V go out before anything else waits on memory.
+  uint32_t kb[NB][KI][NR], vb[NB][KI][NR];
+  if (n > 0) {
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st) load_unit(kb[st], vb[st], pid_of(st), w_lo + min(st, n - 1));
+  }
+
+  // Query rows (fp16, this lane's dims). Scores stay unscaled; the scale
+  // (times log2 e, times the K scale for quantized KV) enters through the
+  // exponent. A negative scale is folded into q's sign so that the running
+  // max of unscaled scores is the max of scaled ones.
+  float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
+  const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
+  qk = fabsf(qk);
+  uint32_t qr[RW][NP];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int gr = rg * RW + r;
+    const int i = gr / G;
+    if (i < Qb) {
+      const uint8_t* qrow = a.q + ((size_t)(off + i) * Hq + g * G + (gr - i * G)) * (D * 2);
       load_q<D, KV>(qr[r], qrow, c);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) qr[r][j] ^= qflip;
     } else {
 #pragma unroll
       for (int j = 0; j < NP; ++j) qr[r][j] = 0u;
     }
   }
-  if (!any_active) w_hi = w_lo;
 
-  const float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
-
+  // Running state. kNoMax is a finite stand-in for "no key yet": it keeps
+  // exp2(m - m_new) finite and equal to 1 while a row has seen nothing.
+  constexpr float kNoMax = -1e30f;
   float m[RW], l[RW], o[RW][DPL];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    m[r] = -INFINITY;
+    m[r] = kNoMax;
     l[r] = 0.0f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[r][e] = 0.0f;
   }
 
-  const size_t key_stride = (size_t)a.num_kv_heads * Gm::kRowBytes;
-  const size_t page_bytes = (size_t)kPageSize * key_stride;
-  const size_t lane_off = (size_t)slot * key_stride + (size_t)g * Gm::kRowBytes;
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-
-  auto load_unit = [&](uint32_t (&kr)[KI][NR], uint32_t (&vr)[KI][NR], int pid, int u) {
-    const size_t base = (size_t)pid * page_bytes + (size_t)(u % UPP) * UK * key_stride + lane_off;
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      load_slice<D, KV>(kr[i], a.k + base + (size_t)(4 * i) * key_stride, c);
-      load_slice<D, KV>(vr[i], a.v + base + (size_t)(4 * i) * key_stride, c);
-    }
-  };
-
   auto process_unit = [&](uint32_t (&kr)[KI][NR], uint32_t (&vr)[KI][NR], int u) {
-    float s[KI][RW];
+    float s[KI][RW];  // raw q.k, then p
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       h2_t kh[NP];
@@ -309,51 +358,68 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < NP; ++j)
           acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, qr[r][j]), kh[j], acc, false);
-        s[i][r] = acc;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KI; ++i)
-#pragma unroll
-      for (int r = 0; r < RW; ++r) s[i][r] = sum16(s[i][r]) * qk;
-
-    const int j0 = u * UK;
-    if (!(j0 >= lo_max && j0 + UK - 1 <= hi_min)) {
-#pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const int j = j0 + 4 * i + slot;
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-          s[i][r] = (j >= lo_r[r] && j <= hi_r[r]) ? s[i][r] : -INFINITY;
-        if (j >= L) {
-#pragma unroll
-          for (int e = 0; e < NR; ++e) vr[i][e] = 0u;
-        }
+        s[i][r] = sum16(acc);
       }
     }
 
     bool rescale = false;
     float alpha[RW];
+    const int j0 = u * UK;
+    if (j0 >= lo_max && j0 + UK - 1 <= hi_min) {
+      // Every key of the unit is visible to every active row.
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      float mt = s[0][r];
+      for (int r = 0; r < RW; ++r) {
+        float mt = s[0][r];
 #pragma unroll
-      for (int i = 1; i < KI; ++i) mt = fmaxf(mt, s[i][r]);
-      mt = max4(mt);
-      const float mn = fmaxf(m[r], mt);
-      const float mref = mn == -INFINITY ? 0.0f : mn;
-      alpha[r] = __builtin_amdgcn_exp2f(m[r] - mref);
-      rescale |= mn != m[r];
-      m[r] = mn;
-      float ps = 0.0f;
+        for (int i = 1; i < KI; ++i) mt = fmaxf(mt, s[i][r]);
+        const float mn = fmaxf(m[r], qk * max4(mt));
+        alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);
+        rescale |= mn != m[r];
+        m[r] = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          s[i][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][r], qk, -mn));
+          ps += s[i][r];
+        }
+        l[r] = __builtin_fmaf(l[r], alpha[r], ps);
+      }
+    } else {
+      // Boundary unit: per-key visibility by select (never by arithmetic, so
+      // poison past the sequence end cannot leak), V rows past the end zeroed.
+      bool valid[KI][RW];
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        s[i][r] = __builtin_amdgcn_exp2f(s[i][r] - mref);
-        ps += s[i][r];
+        const int j = j0 + 4 * i + slot;
+#pragma unroll
+        for (int r = 0; r < RW; ++r) valid[i][r] = j >= lo_r[r] && j <= hi_r[r];
+        if (j >= L) {
+#pragma unroll
+          for (int e = 0; e < NR; ++e) vr[i][e] = 0u;
+        }
       }
-      l[r] = l[r] * alpha[r] + ps;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) mt = fmaxf(mt, valid[i][r] ? s[i][r] : -INFINITY);
+        mt = max4(mt);
+        const float mn = fmaxf(m[r], mt == -INFINITY ? kNoMax : qk * mt);
+        alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);
+        rescale |= mn != m[r];
+        m[r] = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][r], qk, -mn));
+          s[i][r] = valid[i][r] ? p : 0.0f;
+          ps += s[i][r];
+        }
+        l[r] = __builtin_fmaf(l[r], alpha[r], ps);
+      }
     }
-    if (rescale) {
+    // m is the same in every lane, so the ballot is all or nothing: a scalar branch.
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
       for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -373,23 +439,31 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
     }
   };
 
-  if (w_lo < w_hi) {
-    uint32_t kr[KI][NR], vr[KI][NR];
-    int pid = bt[w_lo / UPP];
-    load_unit(kr, vr, pid, w_lo);
-    int pid_next = bt[min(w_lo + 1, w_hi - 1) / UPP];
-    for (int u = w_lo; u < w_hi - 1; ++u) {
-      const int pid_after = bt[min(u + 2, w_hi - 1) / UPP];
-      uint32_t kn[KI][NR], vn[KI][NR];
-      load_unit(kn, vn, pid_next, u + 1);
-      process_unit(kr, vr, u);
+  if (n > 0) {
+    // NB-stage ring of units in registers: the loads of unit k + NB - 1 are
+    // issued before unit k is computed; page ids are fetched NB units before
+    // the loads that use them.
+    int pid_s[NB];
 #pragma unroll
-      for (int i = 0; i < KI; ++i)
+    for (int st = 0; st < NB; ++st) pid_s[st] = pid_of(NB - 1 + st);
+    // Whole groups of NB units: straight-line bodies, so the ring stays in
+    // fixed registers and the loads stay in flight across units.
+    const int n_main = n - n % NB;
+    for (int it = 0; it < n_main; it += NB) {
 #pragma unroll
-        for (int e = 0; e < NR; ++e) { kr[i][e] = kn[i][e]; vr[i][e] = vn[i][e]; }
-      pid_next = pid_after;
+      for (int st = 0; st < NB; ++st) {
+        const int k_issue = it + st + NB - 1;
+        load_unit(kb[(st + NB - 1) % NB], vb[(st + NB - 1) % NB], pid_s[st],
+                  w_lo + min(k_issue, n - 1));
+        pid_s[st] = pid_of(k_issue + NB);
+        process_unit(kb[st], vb[st], w_lo + it + st);
+      }
     }
-    process_unit(kr, vr, w_hi - 1);
+    // The last n % NB units already sit in kb[0 ..] (their loads were issued
+    // by the prologue or the last group).
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st)
+      if (n_main + st < n) process_unit(kb[st], vb[st], w_lo + n_main + st);
   }
 
   // Merge the 4 key groups of the wave (same m everywhere in the wave).
@@ -430,7 +504,7 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
     for (int k = 0; k < a.key_waves; ++k)
       M = fmaxf(M, lds[(size_t)(k * nrg + rgi) * RW * (D + 2) + r]);
     float lsum = 0.0f, osum = 0.0f;
-    if (active && M != -INFINITY) {
+    if (active) {
       for (int k = 0; k < a.key_waves; ++k) {
         const float* wb = lds + (size_t)(k * nrg + rgi) * RW * (D + 2);
         const float wt = __builtin_amdgcn_exp2f(wb[r] - M);

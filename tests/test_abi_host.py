@@ -86,7 +86,7 @@ def test_empty_batch_is_ok_without_launch():
 
 def test_split_policy_and_workspace():
     d = _dims()
-    assert pda.resolve_splits(d, 0, 0, 256) == 8  # 64 (seq, head) units
+    assert pda.resolve_splits(d, 0, 0, 256) == 4  # 64 (seq, head) units, ~1 workgroup per CU
     assert pda.resolve_splits(d, 0, 3, 256) == 3
     d3 = _dims(batch=1, num_tokens=1, num_q_heads=24, num_kv_heads=4, head_dim=256,
                max_pages_per_seq=1025, num_pages=1025)
