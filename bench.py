@@ -78,7 +78,7 @@ class Runner:
     """Pre-marshalled C-ABI calls for one case (no per-step Python work
     beyond the ctypes call)."""
 
-    def __init__(self, case, device, replicas: int, num_splits: int):
+    def __init__(self, case, device, replicas: int, num_splits: int, kernel: str = "auto"):
         import torch
 
         import paged_split_decode_amd as pda
@@ -88,7 +88,7 @@ class Runner:
         self.case = case
         c = case
         self.dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
-                                    c.max_q_len, c.kv_dtype)
+                                    c.max_q_len, c.kv_dtype, kernel)
         self.S = pda.resolve_splits(self.dims, c.window, num_splits)
         T, Hq, D = c.q.shape
         self.T, self.Hq, self.D = T, Hq, D
@@ -145,7 +145,7 @@ def _hold_gpu():
     torch.cuda._sleep(50_000_000)
 
 
-def measure(case, steps: int, warmup: int, num_splits: int, device):
+def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str = "auto"):
     """Time `steps` passes. Returns step time (device, launches queued ahead),
     eager step time (launches paced by the host), and the decode kernel's
     average launch duration from HIP events around each launch."""
@@ -156,7 +156,7 @@ def measure(case, steps: int, warmup: int, num_splits: int, device):
     nbytes = algorithmic_bytes(case)
     pool = case.k_cache.numel() * case.k_cache.element_size() * 2
     replicas = max(1, min(16, math.ceil((1 << 30) / max(pool, 1))))
-    r = Runner(case, device, replicas, num_splits)
+    r = Runner(case, device, replicas, num_splits, kernel)
     for i in range(warmup):
         r.decode(i)
         r.combine()
@@ -247,6 +247,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
+    ap.add_argument("--window", type=int, default=None, help="override the sliding window")
+    ap.add_argument("--splits", type=int, default=None, help="override num_splits (0: auto)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "vector", "matrix"],
+                    help="decode kernel family")
     ap.add_argument("--no-cells", action="store_true", help="skip the extra workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     args = ap.parse_args(argv)
@@ -262,8 +267,12 @@ def main(argv=None):
     device = "cuda:0"
     torch.cuda.set_device(0)
     w = WORKLOADS[args.workload]
+    over = {k: v for k, v in (("batch", args.batch), ("window", args.window),
+                              ("num_splits", args.splits)) if v is not None}
+    if over:
+        w = w.with_(**over)
     case = make_case(w, device=device)
-    m = measure(case, args.steps, args.warmup, w.num_splits, device)
+    m = measure(case, args.steps, args.warmup, w.num_splits, device, args.kernel)
     gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
     dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
     traffic = traffic_for(args.workload)
@@ -280,6 +289,7 @@ def main(argv=None):
                    "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "algorithmic_bytes": m["bytes"], "input_replicas": m["replicas"],
+                   "kernel": args.kernel,
                    "accumulate": "fp32"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
@@ -294,7 +304,7 @@ def main(argv=None):
         for name, over in CELLS:
             wc = WORKLOADS[name].with_(**over)
             c = make_case(wc, device=device)
-            mc = measure(c, max(10, args.steps // 4), 3, wc.num_splits, device)
+            mc = measure(c, max(10, args.steps // 4), 3, wc.num_splits, device, args.kernel)
             cells.append(cell_record(name, wc, mc))
             print(json.dumps({"cell": cells[-1]}), file=sys.stderr, flush=True)
             del c

@@ -70,6 +70,21 @@ typedef enum pda_kv_dtype {
   PDA_KV_INT8 = 2
 } pda_kv_dtype;
 
+/* Decode kernel family. Both compute the same function and are checked
+ * against the same reference; they differ in where the arithmetic runs.
+ *  PDA_KERNEL_VECTOR: scores with packed fp16 v_dot2 (fp32 accumulation) and
+ *    DPP cross-lane sums, P.V with fp32 FMAs; the pull request's "packed
+ *    fdot2" design (section "Purpose") carried to wave64.
+ *  PDA_KERNEL_MATRIX: Q.K^T and P.V on the MFMA units (fp16 operands, fp32
+ *    accumulation; P rounded to fp16 for the P.V product).
+ *  PDA_KERNEL_AUTO: the library's choice (currently the matrix kernel, the
+ *    faster of the two on every measured shape). */
+typedef enum pda_kernel {
+  PDA_KERNEL_AUTO = 0,
+  PDA_KERNEL_VECTOR = 1,
+  PDA_KERNEL_MATRIX = 2
+} pda_kernel;
+
 /* Sizes of one call. */
 typedef struct pda_decode_dims {
   int32_t batch;             /* B: sequences (0: nothing to do) */
@@ -82,6 +97,7 @@ typedef struct pda_decode_dims {
   int32_t max_pages_per_seq; /* columns of block_table */
   int32_t max_q_len;         /* bound on q_lens[b]; 1 when q_lens is NULL */
   int32_t kv_dtype;          /* a pda_kv_dtype */
+  int32_t kernel;            /* a pda_kernel: which decode kernel family runs */
 } pda_decode_dims;
 
 /* Largest (num_q_heads / num_kv_heads) * max_q_len a call accepts. */

@@ -21,13 +21,14 @@ __all__ = [
     "paged_decode_attention", "paged_decode_partials", "split_combine",
     "resolve_splits", "workspace_bytes", "partials_bytes", "decode_dims",
     "load_library", "library_path", "KV_DTYPES", "PDA_MAX_ROWS", "PDA_MAX_SPLITS",
-    "PdaError", "partials_views",
+    "PdaError", "partials_views", "KERNELS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 KV_DTYPES = {"f16": 0, "fp8_e4m3": 1, "int8": 2}
+KERNELS = {"auto": 0, "vector": 1, "matrix": 2}
 PDA_MAX_ROWS = 32
 PDA_MAX_SPLITS = 256
 STATUS = {0: "PDA_OK", -1: "PDA_ERR_NULL", -2: "PDA_ERR_SHAPE", -3: "PDA_ERR_ALIGN",
@@ -43,7 +44,7 @@ class PdaError(RuntimeError):
 class DecodeDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_tokens", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
-        "num_pages", "max_pages_per_seq", "max_q_len", "kv_dtype")]
+        "num_pages", "max_pages_per_seq", "max_q_len", "kv_dtype", "kernel")]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -113,7 +114,7 @@ def _kv_code(k_cache: torch.Tensor, kv_dtype: Optional[str]) -> int:
 
 
 def decode_dims(q, k_cache, block_table, seq_lens, q_lens=None, max_q_len=None,
-                kv_dtype=None) -> DecodeDims:
+                kv_dtype=None, kernel="auto") -> DecodeDims:
     """Sizes of one call, read from tensor shapes. ``max_q_len`` defaults to
     1 without q_lens; with q_lens it must be given (reading q_lens would need
     a device synchronization)."""
@@ -125,7 +126,7 @@ def decode_dims(q, k_cache, block_table, seq_lens, q_lens=None, max_q_len=None,
                       num_kv_heads=Hkv, head_dim=D, page_size=P, num_pages=num_pages,
                       max_pages_per_seq=block_table.shape[1],
                       max_q_len=1 if q_lens is None else int(max_q_len),
-                      kv_dtype=_kv_code(k_cache, kv_dtype))
+                      kv_dtype=_kv_code(k_cache, kv_dtype), kernel=KERNELS[kernel])
 
 
 def _contig(*ts):
@@ -158,12 +159,14 @@ def partials_bytes(dims: DecodeDims, window: int = 0, num_splits: int = 0) -> in
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                            window, num_splits, out, k_scale=None, v_scale=None,
-                           kv_dtype=None, max_q_len=None, workspace=None, stream=None):
+                           kv_dtype=None, max_q_len=None, workspace=None, stream=None,
+                           kernel="auto"):
     """out[t, h] = softmax(scale q.K^T) V over each token's visible keys (see
-    include/pda.h). Writes ``out`` (fp16 [T, Hq, D]) and returns None."""
+    include/pda.h). Writes ``out`` (fp16 [T, Hq, D]) and returns None.
+    ``kernel``: "auto", "vector" (v_dot2) or "matrix" (MFMA)."""
     lib = load_library()
     _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, out, k_scale, v_scale)
-    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel)
     need = workspace_bytes(dims, window, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -177,13 +180,13 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, s
 
 def paged_decode_partials(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                           window, num_splits, workspace, k_scale=None, v_scale=None,
-                          kv_dtype=None, max_q_len=None, stream=None) -> int:
+                          kv_dtype=None, max_q_len=None, stream=None, kernel="auto") -> int:
     """The decode stage alone: writes split partials into ``workspace`` (a
     float32 or uint8 tensor of at least partials_bytes(...) bytes). Returns
     the split count used."""
     lib = load_library()
     _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, workspace, k_scale, v_scale)
-    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel)
     S = resolve_splits(dims, window, num_splits)
     _check(lib.pda_paged_decode_partials(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),

@@ -56,6 +56,9 @@ int kv_kind(int32_t kv_dtype) {
 
 // Launch shape for one call.
 struct Plan {
+  int matrix;      // 1: MFMA kernel, 0: v_dot2 kernel
+  int row_tiles;   // MFMA kernel: 16-row tiles
+  size_t wave_lds; // MFMA kernel: LDS bytes per wave
   int rows;        // G * max_q_len query rows per (sequence, KV head)
   int rows_per_wave;
   int row_groups;
@@ -84,6 +87,8 @@ pda_status check_dims(const pda_decode_dims* d) {
   if (d->max_q_len < 1) return fail(PDA_ERR_SHAPE, "max_q_len %d must be >= 1", d->max_q_len);
   if (kv_kind(d->kv_dtype) < 0)
     return fail(PDA_ERR_UNSUPPORTED, "kv_dtype %d is not a pda_kv_dtype", d->kv_dtype);
+  if (d->kernel < PDA_KERNEL_AUTO || d->kernel > PDA_KERNEL_MATRIX)
+    return fail(PDA_ERR_UNSUPPORTED, "kernel %d is not a pda_kernel", d->kernel);
   const int64_t rows = (int64_t)(d->num_q_heads / d->num_kv_heads) * d->max_q_len;
   if (rows > PDA_MAX_ROWS)
     return fail(PDA_ERR_UNSUPPORTED, "(num_q_heads/num_kv_heads)*max_q_len = %lld exceeds %d",
@@ -93,8 +98,7 @@ pda_status check_dims(const pda_decode_dims* d) {
   return PDA_OK;
 }
 
-int auto_splits(const pda_decode_dims* d, int window, int key_waves, int num_cus) {
-  const int uk = pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype));
+int auto_splits(const pda_decode_dims* d, int window, int uk, int key_waves, int num_cus) {
   int64_t keys = (int64_t)d->max_pages_per_seq * d->page_size;
   if (window > 0) keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + uk);
   const int64_t units = (keys + uk - 1) / uk;
@@ -112,20 +116,36 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
     return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
   p->rows = (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
-  const int cap = d->head_dim == 256 ? 4 : pda::kMaxRowsPerWave;
-  p->row_groups = (p->rows + cap - 1) / cap;
-  p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
-  p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
-  if (p->row_groups >= 4) p->key_waves = 1;
-  const int waves = p->row_groups * p->key_waves;
-  p->threads = 64 * waves;
-  p->lds = pda::decode_lds_bytes(waves, p->rows_per_wave, d->head_dim);
+  // The matrix-core kernel is faster on every measured shape; the v_dot2
+  // kernel stays selectable.
+  p->matrix = d->kernel != PDA_KERNEL_VECTOR;
+  if (p->matrix) {
+    p->row_tiles = (p->rows + 15) / 16;
+    p->wave_lds = pda::mfma_wave_lds_bytes(d->head_dim, p->rows);
+    const int waves = (int)std::max<size_t>(1, std::min<size_t>(4, 65536 / p->wave_lds));
+    p->row_groups = 1;
+    p->rows_per_wave = p->rows;
+    p->key_waves = waves;
+    p->threads = 64 * waves;
+    p->lds = (size_t)waves * p->wave_lds;
+  } else {
+    const int cap = d->head_dim == 256 ? 4 : pda::kMaxRowsPerWave;
+    p->row_groups = (p->rows + cap - 1) / cap;
+    p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
+    p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
+    if (p->row_groups >= 4) p->key_waves = 1;
+    const int waves = p->row_groups * p->key_waves;
+    p->threads = 64 * waves;
+    p->lds = pda::decode_lds_bytes(waves, p->rows_per_wave, d->head_dim);
+    p->row_tiles = 0;
+    p->wave_lds = 0;
+  }
   if (num_splits >= 1) {
     p->splits = num_splits;
   } else {
     if (num_cus <= 0) num_cus = device_cu_count();
     if (num_cus <= 0) return fail(PDA_ERR_DEVICE, "cannot query the device's compute units");
-    p->splits = auto_splits(d, window, p->key_waves, num_cus);
+    p->splits = auto_splits(d, window, p->matrix ? pda::kPageSize : pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype)), p->key_waves, num_cus);
   }
   return PDA_OK;
 }
@@ -154,6 +174,21 @@ pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArg
                          hipStream_t stream) {
   const dim3 grid(p.splits, d->num_kv_heads, d->batch);
   hipError_t e;
+  if (p.matrix) {
+    switch (kv_kind(d->kv_dtype)) {
+      case pda::kKvF16:
+        e = pda::launch_decode_mfma_f16(d->head_dim, p.row_tiles, grid, p.threads, p.lds, stream, args);
+        break;
+      case pda::kKvFp8:
+        e = pda::launch_decode_mfma_fp8(d->head_dim, p.row_tiles, grid, p.threads, p.lds, stream, args);
+        break;
+      default:
+        e = pda::launch_decode_mfma_i8(d->head_dim, p.row_tiles, grid, p.threads, p.lds, stream, args);
+        break;
+    }
+    if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
+    return PDA_OK;
+  }
   switch (kv_kind(d->kv_dtype)) {
     case pda::kKvF16:
       e = pda::launch_decode_f16(d->head_dim, p.rows_per_wave, grid, p.threads, p.lds, stream, args);
@@ -192,6 +227,8 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.num_splits = p.splits;
   a.row_groups = p.row_groups;
   a.key_waves = p.key_waves;
+  a.rows = p.rows;
+  a.wave_lds_bytes = (int32_t)p.wave_lds;
   return a;
 }
 

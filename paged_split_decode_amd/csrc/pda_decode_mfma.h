@@ -1,0 +1,397 @@
+// Paged split-K decode attention on the gfx950 matrix cores.
+//
+// Same operation and work split as the v_dot2 kernel (pda_decode_impl.h):
+// one workgroup per (split, KV head, sequence), each wave streaming a
+// contiguous run of pages with its own online softmax, waves merged through
+// LDS at the end. The difference is where the arithmetic runs. Counters on
+// the v_dot2 kernel show it issue-bound (about 480 VALU instructions per 8 KB
+// of K+V, VALU active half the time at one wave per SIMD), so both products
+// go to MFMA here and the VALU keeps only the softmax:
+//
+//  * Scores as S^T = K . Q^T with v_mfma_f32_16x16x32_f16: the page's 16 keys
+//    are the A rows, the group's query rows (up to 16 per row tile, zero
+//    padded) the B columns. Lane (s = lane/16, c = lane%16) loads 16 bytes of
+//    key c per 32-dim step, so a wave instruction reads 16 keys x 64 bytes.
+//    The result leaves lane (s, c) holding row c's scores for keys 4s..4s+3.
+//  * That is exactly the B layout of P^T for O^T = V^T . P^T with
+//    v_mfma_f32_16x16x16_f16 (k = the page's 16 keys), so P needs no
+//    transpose. V is loaded coalesced (16 lanes per key row), written once to
+//    a wave-private LDS tile and read back column-wise as the A operand. O^T
+//    leaves lane (s, c) holding row c, so the online-softmax rescale is
+//    lane-local.
+//  * The row max crosses the wave's 4 lane groups with permlane16/32 swaps;
+//    the denominator l stays per lane and is summed once at the end.
+//  * fp8-e4m3 / int8 K and V are converted to fp16 exactly in registers; the
+//    per-KV-head scales fold into the score multiplier and the output.
+//  * Query rows beyond the real ones are zero; more than 16 rows take a
+//    second row tile (up to 32).
+#pragma once
+
+#include "pda_decode_impl.h"
+
+namespace pda {
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int KV>
+struct MGeom {
+  static constexpr int kElemBytes = KV == kKvF16 ? 2 : 1;
+  static constexpr int kSteps = D / 32;                 // QK k-steps of 32 dims
+  static constexpr int kKLoads = kSteps * kElemBytes / 2;  // 16-byte K loads per lane
+  static constexpr int kVDims = D / 16;                 // V dims per lane per key row
+  static constexpr int kVRaw = kVDims * kElemBytes / 4; // raw V dwords per lane per key
+  static constexpr int kDTiles = D / 16;                // PV output tiles of 16 dims
+  static constexpr int kLdsRow = D + 8;                 // LDS V row stride in halves
+  static constexpr int kRowBytes = D * kElemBytes;
+};
+
+template <int D, int KV, int NRT>
+__global__ void __launch_bounds__(256) pda_decode_mfma_kernel(const DecodeArgs a) {
+  using Mg = MGeom<D, KV>;
+  constexpr int NS = Mg::kSteps;
+  constexpr int NKL = Mg::kKLoads;
+  constexpr int VR = Mg::kVRaw;
+  constexpr int NDT = Mg::kDTiles;
+  constexpr int LR = Mg::kLdsRow;
+  constexpr int NB = (D == 256 && KV == kKvF16) ? 2 : 3;  // ring depth (pages)
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int s = lane >> 4;  // lane group: keys 4s..4s+3 of a page in the scores
+  const int c = lane & 15;  // key of the page (loads) / query row (scores, output)
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+  const int S = a.num_splits;
+  const int R = a.rows;  // G * max_q_len
+  const size_t wave_lds = a.wave_lds_bytes;
+  uint8_t* my_lds = lds_raw + (size_t)wave * wave_lds;
+  _Float16* vt = reinterpret_cast<_Float16*>(my_lds);
+
+  const int L = a.seq_lens[b];
+  const int Qb = a.q_lens ? a.q_lens[b] : 1;
+  int off = b;
+  if (a.q_lens) {
+    int sum = 0;
+    for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
+    off = wave_sum_int(sum);
+  }
+  const int pos0 = L - Qb;
+
+  // Pages any new token can see, split into `num_splits` chunks, then into one
+  // run per wave.
+  const int klo = a.window > 0 ? max(0, pos0 + 1 - a.window) : 0;
+  const int u_lo = klo / kPageSize;
+  const int nu = max(0, (L + kPageSize - 1) / kPageSize - u_lo);
+  const int per_split = (nu + S - 1) / S;
+  const int s_lo = u_lo + min(nu, split * per_split);
+  const int ns = min(nu, (split + 1) * per_split) - min(nu, split * per_split);
+  const int per_wave = (ns + nwaves - 1) / nwaves;
+  const int w_lo = s_lo + min(ns, wave * per_wave);
+  int w_hi = s_lo + min(ns, (wave + 1) * per_wave);
+
+  // Visibility bounds: uniform summary over the real rows (fast-path test),
+  // and this lane's own rows (16 * rt + c) for masked pages.
+  int lo_max = 0, hi_min = 0x7fffffff;
+  bool any_active = false;
+  for (int r = 0; r < R; ++r) {
+    const int i = r / G;
+    const int pos = pos0 + i;
+    if (i < Qb && pos >= 0) {
+      lo_max = max(lo_max, a.window > 0 ? max(0, pos - a.window + 1) : 0);
+      hi_min = min(hi_min, pos);
+      any_active = true;
+    }
+  }
+  if (!any_active) w_hi = w_lo;
+  const int n = w_hi - w_lo;
+  int lo_c[NRT], hi_c[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = 16 * rt + c;
+    const int i = row / G;
+    const int pos = pos0 + i;
+    const bool active = row < R && i < Qb && pos >= 0;
+    lo_c[rt] = active ? (a.window > 0 ? max(0, pos - a.window + 1) : 0) : 0;
+    hi_c[rt] = active ? pos : -1;
+  }
+
+  // Addresses.
+  const uint32_t key_stride = (uint32_t)a.num_kv_heads * Mg::kRowBytes;
+  const size_t page_bytes = (size_t)kPageSize * key_stride;
+  const uint32_t koff = (uint32_t)c * key_stride + (uint32_t)g * Mg::kRowBytes + 16u * s;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)(s + 4 * i) * key_stride + (uint32_t)g * Mg::kRowBytes +
+              lane_piece_offset<D, KV>(c);
+  typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
+  const bt_ptr_t bt = (bt_ptr_t)(a.block_table + (size_t)b * a.max_pages);
+  auto pid_of = [&](int k) -> int { return bt[w_lo + min(k, n - 1)]; };
+
+  auto load_page = [&](uint32_t (&kr)[NKL][4], uint32_t (&vr)[4][VR], int pid) {
+    const uint8_t* kp = a.k + (size_t)pid * page_bytes;
+    const uint8_t* vp = a.v + (size_t)pid * page_bytes;
+#pragma unroll
+    for (int t = 0; t < NKL; ++t) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(kp + koff + 64 * t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kr[t][e] = x[e];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_slice<D, KV>(vr[i], vp + voff[i]);
+  };
+
+  uint32_t kb[NB][NKL][4], vb[NB][4][VR];
+  if (n > 0) {
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st) load_page(kb[st], vb[st], pid_of(st));
+  }
+
+  // Q^T as the B operand: lane (s, c) holds row 16 rt + c, dims of step t in
+  // the same order as its K slice. A negative scale flips q's sign.
+  float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
+  const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
+  qk = fabsf(qk);
+  h8_t qb[NRT][NS];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = 16 * rt + c;
+    const int i = row / G;
+    const bool exists = row < R && i < Qb;
+    const uint8_t* qrow = a.q + ((size_t)(off + i) * Hq + g * G + (row - i * G)) * (D * 2);
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      // fp16 KV: step t covers K bytes 64t + 16s (dims 32t + 8s ..);
+      // 1-byte KV: K bytes 64(t/2) + 16s hold dims 64(t/2) + 16s + 8(t%2) ...
+      const int qbyte = KV == kKvF16 ? 64 * t + 16 * s : 128 * (t / 2) + 32 * s + 16 * (t % 2);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (exists) x = *reinterpret_cast<const u32x4*>(qrow + qbyte);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] ^= qflip;
+      qb[rt][t] = __builtin_bit_cast(h8_t, x);
+    }
+  }
+
+  constexpr float kNoMax = -1e30f;
+  float m[NRT], l[NRT];
+  f4_t o[NRT][NDT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    m[rt] = kNoMax;
+    l[rt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  auto process_page = [&](uint32_t (&kr)[NKL][4], uint32_t (&vr)[4][VR], int u) {
+    const int j0 = u * kPageSize;
+    const bool full = j0 >= lo_max && j0 + kPageSize - 1 <= hi_min;
+
+    // V rows past the sequence end are zeroed (their contents are arbitrary),
+    // then the page's V goes to this wave's LDS tile as fp16 rows.
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j0 + 4 * i + s >= L) {
+#pragma unroll
+          for (int e = 0; e < VR; ++e) vr[i][e] = 0u;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h2_t vh[D / 32];
+      to_pairs<KV>(vr[i], vh);
+      _Float16* row = vt + (4 * i + s) * LR;
+#pragma unroll
+      for (int e8 = 0; e8 < D / 128; ++e8) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, vh[4 * e8 + e]);
+        const int d0 = dim_of<D, KV>(c, 8 * e8);
+        *reinterpret_cast<u32x4*>(row + d0) = w;
+      }
+    }
+
+    // Scores S^T[key 4s+i][row c] for every row tile.
+    h8_t ka[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      if constexpr (KV == kKvF16) {
+        ka[t] = __builtin_bit_cast(h8_t, u32x4{kr[t][0], kr[t][1], kr[t][2], kr[t][3]});
+      } else {
+        uint32_t raw[2] = {kr[t / 2][2 * (t % 2)], kr[t / 2][2 * (t % 2) + 1]};
+        h2_t kh[4];
+        to_pairs<KV>(raw, kh);
+        ka[t] = __builtin_bit_cast(h8_t, u32x4{__builtin_bit_cast(uint32_t, kh[0]),
+                                                __builtin_bit_cast(uint32_t, kh[1]),
+                                                __builtin_bit_cast(uint32_t, kh[2]),
+                                                __builtin_bit_cast(uint32_t, kh[3])});
+      }
+    }
+    f4_t sc[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      sc[rt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+        sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t], qb[rt][t], sc[rt], 0, 0, 0);
+    }
+
+    // Online softmax per row (lane-local row c; the max crosses lane groups).
+    bool rescale = false;
+    float alpha[NRT];
+    h4_t pb[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      float p[4];
+      if (full) {
+        float mt = fmaxf(fmaxf(sc[rt][0], sc[rt][1]), fmaxf(sc[rt][2], sc[rt][3]));
+        const float mn = fmaxf(m[rt], qk * max4(mt));
+        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mn);
+        rescale |= mn != m[rt];
+        m[rt] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -mn));
+      } else {
+        bool valid[4];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 4 * s + i;
+          valid[i] = j >= lo_c[rt] && j <= hi_c[rt];
+          mt = fmaxf(mt, valid[i] ? sc[rt][i] : -INFINITY);
+        }
+        mt = max4(mt);
+        const float mn = fmaxf(m[rt], mt == -INFINITY ? kNoMax : qk * mt);
+        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mn);
+        rescale |= mn != m[rt];
+        m[rt] = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -mn));
+          p[i] = valid[i] ? e : 0.0f;
+        }
+      }
+      l[rt] = __builtin_fmaf(l[rt], alpha[rt], (p[0] + p[1]) + (p[2] + p[3]));
+      pb[rt] = h4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+    }
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha[rt];
+    }
+
+    // O^T[dims][rows] += V^T . P^T, V^T read column-wise from the LDS tile.
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const _Float16* col = vt + (4 * s) * LR + 16 * dt + c;
+      const h4_t va = h4_t{col[0], col[LR], col[2 * LR], col[3 * LR]};
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], o[rt][dt], 0, 0, 0);
+    }
+  };
+
+  if (n > 0) {
+    int pid_s[NB];
+#pragma unroll
+    for (int st = 0; st < NB; ++st) pid_s[st] = pid_of(NB - 1 + st);
+    const int n_main = n - n % NB;
+    for (int it = 0; it < n_main; it += NB) {
+#pragma unroll
+      for (int st = 0; st < NB; ++st) {
+        const int k_issue = it + st + NB - 1;
+        load_page(kb[(st + NB - 1) % NB], vb[(st + NB - 1) % NB], pid_s[st]);
+        pid_s[st] = pid_of(k_issue + NB);
+        process_page(kb[st], vb[st], w_lo + it + st);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st)
+      if (n_main + st < n) process_page(kb[st], vb[st], w_lo + n_main + st);
+  }
+
+  // Denominators over the 4 lane groups; m is already the same in them.
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) l[rt] = add4(l[rt]);
+
+  // Merge the waves through LDS: per wave, rows [R] of (m, l, -, -, o[D]).
+  __syncthreads();  // every wave is done with its V tile (the region aliases)
+  float* wm = reinterpret_cast<float*>(my_lds);
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = 16 * rt + c;
+    if (row < R) {
+      float* rec = wm + (size_t)row * (D + 4);
+      if (s == 0) { rec[0] = m[rt]; rec[1] = l[rt]; }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f4_t*>(rec + 4 + 16 * dt + 4 * s) = o[rt][dt];
+    }
+  }
+  __syncthreads();
+
+  const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
+  for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
+    const int row = idx / D;
+    const int d = idx - row * D;
+    const int i = row / G;
+    if (i >= Qb) continue;
+    const int h = g * G + (row - i * G);
+    const int t = off + i;
+    const bool active = pos0 + i >= 0;
+    float M = -INFINITY;
+    for (int w = 0; w < nwaves; ++w)
+      M = fmaxf(M, reinterpret_cast<const float*>(lds_raw + (size_t)w * wave_lds)[(size_t)row * (D + 4)]);
+    float lsum = 0.0f, osum = 0.0f;
+    if (active) {
+      for (int w = 0; w < nwaves; ++w) {
+        const float* rec = reinterpret_cast<const float*>(lds_raw + (size_t)w * wave_lds) +
+                           (size_t)row * (D + 4);
+        const float wt = __builtin_amdgcn_exp2f(rec[0] - M);
+        lsum += wt * rec[1];
+        osum += wt * rec[4 + d];
+      }
+    }
+    osum *= vs;
+    if (a.direct) {
+      const _Float16 y = lsum > 0.0f ? (_Float16)(osum / lsum) : (_Float16)0.0f;
+      a.out[((size_t)t * Hq + h) * D + d] = __builtin_bit_cast(uint16_t, y);
+    } else {
+      const size_t prow = ((size_t)t * Hq + h) * S + split;
+      a.part_o[prow * D + d] = osum;
+      if (d == 0) {
+        a.part_ml[prow * 2] = lsum > 0.0f ? M : -INFINITY;
+        a.part_ml[prow * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+template <int KV>
+hipError_t launch_mfma_kv(int head_dim, int row_tiles, dim3 grid, int threads, size_t lds,
+                          hipStream_t stream, const DecodeArgs& args) {
+#define PDA_MCASE(DD, NT)                                                              \
+  if (head_dim == DD && row_tiles == NT) {                                             \
+    hipLaunchKernelGGL((pda_decode_mfma_kernel<DD, KV, NT>), grid, dim3(threads), lds, \
+                       stream, args);                                                  \
+    return hipGetLastError();                                                          \
+  }
+  PDA_MCASE(128, 1)
+  PDA_MCASE(128, 2)
+  PDA_MCASE(256, 1)
+  PDA_MCASE(256, 2)
+#undef PDA_MCASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pda

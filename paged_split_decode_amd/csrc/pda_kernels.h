@@ -46,6 +46,8 @@ struct DecodeArgs {
   int32_t row_groups;          // waves of a workgroup sharing keys, split by rows
   int32_t key_waves;           // waves of a workgroup splitting the key range
   int32_t direct;              // 1: write out (one split); 0: write partials
+  int32_t rows;                // G * max_q_len (matrix kernel)
+  int32_t wave_lds_bytes;      // LDS bytes per wave (matrix kernel)
 };
 
 // Launch the decode kernel for (head_dim, kv_kind, rows_per_wave) with
@@ -60,6 +62,24 @@ hipError_t launch_decode_fp8(int head_dim, int rows_per_wave, dim3 grid,
 hipError_t launch_decode_i8(int head_dim, int rows_per_wave, dim3 grid,
                             int threads, size_t lds, hipStream_t stream,
                             const DecodeArgs& args);
+
+// Matrix-core (MFMA) decode kernel for (head_dim, kv_kind, row_tiles of 16
+// query rows), grid (num_splits, Hkv, B), `threads` / 64 waves per workgroup.
+hipError_t launch_decode_mfma_f16(int head_dim, int row_tiles, dim3 grid, int threads,
+                                  size_t lds, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_mfma_fp8(int head_dim, int row_tiles, dim3 grid, int threads,
+                                  size_t lds, hipStream_t stream, const DecodeArgs& args);
+hipError_t launch_decode_mfma_i8(int head_dim, int row_tiles, dim3 grid, int threads,
+                                 size_t lds, hipStream_t stream, const DecodeArgs& args);
+// LDS bytes one wave of the matrix kernel needs: its fp16 V tile (16 rows of
+// D + 8 halves) during the loop, then its merge records (per row: m, l, two
+// pad floats, o[D]); the two uses alias. Rounded up to 256 bytes.
+inline size_t mfma_wave_lds_bytes(int head_dim, int rows) {
+  const size_t tile = (size_t)16 * (head_dim + 8) * 2;
+  const size_t merge = (size_t)rows * (head_dim + 4) * 4;
+  const size_t bytes = tile > merge ? tile : merge;
+  return (bytes + 255) & ~(size_t)255;
+}
 
 // Bytes of dynamic LDS the decode kernel needs for the final merge.
 inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {

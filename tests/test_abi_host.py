@@ -58,6 +58,7 @@ def _call(dims, **over):
     (dict(max_q_len=0), {}, -2),
     (dict(num_q_heads=64, num_kv_heads=1), {}, -4),  # 64 rows > PDA_MAX_ROWS
     (dict(num_pages=0), {}, -2),
+    (dict(kernel=3), {}, -4),
     ({}, dict(q=None), -1),
     ({}, dict(out=None), -1),
     ({}, dict(q=ctypes.c_void_p(0x100004)), -3),
@@ -87,6 +88,7 @@ def test_empty_batch_is_ok_without_launch():
 def test_split_policy_and_workspace():
     d = _dims()
     assert pda.resolve_splits(d, 0, 0, 256) == 4  # 64 (seq, head) units, ~1 workgroup per CU
+    assert pda.resolve_splits(_dims(kernel=1), 0, 0, 256) == 4
     assert pda.resolve_splits(d, 0, 3, 256) == 3
     d3 = _dims(batch=1, num_tokens=1, num_q_heads=24, num_kv_heads=4, head_dim=256,
                max_pages_per_seq=1025, num_pages=1025)

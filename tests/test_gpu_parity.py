@@ -23,7 +23,11 @@ DEV = "cuda"
 TOL = {"f16": 2e-3, "fp8_e4m3": 2e-2, "int8": 2e-2}
 
 
-def run_gpu(case, num_splits=None, scale=None, window=None, out=None, use_q_lens=True):
+KERNELS = ["vector", "matrix"]
+
+
+def run_gpu(case, num_splits=None, scale=None, window=None, out=None, use_q_lens=True,
+            kernel="auto"):
     T, Hq, D = case.q.shape
     if out is None:
         out = torch.full((T, Hq, D), float("nan"), dtype=torch.float16, device=DEV)
@@ -34,7 +38,7 @@ def run_gpu(case, num_splits=None, scale=None, window=None, out=None, use_q_lens
         case.window if window is None else window,
         case.workload.num_splits if num_splits is None else num_splits, out,
         k_scale=case.k_scale, v_scale=case.v_scale, kv_dtype=case.kv_dtype,
-        max_q_len=case.max_q_len if use_q_lens else None)
+        max_q_len=case.max_q_len if use_q_lens else None, kernel=kernel)
     torch.cuda.synchronize()
     return out
 
@@ -73,9 +77,10 @@ def small(seed, **kw):
 
 
 @pytest.mark.parametrize("splits", [1, 3, 0])
-def test_tiny_workload(splits):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_tiny_workload(splits, kernel):
     c = case_on_gpu(WORKLOADS["tiny_d128"])
-    assert_parity(run_gpu(c, num_splits=splits), oracle_full(c), "f16", f"tiny S={splits}")
+    assert_parity(run_gpu(c, kernel=kernel, num_splits=splits), oracle_full(c), "f16", f"tiny S={splits}")
 
 
 def _random_case(seed):
@@ -96,20 +101,22 @@ def _random_case(seed):
 
 
 @pytest.mark.parametrize("seed", range(40))
-def test_random_small_cases(seed):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_random_small_cases(seed, kernel):
     w = _random_case(seed)
     c = case_on_gpu(w)
-    assert_parity(run_gpu(c), oracle_full(c), w.kv_dtype, repr(w))
+    assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), w.kv_dtype, repr(w))
 
 
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("G,Q", [(1, 1), (4, 1), (6, 1), (8, 1), (7, 3), (8, 4), (5, 2)])
-def test_head_dims_dtypes_groups(kv, D, G, Q):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_head_dims_dtypes_groups(kv, D, G, Q, kernel):
     w = small(11, head_dim=D, kv_dtype=kv, num_q_heads=2 * G, num_kv_heads=2, q_len=Q,
               num_splits=3)
     c = case_on_gpu(w)
-    assert_parity(run_gpu(c), oracle_full(c), kv, repr(w))
+    assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), kv, repr(w))
 
 
 # ---------------------------------------------------------------------------
@@ -117,13 +124,14 @@ def test_head_dims_dtypes_groups(kv, D, G, Q):
 # ---------------------------------------------------------------------------
 
 
-def test_writer_layout_identity_and_permuted_tables():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_writer_layout_identity_and_permuted_tables(kernel):
     # The kernel reads [page, slot, KV head, dim] pages through the table,
     # whether the table is an identity (dense layout) or a permutation.
     w = small(12, seq_lens=(64, 160), pool_pages=0, table_pad=0)
     c = case_on_gpu(w)
     want = oracle_full(c)
-    assert_parity(run_gpu(c), want, "f16", "permuted")
+    assert_parity(run_gpu(c, kernel=kernel), want, "f16", "permuted")
     n = c.k_cache.shape[0]
     bt = c.block_table.long()
     order = torch.cat([bt[0, :4], bt[1, :10]])
@@ -133,14 +141,15 @@ def test_writer_layout_identity_and_permuted_tables():
     c.v_cache = c.v_cache[order].contiguous()
     c.block_table = torch.tensor([[0, 1, 2, 3] + [n - 1] * 6, list(range(4, 14))],
                                  dtype=torch.int32, device=DEV)
-    assert_parity(run_gpu(c), want, "f16", "identity table")
+    assert_parity(run_gpu(c, kernel=kernel), want, "f16", "identity table")
 
 
 @pytest.mark.parametrize("D", [128, 256])
-def test_empty_rows_are_zero(D):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_empty_rows_are_zero(D, kernel):
     w = small(13, head_dim=D, q_len=3, seq_lens=(0, 2, 1, 40, 0), num_splits=4)
     c = case_on_gpu(w)
-    got = run_gpu(c)
+    got = run_gpu(c, kernel=kernel)
     want = oracle_full(c)
     assert_parity(got, want, "f16", "empty rows")
     g = got.cpu().numpy()
@@ -151,44 +160,49 @@ def test_empty_rows_are_zero(D):
 
 
 @pytest.mark.parametrize("splits", [1, 4])
-def test_custom_scale_into_out(splits):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_custom_scale_into_out(splits, kernel):
     c = case_on_gpu(small(14, num_splits=splits))
     out = torch.full(tuple(c.q.shape), float("nan"), dtype=torch.float16, device=DEV)
-    got = run_gpu(c, scale=0.37, out=out)
+    got = run_gpu(c, kernel=kernel, scale=0.37, out=out)
     assert got.data_ptr() == out.data_ptr()
     assert_parity(out, oracle_full(c, scale=0.37), "f16", "scale 0.37")
 
 
 @pytest.mark.parametrize("W", [1, 2, 15, 16, 17, 64, 299, 300, 10000])
 @pytest.mark.parametrize("Q", [1, 3])
-def test_decode_paged_sliding_window(W, Q):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_paged_sliding_window(W, Q, kernel):
     c = case_on_gpu(small(15, window=W, q_len=Q, num_q_heads=4, num_splits=0))
-    assert_parity(run_gpu(c), oracle_full(c), "f16", f"W={W} Q={Q}")
+    assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), "f16", f"W={W} Q={Q}")
 
 
 @pytest.mark.parametrize("Q", [2, 3, 4])
 @pytest.mark.parametrize("D", [128, 256])
-def test_decode_multi_token_queries(Q, D):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_multi_token_queries(Q, D, kernel):
     c = case_on_gpu(small(16, q_len=Q, head_dim=D, seq_lens=(3, 50, 257, 2), num_splits=2))
-    assert_parity(run_gpu(c), oracle_full(c), "f16", f"Q={Q} D={D}")
+    assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), "f16", f"Q={Q} D={D}")
 
 
 @pytest.mark.parametrize("kv", ["f16", "int8"])
-def test_forward_split_decode_counts_agree(kv):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_forward_split_decode_counts_agree(kv, kernel):
     c = case_on_gpu(small(17, kv_dtype=kv, seq_lens=(5, 123, 700, 0), q_len=2, window=250))
     want = oracle_full(c)
     outs = {}
     for S in (1, 2, 3, 8, 0, 64, 256):
-        outs[S] = run_gpu(c, num_splits=S)
+        outs[S] = run_gpu(c, kernel=kernel, num_splits=S)
         assert_parity(outs[S], want, kv, f"S={S}")
     base = outs[1].float()
     for S, o in outs.items():
         assert (o.float() - base).abs().max().item() <= 2 * TOL[kv]
 
 
-def test_page_permutation_is_bit_exact_on_gpu():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_page_permutation_is_bit_exact_on_gpu(kernel):
     c = case_on_gpu(small(18, seq_lens=(40, 333), q_len=2, num_splits=3))
-    base = run_gpu(c).clone()
+    base = run_gpu(c, kernel=kernel).clone()
     n = c.k_cache.shape[0]
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(5)).to(DEV)
     k2 = torch.empty_like(c.k_cache)
@@ -197,36 +211,39 @@ def test_page_permutation_is_bit_exact_on_gpu():
     v2[perm] = c.v_cache
     c.k_cache, c.v_cache = k2, v2
     c.block_table = perm[c.block_table.long()].to(torch.int32)
-    got = run_gpu(c)
+    got = run_gpu(c, kernel=kernel)
     assert torch.equal(got.view(torch.int16), base.view(torch.int16))
 
 
 @pytest.mark.parametrize("splits", [1, 5])
-def test_uniform_v_returns_v_bit_exact(splits):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_uniform_v_returns_v_bit_exact(splits, kernel):
     c = case_on_gpu(small(19, seq_lens=(9, 300), num_splits=splits))
     c.v_cache = torch.full_like(c.v_cache, 0.7)
-    got = run_gpu(c)
+    got = run_gpu(c, kernel=kernel)
     assert torch.all(got == torch.tensor(0.7, dtype=torch.float16)).item()
 
 
-def test_q_lens_null_equals_ones():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_q_lens_null_equals_ones(kernel):
     c = case_on_gpu(small(20, num_splits=2))
-    a = run_gpu(c, use_q_lens=False)
-    b = run_gpu(c, use_q_lens=True)
+    a = run_gpu(c, kernel=kernel, use_q_lens=False)
+    b = run_gpu(c, kernel=kernel, use_q_lens=True)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
-def test_partials_then_combine_equals_attention(kv):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_partials_then_combine_equals_attention(kv, kernel):
     c = case_on_gpu(small(21, kv_dtype=kv, q_len=2, seq_lens=(0, 90, 500), num_splits=6))
-    ref = run_gpu(c)
+    ref = run_gpu(c, kernel=kernel)
     dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
-                           c.max_q_len, kv)
+                           c.max_q_len, kv, kernel)
     nbytes = pda.partials_bytes(dims, c.window, 6)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
     S = pda.paged_decode_partials(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
                                   c.q_lens, c.scale, c.window, 6, ws, c.k_scale, c.v_scale,
-                                  kv_dtype=kv, max_q_len=c.max_q_len)
+                                  kv_dtype=kv, max_q_len=c.max_q_len, kernel=kernel)
     T, Hq, D = c.q.shape
     po, pml = pda.partials_views(ws, T, Hq, S, D)
     out = torch.full((T, Hq, D), float("nan"), dtype=torch.float16, device=DEV)
@@ -268,8 +285,8 @@ def test_split_combine_vs_oracle(D, S):
 # ---------------------------------------------------------------------------
 
 
-def sampled_parity(c, units):
-    got = run_gpu(c)
+def sampled_parity(c, units, kernel):
+    got = run_gpu(c, kernel=kernel)
     assert torch.isfinite(got.float()).all()
     G = c.q.shape[1] // c.k_cache.shape[2]
     worst = 0.0
@@ -283,32 +300,36 @@ def sampled_parity(c, units):
     return got, worst
 
 
-def test_full_gqa4_d128_b8_l4096():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_gqa4_d128_b8_l4096(kernel):
     c = case_on_gpu(WORKLOADS["gqa4_d128_b8_l4096"])
-    got = run_gpu(c)
+    got = run_gpu(c, kernel=kernel)
     assert_parity(got, oracle_full(c), "f16", "gqa4 full")
 
 
 @pytest.mark.parametrize("window", [0, 4096])
 @pytest.mark.parametrize("B", [1, 2, 3, 8, 32])
-def test_full_gqa6_d256_l16384(B, window):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_gqa6_d256_l16384(B, window, kernel):
     w = WORKLOADS["gqa6_d256_l16384"].with_(batch=B, window=window)
     c = case_on_gpu(w)
     units = sorted({(0, 0), (B - 1, 3), (B // 2, 1)})
-    sampled_parity(c, units)
+    sampled_parity(c, units, kernel)
 
 
-def test_full_verify_q3_d128_b32():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_verify_q3_d128_b32(kernel):
     c = case_on_gpu(WORKLOADS["verify_q3_d128_b32"])
     lens = c.seq_lens_host
     zero = int(np.flatnonzero(lens == 0)[0])
     units = [(int(np.argmax(lens)), 0), (zero, 1), (int(np.argmin(np.where(lens > 0, lens,
                                                                              1 << 30))), 3),
              (7, 2)]
-    sampled_parity(c, units)
+    sampled_parity(c, units, kernel)
 
 
 @pytest.mark.parametrize("name", ["quant_fp8_d256_b64_l32768", "quant_int8_d256_b64_l32768"])
-def test_full_quantized_d256_b64_l32768(name):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_quantized_d256_b64_l32768(name, kernel):
     c = case_on_gpu(WORKLOADS[name])
-    sampled_parity(c, [(0, 0), (63, 3), (31, 2)])
+    sampled_parity(c, [(0, 0), (63, 3), (31, 2)], kernel)
