@@ -14,10 +14,12 @@ Reported (one JSON line):
   value        algorithmic bytes (every visible K/V element once, q, out) per
                step / measured step time, GB/s
   roofline     the decode kernel alone: same bytes / its average launch
-               duration measured with HIP events on the launch stream, against
-               the 8 TB/s HBM peak; traffic = HBM bytes per launch from
-               rocprofv3 FETCH_SIZE + WRITE_SIZE counters when a counter
-               summary for the current kernel sources exists, else null
+               duration (launches queued back to back on the launch stream,
+               HIP events around them), against the 8 TB/s HBM peak;
+               traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE +
+               WRITE_SIZE counters (each scaled by what the counter reads for
+               a plain 1 GiB copy) when a counter summary for the current
+               kernel sources exists, else null
   cpu_baseline the fp64 oracle on this host's cores, on a bounded sample of
                the same workload
   cells        the same measurement for the D=256 and other workloads
@@ -49,14 +51,14 @@ CELLS = [
     ("quant_fp8_d256_b64_l32768", {}),
     ("quant_int8_d256_b64_l32768", {}),
 ]
-KERNEL_SOURCES = ["pda_decode_impl.h", "pda_kernels.h", "pda_combine.hip", "pda_api.hip"]
-
-
 def kernel_source_hash() -> str:
+    """Hash of every HIP source of the library: counter figures recorded for
+    one hash do not describe a kernel built from different sources."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_split_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "paged_split_decode_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -183,20 +185,17 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / steps
 
-    # The decode kernel alone, each launch bracketed by events on its stream.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # The decode kernel alone: `steps` launches queued back to back on the
+    # launch stream, bracketed by two events.
     _hold_gpu()
+    t0.record()
     for i in range(steps):
-        ev[i][0].record()
         r.decode(i)
-        ev[i][1].record()
+    t1.record()
     torch.cuda.synchronize()
-    dec = sorted(a.elapsed_time(b) for a, b in ev)
-    decode_ms = sum(dec) / len(dec)
-    return dict(ms_per_step=ms_step, ms_eager=ms_eager, decode_ms=decode_ms,
-                decode_ms_median=dec[len(dec) // 2], bytes=nbytes, splits=r.S,
-                replicas=replicas)
+    decode_ms = t0.elapsed_time(t1) / steps
+    return dict(ms_per_step=ms_step, ms_eager=ms_eager, decode_ms=decode_ms, bytes=nbytes,
+                splits=r.S, replicas=replicas)
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -252,6 +251,9 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=None, help="override num_splits (0: auto)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "vector", "matrix"],
                     help="decode kernel family")
+    ap.add_argument("--reference-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for calibrating HBM byte counters)")
     ap.add_argument("--no-cells", action="store_true", help="skip the extra workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     args = ap.parse_args(argv)
@@ -266,6 +268,13 @@ def main(argv=None):
 
     device = "cuda:0"
     torch.cuda.set_device(0)
+    if args.reference_copy_mib > 0:
+        src = torch.ones(args.reference_copy_mib << 20, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = WORKLOADS[args.workload]
     over = {k: v for k, v in (("batch", args.batch), ("window", args.window),
                               ("num_splits", args.splits)) if v is not None}
@@ -293,9 +302,9 @@ def main(argv=None):
                    "accumulate": "fp32"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "pda_decode_kernel",
+                     "traffic": traffic, "kernel": "pda_decode_mfma_kernel" if args.kernel != "vector" else "pda_decode_kernel",
                      "decode_us": round(m["decode_ms"] * 1e3, 3),
-                     "decode_us_median": round(m["decode_ms_median"] * 1e3, 3)},
+                     "kernel_source_hash": kernel_source_hash()},
     }
     if not args.no_cells:
         cells = []
