@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one pass of the whole hot path (decode kernel + split combine) over
-one batch of synthetic input already resident in HBM. The headline workload
+A step is one call of the whole hot path (pda_paged_decode_attention: decode
+and split combine) over one batch of synthetic input already resident in HBM. The headline workload
 is the fp16-KV D=128 case: 8 sequences of 4096 keys, 32 query heads over 8
 KV heads, page size 16, seeded random page permutation, automatic splits.
 Its KV pool (134 MB) fits in the 256 MiB Infinity Cache, so the timed loop
@@ -95,9 +95,14 @@ class Runner:
         T, Hq, D = c.q.shape
         self.T, self.Hq, self.D = T, Hq, D
         self.out = torch.empty((T, Hq, D), dtype=torch.float16, device=device)
+        # One-call path workspace, and the decode-stage-only path's partials.
+        nws = pda.workspace_bytes(self.dims, c.window, self.S)
+        self.ws_all = torch.empty(max(nws, 16), dtype=torch.uint8, device=device)
         nbytes = pda.partials_bytes(self.dims, c.window, self.S)
         self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
         self.po, self.pml = pda.partials_views(self.ws, T, Hq, self.S, D)
+        # With several splits a step is two launches (decode, then combine).
+        self.two_launches = self.S > 1
         # Replicas of everything a step reads, so consecutive steps do not
         # hit in the Infinity Cache.
         self.reps = [(c.q, c.k_cache, c.v_cache)]
@@ -112,30 +117,32 @@ class Runner:
                        None if c.v_scale is None else P(c.v_scale.data_ptr()))
         self.dims_ref = ctypes.byref(self.dims)
         self.ws_ptr, self.ws_bytes = P(self.ws.data_ptr()), nbytes
+        self.wsa_ptr, self.wsa_bytes = P(self.ws_all.data_ptr()), self.ws_all.numel()
         self.po_ptr, self.pml_ptr = P(self.po.data_ptr()), P(self.pml.data_ptr())
         self.out_ptr = P(self.out.data_ptr())
         self.rep_ptrs = [tuple(P(t.data_ptr()) for t in r) for r in self.reps]
 
-    def decode(self, i: int):
+    def step(self, i: int):
+        """One full call of the hot path (pda_paged_decode_attention)."""
         q, k, v = self.rep_ptrs[i % len(self.rep_ptrs)]
-        if self.S == 1:
-            st = self.lib.pda_paged_decode_attention(
-                q, k, v, *self.common, self.out_ptr, *self.scales, self.dims_ref, None, 0,
-                self.stream)
-        else:
-            st = self.lib.pda_paged_decode_partials(
-                q, k, v, *self.common, *self.scales, self.dims_ref, self.ws_ptr,
-                self.ws_bytes, self.stream)
+        st = self.lib.pda_paged_decode_attention(
+            q, k, v, *self.common, self.out_ptr, *self.scales, self.dims_ref, self.wsa_ptr,
+            self.wsa_bytes, self.stream)
         if st != 0:
             raise RuntimeError(self.lib.pda_last_error().decode())
 
-    def combine(self):
-        if self.S == 1:
-            return
-        st = self.lib.pda_split_combine(self.po_ptr, self.pml_ptr, self.out_ptr, self.T,
-                                        self.Hq, self.D, self.S, self.stream)
+    def decode(self, i: int):
+        """The dominant kernel alone: the decode stage of a two-launch step,
+        otherwise the step's single launch."""
+        if not self.two_launches:
+            return self.step(i)
+        q, k, v = self.rep_ptrs[i % len(self.rep_ptrs)]
+        st = self.lib.pda_paged_decode_partials(
+            q, k, v, *self.common, *self.scales, self.dims_ref, self.ws_ptr,
+            self.ws_bytes, self.stream)
         if st != 0:
             raise RuntimeError(self.lib.pda_last_error().decode())
+
 
 
 def _hold_gpu():
@@ -160,18 +167,16 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     replicas = max(1, min(16, math.ceil((1 << 30) / max(pool, 1))))
     r = Runner(case, device, replicas, num_splits, kernel)
     for i in range(warmup):
-        r.decode(i)
-        r.combine()
+        r.step(i)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
 
-    # Whole steps (decode + combine), queued ahead of the device.
+    # Whole steps, queued ahead of the device.
     _hold_gpu()
     t0.record()
     for i in range(steps):
-        r.decode(i)
-        r.combine()
+        r.step(i)
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
@@ -179,8 +184,7 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     # The same, paced by the host (no queue-ahead).
     t0.record()
     for i in range(steps):
-        r.decode(i)
-        r.combine()
+        r.step(i)
     t1.record()
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / steps

@@ -126,9 +126,11 @@ typedef struct pda_decode_dims {
  *  workspace    device scratch for the split partials, at least
  *               pda_decode_workspace_bytes(dims, window, num_splits) bytes,
  *               16-byte aligned; may be NULL when that size is 0 (one split).
+ *               Calls that overlap on one workspace race.
  *
- * Launches the decode kernel and, with more than one split, the combine
- * kernel, both on `stream`.
+ * With one split the decode kernel writes `out` directly; with more, it
+ * writes partials and a second launch (the combine kernel) merges them. Both
+ * launches go on `stream`.
  */
 pda_status pda_paged_decode_attention(
     const void* q, const void* k_cache, const void* v_cache,

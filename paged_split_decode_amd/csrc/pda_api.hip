@@ -155,6 +155,10 @@ int64_t partials_bytes(const pda_decode_dims* d, int splits) {
          (int64_t)sizeof(float);
 }
 
+int64_t attention_workspace_bytes(const pda_decode_dims* d, int splits) {
+  return splits == 1 ? 0 : partials_bytes(d, splits);
+}
+
 pda_status check_pointers(const void* q, const void* k, const void* v, const int32_t* bt,
                           const int32_t* sl, const float* ks, const float* vs,
                           const pda_decode_dims* d) {
@@ -268,12 +272,12 @@ pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const 
   if ((st = make_plan(dims, window, num_splits, 0, &p))) return st;
   pda::DecodeArgs a = make_args(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                                 window, k_scale, v_scale, dims, p);
+  a.out = static_cast<uint16_t*>(out);
   if (p.splits == 1) {
     a.direct = 1;
-    a.out = static_cast<uint16_t*>(out);
     return launch_decode(p, dims, a, stream);
   }
-  const int64_t need = partials_bytes(dims, p.splits);
+  const int64_t need = attention_workspace_bytes(dims, p.splits);
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
                 workspace_bytes, workspace, (long long)need, p.splits);
@@ -360,7 +364,7 @@ int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
   Plan p;
   const pda_status st = make_plan(dims, window, num_splits, 0, &p);
   if (st != PDA_OK) return st;
-  return p.splits == 1 ? 0 : partials_bytes(dims, p.splits);
+  return attention_workspace_bytes(dims, p.splits);
 }
 
 const char* pda_last_error(void) { return g_last_error.c_str(); }

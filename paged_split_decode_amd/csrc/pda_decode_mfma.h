@@ -16,7 +16,8 @@
 //  * That is exactly the B layout of P^T for O^T = V^T . P^T with
 //    v_mfma_f32_16x16x16_f16 (k = the page's 16 keys), so P needs no
 //    transpose. V is loaded coalesced (16 lanes per key row), written once to
-//    a wave-private LDS tile and read back column-wise as the A operand. O^T
+//    a wave-private LDS tile and read back as the A operand with gfx950's
+//    transposing LDS read (one ds_read_b64_tr_b16 per 16 dims). O^T
 //    leaves lane (s, c) holding row c, so the online-softmax rescale is
 //    lane-local.
 //  * The row max crosses the wave's 4 lane groups with permlane16/32 swaps;
@@ -47,15 +48,24 @@ struct MGeom {
   static constexpr int kRowBytes = D * kElemBytes;
 };
 
+// Waves per SIMD the register allocation must leave room for: two wherever
+// the working set fits in 256 registers (a second wave hides the first one's
+// memory and MFMA latency), one for fp16 at D=256 (its K+V ring alone is 128
+// registers) and for two row tiles.
+constexpr int mfma_min_waves(int D, int KV, int NRT) {
+  return (NRT == 1 && !(D == 256 && KV == kKvF16)) ? 2 : 1;
+}
+
 template <int D, int KV, int NRT>
-__global__ void __launch_bounds__(256) pda_decode_mfma_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(256, mfma_min_waves(D, KV, NRT))
+pda_decode_mfma_kernel(const DecodeArgs a) {
   using Mg = MGeom<D, KV>;
   constexpr int NS = Mg::kSteps;
   constexpr int NKL = Mg::kKLoads;
   constexpr int VR = Mg::kVRaw;
   constexpr int NDT = Mg::kDTiles;
   constexpr int LR = Mg::kLdsRow;
-  constexpr int NB = (D == 256 && KV == kKvF16) ? 2 : 3;  // ring depth (pages)
+  constexpr int NB = D == 256 ? 2 : 3;  // ring depth (pages)
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
 
@@ -290,11 +300,19 @@ __global__ void __launch_bounds__(256) pda_decode_mfma_kernel(const DecodeArgs a
         for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha[rt];
     }
 
-    // O^T[dims][rows] += V^T . P^T, V^T read column-wise from the LDS tile.
+    // O^T[dims][rows] += V^T . P^T. The A operand (lane (s, c): V[4s + k][16 dt + c],
+    // k = 0..3) comes from the row-major LDS tile with one transposing read:
+    // within each 16-lane group, ds_read_b64_tr_b16 hands lane i element i % 4
+    // of the 8-byte rows addressed by lanes i/4 + 4k, so lane (s, c) points at
+    // row 4s + c/4, dims 16 dt + 4 (c % 4) .. + 3.
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t lds_s4_t;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const _Float16* col = vt + (4 * s) * LR + 16 * dt + c;
-      const h4_t va = h4_t{col[0], col[LR], col[2 * LR], col[3 * LR]};
+      _Float16* src = vt + (4 * s + (c >> 2)) * LR + 16 * dt + 4 * (c & 3);
+      const auto raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src);
+      const h4_t va = __builtin_bit_cast(h4_t, raw);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt)
         o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], o[rt][dt], 0, 0, 0);

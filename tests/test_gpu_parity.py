@@ -256,6 +256,32 @@ def test_partials_then_combine_equals_attention(kv, kernel):
     assert_parity(torch.from_numpy(mixed), oracle_full(c), kv, "oracle-combined partials")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("D", [128, 256])
+def test_workspace_reuse(kernel, D):
+    """One workspace serves repeated calls, whatever it held before (here:
+    NaN partials); results repeat bit for bit."""
+    c = case_on_gpu(small(22, head_dim=D, q_len=2, seq_lens=(0, 70, 600, 33), num_splits=5))
+    dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
+                           c.max_q_len, "f16", kernel)
+    nbytes = pda.workspace_bytes(dims, c.window, 5)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    # Poison the partials: a merge that read them before they were written
+    # would produce NaN.
+    ws.view(torch.float32).fill_(float("nan"))
+    outs = []
+    for _ in range(3):
+        out = torch.full(tuple(c.q.shape), float("nan"), dtype=torch.float16, device=DEV)
+        pda.paged_decode_attention(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                   c.q_lens, c.scale, c.window, 5, out, workspace=ws,
+                                   max_q_len=c.max_q_len, kernel=kernel)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert_parity(outs[0], oracle_full(c), "f16", "reused workspace")
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("S", [1, 2, 7, 64])
 def test_split_combine_vs_oracle(D, S):
