@@ -43,14 +43,18 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "decode-attn achieved HBM GB/s (fraction of peak) + us/call, D=128 & D=256"
 HEADLINE = "gqa4_d128_b8_l4096"
 CELLS = [
-    ("gqa6_d256_l16384", dict(batch=8)),
-    ("gqa6_d256_l16384", dict(batch=32)),
-    ("gqa6_d256_l16384", dict(batch=32, window=4096)),
-    ("gqa6_d256_l16384", dict(batch=1)),
+    # the headline shape with a caller split count inside the 1..8 range its
+    # configuration names for automatic splitting
+    ("gqa4_d128_b8_l4096", dict(num_splits=8)),
+    # D=256 batch sweep, without and with a 4096-key sliding window
+    *[("gqa6_d256_l16384", dict(batch=b, window=win))
+      for win in (0, 4096) for b in (1, 2, 3, 8, 32)],
     ("verify_q3_d128_b32", {}),
     ("quant_fp8_d256_b64_l32768", {}),
     ("quant_int8_d256_b64_l32768", {}),
 ]
+
+
 def kernel_source_hash() -> str:
     """Hash of every HIP source of the library: counter figures recorded for
     one hash do not describe a kernel built from different sources."""

@@ -62,7 +62,9 @@ struct Plan {
   int rows;        // G * max_q_len query rows per (sequence, KV head)
   int rows_per_wave;
   int row_groups;
-  int key_waves;
+  int key_waves;       // waves per KV head (matrix) / per key range (v_dot2)
+  int heads_per_group; // matrix kernel: KV heads per workgroup
+  int head_groups;     // grid y: workgroups across the KV heads
   int splits;
   int threads;
   size_t lds;
@@ -98,15 +100,59 @@ pda_status check_dims(const pda_decode_dims* d) {
   return PDA_OK;
 }
 
+// Splits for the v_dot2 kernel: about one workgroup per compute unit.
 int auto_splits(const pda_decode_dims* d, int window, int uk, int key_waves, int num_cus) {
   int64_t keys = (int64_t)d->max_pages_per_seq * d->page_size;
   if (window > 0) keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + uk);
   const int64_t units = (keys + uk - 1) / uk;
   const int64_t work = std::max<int64_t>(1, (int64_t)d->batch * d->num_kv_heads);
-  const int64_t target = (int64_t)num_cus;  // about one workgroup per compute unit
+  const int64_t target = (int64_t)num_cus;
   int64_t s = (target + work - 1) / work;
   s = std::min<int64_t>(s, std::max<int64_t>(1, units / (2 * key_waves)));
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, PDA_MAX_SPLITS));
+}
+
+// Pages of keys a call's longest sequence can have visible.
+int64_t visible_pages(const pda_decode_dims* d, int window) {
+  int64_t keys = (int64_t)d->max_pages_per_seq * d->page_size;
+  if (window > 0) keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + d->page_size);
+  return (keys + d->page_size - 1) / d->page_size;
+}
+
+// Workgroup shape and split count of the matrix kernel.
+//  * Up to 4 KV heads share a workgroup, one wave each: the heads of a page
+//    block (contiguous in the pool) are then fetched together, which measures
+//    faster than one head per workgroup. Fewer heads leave room for several
+//    waves per head (key_waves), to keep 4-wave workgroups.
+//  * Automatic splits: enough workgroups to fill every SIMD's wave slots once
+//    (all workgroups resident together), each wave keeping at least 2 pages.
+//  * A caller's split count: the head group shrinks until the workgroups
+//    cover every compute unit, and key_waves grows to fill the wave slots.
+void matrix_plan(const pda_decode_dims* d, int window, int num_splits, int num_cus,
+                 int waves_per_simd, int max_waves, Plan* p) {
+  const int64_t pages = visible_pages(d, window);
+  const int64_t B = std::max(1, d->batch);
+  const int Hkv = d->num_kv_heads;
+  auto groups = [&](int h) { return (int64_t)((Hkv + h - 1) / h); };
+  int hpw = std::min({Hkv, 4, max_waves});
+  int kw = std::max(1, std::min(4, max_waves) / hpw);
+  int64_t S;
+  if (num_splits >= 1) {
+    S = num_splits;
+    while (hpw > 1 && S * B * groups(hpw) < num_cus) hpw = (hpw + 1) / 2;
+    const int64_t slots = (int64_t)num_cus * 4 * waves_per_simd;
+    const int64_t want = slots / (S * B * groups(hpw) * hpw);
+    const int64_t by_pages = std::max<int64_t>(1, pages / (2 * S));
+    kw = (int)std::max<int64_t>(1, std::min<int64_t>({want, max_waves / hpw, by_pages}));
+  } else {
+    S = (int64_t)num_cus * waves_per_simd / (B * groups(hpw));  // never a second round
+    S = std::min<int64_t>(S, std::max<int64_t>(1, pages / (2 * kw)));
+    S = std::max<int64_t>(1, std::min<int64_t>(S, PDA_MAX_SPLITS));
+  }
+  p->heads_per_group = hpw;
+  p->key_waves = kw;
+  p->head_groups = (int)groups(hpw);
+  p->splits = (int)S;
 }
 
 pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_splits, int num_cus,
@@ -119,34 +165,55 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   // The matrix-core kernel is faster on every measured shape; the v_dot2
   // kernel stays selectable.
   p->matrix = d->kernel != PDA_KERNEL_VECTOR;
+  if (num_cus <= 0 && (p->matrix || num_splits < 1)) num_cus = device_cu_count();
+  if (num_cus <= 0 && (p->matrix || num_splits < 1))
+    return fail(PDA_ERR_DEVICE, "cannot query the device's compute units");
   if (p->matrix) {
     p->row_tiles = (p->rows + 15) / 16;
     p->wave_lds = pda::mfma_wave_lds_bytes(d->head_dim, p->rows);
-    const int waves = (int)std::max<size_t>(1, std::min<size_t>(4, 65536 / p->wave_lds));
+    const int waves_per_simd =
+        pda::mfma_waves_per_simd(d->head_dim, kv_kind(d->kv_dtype), p->row_tiles);
+    const int lds_waves = (int)std::max<size_t>(1, 65536 / p->wave_lds);
+    matrix_plan(d, window, num_splits, num_cus, waves_per_simd,
+                std::min(4 * waves_per_simd, lds_waves), p);
+    const int waves = p->heads_per_group * p->key_waves;
     p->row_groups = 1;
     p->rows_per_wave = p->rows;
-    p->key_waves = waves;
     p->threads = 64 * waves;
-    p->lds = (size_t)waves * p->wave_lds;
-  } else {
-    const int cap = d->head_dim == 256 ? 4 : pda::kMaxRowsPerWave;
-    p->row_groups = (p->rows + cap - 1) / cap;
-    p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
-    p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
-    if (p->row_groups >= 4) p->key_waves = 1;
-    const int waves = p->row_groups * p->key_waves;
-    p->threads = 64 * waves;
-    p->lds = pda::decode_lds_bytes(waves, p->rows_per_wave, d->head_dim);
-    p->row_tiles = 0;
-    p->wave_lds = 0;
+    p->lds = (size_t)waves * p->wave_lds;  // V tiles, then merge records
+    return PDA_OK;
   }
-  if (num_splits >= 1) {
-    p->splits = num_splits;
-  } else {
-    if (num_cus <= 0) num_cus = device_cu_count();
-    if (num_cus <= 0) return fail(PDA_ERR_DEVICE, "cannot query the device's compute units");
-    p->splits = auto_splits(d, window, p->matrix ? pda::kPageSize : pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype)), p->key_waves, num_cus);
+  const int cap = d->head_dim == 256 ? 4 : pda::kMaxRowsPerWave;
+  p->row_groups = (p->rows + cap - 1) / cap;
+  p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
+  p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
+  if (p->row_groups >= 4) p->key_waves = 1;
+  const int waves = p->row_groups * p->key_waves;
+  p->threads = 64 * waves;
+  p->lds = pda::decode_lds_bytes(waves, p->rows_per_wave, d->head_dim);
+  p->row_tiles = 0;
+  p->wave_lds = 0;
+  p->heads_per_group = 1;
+  p->head_groups = d->num_kv_heads;
+  p->splits = num_splits >= 1
+                  ? num_splits
+                  : auto_splits(d, window, pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype)),
+                                p->key_waves, num_cus);
+  return PDA_OK;
+}
+
+// The split count alone (for size queries): a caller's count needs no device.
+pda_status resolve_split_count(const pda_decode_dims* d, int32_t window, int32_t num_splits,
+                               int num_cus, int* splits) {
+  pda_status st = check_dims(d);
+  if (st != PDA_OK) return st;
+  if (num_splits >= 1 && num_splits <= PDA_MAX_SPLITS) {
+    *splits = num_splits;
+    return PDA_OK;
   }
+  Plan p;
+  if ((st = make_plan(d, window, num_splits, num_cus, &p))) return st;
+  *splits = p.splits;
   return PDA_OK;
 }
 
@@ -176,7 +243,7 @@ pda_status check_pointers(const void* q, const void* k, const void* v, const int
 
 pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArgs& args,
                          hipStream_t stream) {
-  const dim3 grid(p.splits, d->num_kv_heads, d->batch);
+  const dim3 grid(p.splits, p.head_groups, d->batch);
   hipError_t e;
   if (p.matrix) {
     switch (kv_kind(d->kv_dtype)) {
@@ -231,6 +298,7 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.num_splits = p.splits;
   a.row_groups = p.row_groups;
   a.key_waves = p.key_waves;
+  a.heads_per_group = p.heads_per_group;
   a.rows = p.rows;
   a.wave_lds_bytes = (int32_t)p.wave_lds;
   return a;
@@ -268,8 +336,17 @@ pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const 
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
     return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
   if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
+  int splits = 0;
+  if ((st = resolve_split_count(dims, window, num_splits, 0, &splits))) return st;
+  if (splits > 1) {
+    const int64_t need = attention_workspace_bytes(dims, splits);
+    if (!workspace || (int64_t)workspace_bytes < need)
+      return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
+                  workspace_bytes, workspace, (long long)need, splits);
+    if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
   Plan p;
-  if ((st = make_plan(dims, window, num_splits, 0, &p))) return st;
+  if ((st = make_plan(dims, window, splits, 0, &p))) return st;
   pda::DecodeArgs a = make_args(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                                 window, k_scale, v_scale, dims, p);
   a.out = static_cast<uint16_t*>(out);
@@ -277,11 +354,6 @@ pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const 
     a.direct = 1;
     return launch_decode(p, dims, a, stream);
   }
-  const int64_t need = attention_workspace_bytes(dims, p.splits);
-  if (!workspace || (int64_t)workspace_bytes < need)
-    return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
-                workspace_bytes, workspace, (long long)need, p.splits);
-  if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
   a.direct = 0;
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)dims->num_tokens * dims->num_q_heads * p.splits * dims->head_dim;
@@ -308,13 +380,15 @@ pda_status pda_paged_decode_partials(const void* q, const void* k_cache, const v
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
     return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
   if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
-  Plan p;
-  if ((st = make_plan(dims, window, num_splits, 0, &p))) return st;
-  const int64_t need = partials_bytes(dims, p.splits);
+  int splits = 0;
+  if ((st = resolve_split_count(dims, window, num_splits, 0, &splits))) return st;
+  const int64_t need = partials_bytes(dims, splits);
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
-                workspace_bytes, workspace, (long long)need, p.splits);
+                workspace_bytes, workspace, (long long)need, splits);
   if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  Plan p;
+  if ((st = make_plan(dims, window, splits, 0, &p))) return st;
   pda::DecodeArgs a = make_args(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                                 window, k_scale, v_scale, dims, p);
   a.direct = 0;
@@ -347,24 +421,23 @@ pda_status pda_split_combine(const float* partial_o, const float* partial_ml, vo
 
 int32_t pda_decode_resolve_splits(const pda_decode_dims* dims, int32_t window,
                                   int32_t num_splits, int32_t num_cus) {
-  Plan p;
-  const pda_status st = make_plan(dims, window, num_splits, num_cus, &p);
-  return st == PDA_OK ? p.splits : st;
+  int splits = 0;
+  const pda_status st = resolve_split_count(dims, window, num_splits, num_cus, &splits);
+  return st == PDA_OK ? splits : st;
 }
 
 int64_t pda_decode_partials_bytes(const pda_decode_dims* dims, int32_t window,
                                   int32_t num_splits) {
-  Plan p;
-  const pda_status st = make_plan(dims, window, num_splits, 0, &p);
-  return st == PDA_OK ? partials_bytes(dims, p.splits) : st;
+  int splits = 0;
+  const pda_status st = resolve_split_count(dims, window, num_splits, 0, &splits);
+  return st == PDA_OK ? partials_bytes(dims, splits) : st;
 }
 
 int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
                                    int32_t num_splits) {
-  Plan p;
-  const pda_status st = make_plan(dims, window, num_splits, 0, &p);
-  if (st != PDA_OK) return st;
-  return attention_workspace_bytes(dims, p.splits);
+  int splits = 0;
+  const pda_status st = resolve_split_count(dims, window, num_splits, 0, &splits);
+  return st == PDA_OK ? attention_workspace_bytes(dims, splits) : st;
 }
 
 const char* pda_last_error(void) { return g_last_error.c_str(); }

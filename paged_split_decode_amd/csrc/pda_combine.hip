@@ -4,28 +4,32 @@
 // scores on every wave and 4 barriers per tile"), sections "Purpose" and
 // "Test Result" (split-K combine).
 //
-// One workgroup (4 waves) per row. Every wave reads the row's (m, l) pairs
-// into lanes (split s in lane s % 64), so the global max M and each split's
-// weight 2^(m_s - M) sit in registers; wave w then streams the o rows of
-// splits w, w+4, ... (lane = D/64 contiguous dims, one coalesced row per
-// split, 8 independent loads in flight) and the 4 waves add up through LDS.
-// A split with l = 0 (no visible key) has weight 0 and its o is never used;
-// a row with no live split is written as zeros.
+// One workgroup per row with ceil(S / 16) waves; wave w owns splits
+// 16w .. 16w + 15 and issues all of their o loads at once (lane = D/64
+// contiguous dims of a split row), so the partials cost about one memory
+// round trip whatever S is. Every wave reads all (m, l) pairs into lanes
+// (split s in lane s % 64, slot s / 64) to get the global max M and the
+// denominator; a split's weight is 2^(m_s - M). Several waves add up through
+// LDS. A split with l = 0 (no visible key) has weight 0 and its o is never
+// used; a row with no live split is written as zeros.
 #include "pda_kernels.h"
 
 namespace pda {
 
-constexpr int kCombineWaves = 4;
-constexpr int kMaxSplitSlots = 4;  // splits per lane: 4 x 64 >= PDA_MAX_SPLITS
+constexpr int kSplitsPerWave = 16;
+constexpr int kMaxSplitSlots = 4;  // (m, l) slots per lane: 4 x 64 >= PDA_MAX_SPLITS
+constexpr int kMaxCombineWaves = 64 * kMaxSplitSlots / kSplitsPerWave;
 
 template <int D>
-__global__ void __launch_bounds__(64 * kCombineWaves)
+__global__ void __launch_bounds__(64 * kMaxCombineWaves)
 pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                    uint16_t* __restrict__ out, int S) {
   constexpr int DT = D / 64;
-  __shared__ float red[kCombineWaves][D + 1];
+  typedef float fv_t __attribute__((ext_vector_type(DT)));
+  extern __shared__ float red[];  // [waves][D] when there are several waves
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
   const size_t row = blockIdx.x;
   const float* ml = part_ml + row * S * 2;
 
@@ -42,8 +46,17 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
     }
     if (lv[k] > 0.0f) M = fmaxf(M, mv[k]);
   }
-  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
 
+  // This wave's o rows, all loads in flight before any is used.
+  const int s0 = kSplitsPerWave * wave;
+  const int n = min(kSplitsPerWave, S - s0);
+  const float* src = part_o + (row * S + s0) * D + lane * DT;
+  fv_t x[kSplitsPerWave];
+#pragma unroll
+  for (int j = 0; j < kSplitsPerWave; ++j)
+    if (j < n) x[j] = *reinterpret_cast<const fv_t*>(src + (size_t)j * D);
+
+  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
   float wv[kMaxSplitSlots];
   float den = 0.0f;
 #pragma unroll
@@ -53,32 +66,33 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   }
   for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k, 64);
 
-  float acc[DT];
+  // Weights of splits s0 .. s0 + 15: slot s0 / 64, lanes s0 % 64 + j.
+  const int slot = s0 >> 6;
+  const float wsel = slot == 0 ? wv[0] : slot == 1 ? wv[1] : slot == 2 ? wv[2] : wv[3];
+  const int lane0 = s0 & 63;
+  fv_t acc = {};
 #pragma unroll
-  for (int e = 0; e < DT; ++e) acc[e] = 0.0f;
-  const float* src = part_o + row * S * D + lane * DT;
-#pragma unroll
-  for (int k = 0; k < kMaxSplitSlots; ++k) {
-    const int n = min(64, S - 64 * k);
-#pragma unroll 8
-    for (int j = wave; j < n; j += kCombineWaves) {
+  for (int j = 0; j < kSplitsPerWave; ++j) {
+    if (j < n) {
       const float w = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv[k]), j));
-      const float* p = src + (size_t)(64 * k + j) * D;
-#pragma unroll
-      for (int e = 0; e < DT; ++e) {
-        const float x = p[e];
-        acc[e] += w > 0.0f ? w * x : 0.0f;
-      }
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsel), lane0 + j));
+      if (w > 0.0f) acc += w * x[j];
     }
   }
+
+  if (nwaves == 1) {
+    typedef _Float16 hv_t __attribute__((ext_vector_type(DT)));
+    hv_t y;
 #pragma unroll
-  for (int e = 0; e < DT; ++e) red[wave][lane * DT + e] = acc[e];
+    for (int e = 0; e < DT; ++e) y[e] = den > 0.0f ? (_Float16)(acc[e] / den) : (_Float16)0.0f;
+    *reinterpret_cast<hv_t*>(out + row * D + lane * DT) = y;
+    return;
+  }
+  *reinterpret_cast<fv_t*>(red + wave * D + lane * DT) = acc;
   __syncthreads();
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kCombineWaves; ++w) o += red[w][d];
+    for (int w = 0; w < nwaves; ++w) o += red[w * D + d];
     const _Float16 y = den > 0.0f ? (_Float16)(o / den) : (_Float16)0.0f;
     out[row * D + d] = __builtin_bit_cast(uint16_t, y);
   }
@@ -86,13 +100,15 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
 
 hipError_t launch_combine(const float* part_o, const float* part_ml, uint16_t* out,
                           int rows, int head_dim, int num_splits, hipStream_t stream) {
-  if (num_splits > 64 * kMaxSplitSlots) return hipErrorInvalidValue;
-  const dim3 grid(rows), block(64 * kCombineWaves);
+  if (num_splits < 1 || num_splits > 64 * kMaxSplitSlots) return hipErrorInvalidValue;
+  const int waves = (num_splits + kSplitsPerWave - 1) / kSplitsPerWave;
+  const dim3 grid(rows), block(64 * waves);
+  const size_t lds = waves > 1 ? (size_t)waves * head_dim * sizeof(float) : 0;
   if (head_dim == 128) {
-    hipLaunchKernelGGL(pda_combine_kernel<128>, grid, block, 0, stream, part_o, part_ml, out,
+    hipLaunchKernelGGL(pda_combine_kernel<128>, grid, block, lds, stream, part_o, part_ml, out,
                        num_splits);
   } else if (head_dim == 256) {
-    hipLaunchKernelGGL(pda_combine_kernel<256>, grid, block, 0, stream, part_o, part_ml, out,
+    hipLaunchKernelGGL(pda_combine_kernel<256>, grid, block, lds, stream, part_o, part_ml, out,
                        num_splits);
   } else {
     return hipErrorInvalidValue;

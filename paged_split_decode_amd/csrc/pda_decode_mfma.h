@@ -1,15 +1,21 @@
 // Paged split-K decode attention on the gfx950 matrix cores.
 //
-// Same operation and work split as the v_dot2 kernel (pda_decode_impl.h):
-// one workgroup per (split, KV head, sequence), each wave streaming a
-// contiguous run of pages with its own online softmax, waves merged through
-// LDS at the end. The difference is where the arithmetic runs. Counters on
-// the v_dot2 kernel show it issue-bound (about 480 VALU instructions per 8 KB
-// of K+V, VALU active half the time at one wave per SIMD), so both products
-// go to MFMA here and the VALU keeps only the softmax:
+// Work split: one workgroup per (split, group of KV heads, sequence). Its
+// waves are heads_per_group x key_waves: each KV head of the group gets
+// key_waves waves, each streaming a contiguous run of the split's pages with
+// its own online softmax. The waves of one workgroup read the same pages of
+// the pool at about the same time, one head's rows each, so the page blocks
+// (all heads of 16 slots, contiguous in memory) are fetched together. With
+// one wave per head a wave writes its result from registers; otherwise the
+// waves of a head merge through LDS.
+//
+// Counters on the v_dot2 kernel (pda_decode_impl.h) show it issue-bound
+// (about 480 VALU instructions per 8 KB of K+V, VALU active half the time at
+// one wave per SIMD), so both products go to MFMA here and the VALU keeps
+// only the softmax:
 //
 //  * Scores as S^T = K . Q^T with v_mfma_f32_16x16x32_f16: the page's 16 keys
-//    are the A rows, the group's query rows (up to 16 per row tile, zero
+//    are the A rows, the head's query rows (up to 16 per row tile, zero
 //    padded) the B columns. Lane (s = lane/16, c = lane%16) loads 16 bytes of
 //    key c per 32-dim step, so a wave instruction reads 16 keys x 64 bytes.
 //    The result leaves lane (s, c) holding row c's scores for keys 4s..4s+3.
@@ -48,16 +54,9 @@ struct MGeom {
   static constexpr int kRowBytes = D * kElemBytes;
 };
 
-// Waves per SIMD the register allocation must leave room for: two wherever
-// the working set fits in 256 registers (a second wave hides the first one's
-// memory and MFMA latency), one for fp16 at D=256 (its K+V ring alone is 128
-// registers) and for two row tiles.
-constexpr int mfma_min_waves(int D, int KV, int NRT) {
-  return (NRT == 1 && !(D == 256 && KV == kKvF16)) ? 2 : 1;
-}
-
 template <int D, int KV, int NRT>
-__global__ void __launch_bounds__(256, mfma_min_waves(D, KV, NRT))
+__global__ void __launch_bounds__(256 * mfma_waves_per_simd(D, KV, NRT),
+                                  mfma_waves_per_simd(D, KV, NRT))
 pda_decode_mfma_kernel(const DecodeArgs a) {
   using Mg = MGeom<D, KV>;
   constexpr int NS = Mg::kSteps;
@@ -71,12 +70,16 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
   const int s = lane >> 4;  // lane group: keys 4s..4s+3 of a page in the scores
   const int c = lane & 15;  // key of the page (loads) / query row (scores, output)
   const int split = blockIdx.x;
-  const int g = blockIdx.y;
   const int b = blockIdx.z;
+  const int KW = a.key_waves;   // waves sharing this KV head's key range
+  const int hw = wave / KW;     // head slot of this wave in the workgroup
+  const int kw = wave - hw * KW;
+  const int g_raw = blockIdx.y * a.heads_per_group + hw;
+  const bool head_ok = g_raw < a.num_kv_heads;  // the last group may be short
+  const int g = head_ok ? g_raw : 0;
   const int G = a.group;
   const int Hq = a.num_q_heads;
   const int S = a.num_splits;
@@ -103,9 +106,9 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   const int per_split = (nu + S - 1) / S;
   const int s_lo = u_lo + min(nu, split * per_split);
   const int ns = min(nu, (split + 1) * per_split) - min(nu, split * per_split);
-  const int per_wave = (ns + nwaves - 1) / nwaves;
-  const int w_lo = s_lo + min(ns, wave * per_wave);
-  int w_hi = s_lo + min(ns, (wave + 1) * per_wave);
+  const int per_wave = (ns + KW - 1) / KW;
+  const int w_lo = s_lo + min(ns, kw * per_wave);
+  int w_hi = s_lo + min(ns, (kw + 1) * per_wave);
 
   // Visibility bounds: uniform summary over the real rows (fast-path test),
   // and this lane's own rows (16 * rt + c) for masked pages.
@@ -120,7 +123,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
       any_active = true;
     }
   }
-  if (!any_active) w_hi = w_lo;
+  if (!any_active || !head_ok) w_hi = w_lo;
   const int n = w_hi - w_lo;
   int lo_c[NRT], hi_c[NRT];
 #pragma unroll
@@ -175,7 +178,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   for (int rt = 0; rt < NRT; ++rt) {
     const int row = 16 * rt + c;
     const int i = row / G;
-    const bool exists = row < R && i < Qb;
+    const bool exists = head_ok && row < R && i < Qb;
     const uint8_t* qrow = a.q + ((size_t)(off + i) * Hq + g * G + (row - i * G)) * (D * 2);
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
@@ -342,7 +345,44 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) l[rt] = add4(l[rt]);
 
-  // Merge the waves through LDS: per wave, rows [R] of (m, l, -, -, o[D]).
+  // One wave per head: write the result from registers (lane (s, c) holds
+  // row 16 rt + c, dims 16 dt + 4 s .. + 3).
+  if (KW == 1) {
+    if (!head_ok) return;
+    const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int row = 16 * rt + c;
+      const int i = row / G;
+      if (row >= R || i >= Qb) continue;
+      const size_t hrow = (size_t)(off + i) * Hq + g * G + (row - i * G);
+      const float lsum = l[rt];
+      if (a.direct) {
+        uint16_t* dst = a.out + hrow * D + 4 * s;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          h4_t y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[e] = lsum > 0.0f ? (_Float16)((o[rt][dt][e] * vs) / lsum) : (_Float16)0.0f;
+          *reinterpret_cast<h4_t*>(dst + 16 * dt) = y;
+        }
+      } else {
+        const size_t prow = hrow * S + split;
+        float* dst = a.part_o + prow * D + 4 * s;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f4_t*>(dst + 16 * dt) = o[rt][dt] * vs;
+        if (s == 0) {
+          a.part_ml[prow * 2] = lsum > 0.0f ? m[rt] : -INFINITY;
+          a.part_ml[prow * 2 + 1] = lsum;
+        }
+      }
+    }
+    return;
+  }
+
+  // Several waves per head: merge them through LDS; per wave, rows [R] of
+  // (m, l, -, -, o[D]).
   __syncthreads();  // every wave is done with its V tile (the region aliases)
   float* wm = reinterpret_cast<float*>(my_lds);
 #pragma unroll
@@ -358,29 +398,30 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   }
   __syncthreads();
 
-  const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
-  for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
-    const int row = idx / D;
-    const int d = idx - row * D;
+  const int HPW = a.heads_per_group;
+  for (int idx = threadIdx.x; idx < HPW * R * D; idx += blockDim.x) {
+    const int hs = idx / (R * D);
+    const int rem = idx - hs * (R * D);
+    const int row = rem / D;
+    const int d = rem - row * D;
+    const int gg = blockIdx.y * HPW + hs;
     const int i = row / G;
-    if (i >= Qb) continue;
-    const int h = g * G + (row - i * G);
+    if (gg >= a.num_kv_heads || i >= Qb) continue;
+    const int h = gg * G + (row - i * G);
     const int t = off + i;
-    const bool active = pos0 + i >= 0;
+    const int w0 = hs * KW;
     float M = -INFINITY;
-    for (int w = 0; w < nwaves; ++w)
+    for (int w = w0; w < w0 + KW; ++w)
       M = fmaxf(M, reinterpret_cast<const float*>(lds_raw + (size_t)w * wave_lds)[(size_t)row * (D + 4)]);
     float lsum = 0.0f, osum = 0.0f;
-    if (active) {
-      for (int w = 0; w < nwaves; ++w) {
-        const float* rec = reinterpret_cast<const float*>(lds_raw + (size_t)w * wave_lds) +
-                           (size_t)row * (D + 4);
-        const float wt = __builtin_amdgcn_exp2f(rec[0] - M);
-        lsum += wt * rec[1];
-        osum += wt * rec[4 + d];
-      }
+    for (int w = w0; w < w0 + KW; ++w) {
+      const float* rec = reinterpret_cast<const float*>(lds_raw + (size_t)w * wave_lds) +
+                         (size_t)row * (D + 4);
+      const float wt = __builtin_amdgcn_exp2f(rec[0] - M);
+      lsum += wt * rec[1];
+      osum += wt * rec[4 + d];
     }
-    osum *= vs;
+    osum *= a.v_scale ? a.v_scale[gg] : 1.0f;
     if (a.direct) {
       const _Float16 y = lsum > 0.0f ? (_Float16)(osum / lsum) : (_Float16)0.0f;
       a.out[((size_t)t * Hq + h) * D + d] = __builtin_bit_cast(uint16_t, y);

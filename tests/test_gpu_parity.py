@@ -87,7 +87,7 @@ def _random_case(seed):
     r = np.random.default_rng(500 + seed)
     D = int(r.choice([128, 256]))
     kv = str(r.choice(["f16", "fp8_e4m3", "int8"]))
-    Hkv = int(r.choice([1, 2, 4]))
+    Hkv = int(r.choice([1, 2, 3, 4, 5, 8, 12]))
     Q = int(r.choice([1, 1, 2, 3, 4]))
     max_g = max(1, 32 // Q)
     G = int(r.choice([g for g in (1, 2, 3, 4, 5, 6, 7, 8) if g <= max_g]))
@@ -106,6 +106,21 @@ def test_random_small_cases(seed, kernel):
     w = _random_case(seed)
     c = case_on_gpu(w)
     assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), w.kv_dtype, repr(w))
+
+
+@pytest.mark.parametrize("Hkv", [1, 3, 4, 5, 6, 8, 12, 16])
+@pytest.mark.parametrize("D,kv,G,Q", [(128, "f16", 4, 1), (256, "f16", 6, 1),
+                                      (256, "fp8_e4m3", 4, 1), (128, "int8", 7, 3),
+                                      (256, "f16", 5, 4)])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_kv_head_groups(Hkv, D, kv, G, Q, splits):
+    """KV heads are grouped into workgroups (one or several waves per head,
+    the last group possibly short); every head's rows must come out right,
+    written directly (one split) or through partials."""
+    w = small(23, head_dim=D, kv_dtype=kv, num_q_heads=G * Hkv, num_kv_heads=Hkv, q_len=Q,
+              seq_lens=(0, 45, 700, 129), num_splits=splits)
+    c = case_on_gpu(w)
+    assert_parity(run_gpu(c, kernel="matrix"), oracle_full(c), kv, repr(w))
 
 
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
@@ -283,7 +298,7 @@ def test_workspace_reuse(kernel, D):
 
 
 @pytest.mark.parametrize("D", [128, 256])
-@pytest.mark.parametrize("S", [1, 2, 7, 64])
+@pytest.mark.parametrize("S", [1, 2, 7, 16, 17, 64, 65, 200, 256])
 def test_split_combine_vs_oracle(D, S):
     g = torch.Generator(device=DEV).manual_seed(S * D)
     T, Hq = 5, 3
