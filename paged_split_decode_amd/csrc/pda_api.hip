@@ -65,6 +65,7 @@ struct Plan {
   int key_waves;       // waves per KV head (matrix) / per key range (v_dot2)
   int heads_per_group; // matrix kernel: KV heads per workgroup
   int head_groups;     // grid y: workgroups across the KV heads
+  int longest_first;   // matrix kernel: order grid rows by sequence length
   int splits;
   int threads;
   size_t lds;
@@ -153,6 +154,12 @@ void matrix_plan(const pda_decode_dims* d, int window, int num_splits, int num_c
   p->key_waves = kw;
   p->head_groups = (int)groups(hpw);
   p->splits = (int)S;
+  // With more workgroups than fit at once, dispatch the longest sequences
+  // first (ragged batches then finish together); with one round the order
+  // cannot matter.
+  const int64_t wgs = S * B * groups(hpw);
+  const int64_t wg_fit = (int64_t)num_cus * std::max(1, 4 * waves_per_simd / (hpw * kw));
+  p->longest_first = d->batch <= 64 && wgs > wg_fit;
 }
 
 pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_splits, int num_cus,
@@ -195,6 +202,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   p->wave_lds = 0;
   p->heads_per_group = 1;
   p->head_groups = d->num_kv_heads;
+  p->longest_first = 0;
   p->splits = num_splits >= 1
                   ? num_splits
                   : auto_splits(d, window, pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype)),
@@ -299,6 +307,8 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.row_groups = p.row_groups;
   a.key_waves = p.key_waves;
   a.heads_per_group = p.heads_per_group;
+  a.batch = d->batch;
+  a.longest_first = p.longest_first;
   a.rows = p.rows;
   a.wave_lds_bytes = (int32_t)p.wave_lds;
   return a;

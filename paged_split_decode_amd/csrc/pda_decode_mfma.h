@@ -54,6 +54,19 @@ struct MGeom {
   static constexpr int kRowBytes = D * kElemBytes;
 };
 
+// Pages in a wave's load ring (NB - 1 pages in flight while one is used).
+// Deeper rings measured no faster: a wave is issue-bound before it runs out
+// of bytes in flight. PDA_RING overrides it when tuning.
+template <int D, int KV, int NRT>
+constexpr int mfma_ring_depth() {
+#ifdef PDA_RING
+  return PDA_RING;
+#else
+  if (mfma_waves_per_simd(D, KV, NRT) == 2) return (D == 256 || NRT == 2) ? 2 : 3;
+  return D == 128 ? 3 : 2;
+#endif
+}
+
 template <int D, int KV, int NRT>
 __global__ void __launch_bounds__(256 * mfma_waves_per_simd(D, KV, NRT),
                                   mfma_waves_per_simd(D, KV, NRT))
@@ -64,7 +77,11 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   constexpr int VR = Mg::kVRaw;
   constexpr int NDT = Mg::kDTiles;
   constexpr int LR = Mg::kLdsRow;
-  constexpr int NB = D == 256 ? 2 : 3;  // ring depth (pages)
+  constexpr int NB = mfma_ring_depth<D, KV, NRT>();
+  // Hold all of a page's V fragments from the tile write to P.V, except where
+  // they do not fit beside the rest (two row tiles; D=256 at two waves per
+  // SIMD).
+  constexpr bool kHoistV = !(NRT == 2 || (D == 256 && mfma_waves_per_simd(D, KV, NRT) == 2));
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
 
@@ -73,7 +90,6 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   const int s = lane >> 4;  // lane group: keys 4s..4s+3 of a page in the scores
   const int c = lane & 15;  // key of the page (loads) / query row (scores, output)
   const int split = blockIdx.x;
-  const int b = blockIdx.z;
   const int KW = a.key_waves;   // waves sharing this KV head's key range
   const int hw = wave / KW;     // head slot of this wave in the workgroup
   const int kw = wave - hw * KW;
@@ -88,7 +104,25 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   uint8_t* my_lds = lds_raw + (size_t)wave * wave_lds;
   _Float16* vt = reinterpret_cast<_Float16*>(my_lds);
 
-  const int L = a.seq_lens[b];
+  // Sequence of this workgroup row. In a grid of several rounds, row z takes
+  // the sequence of z-th largest length (ties in index order), so the longest
+  // ones are dispatched first and the short ones fill in behind them.
+  int b = blockIdx.z;
+  int L;
+  if (a.longest_first) {
+    const int B = a.batch;
+    const int my_len = lane < B ? a.seq_lens[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = __builtin_amdgcn_readlane(my_len, j);
+      rank += (lj > my_len || (lj == my_len && j < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && rank == (int)blockIdx.z);
+    b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    L = __builtin_amdgcn_readlane(my_len, b);
+  } else {
+    L = a.seq_lens[b];
+  }
   const int Qb = a.q_lens ? a.q_lens[b] : 1;
   int off = b;
   if (a.q_lens) {
@@ -193,12 +227,19 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
+  // Online softmax with a lazily moved reference: p = 2^(score - m) with m a
+  // reference that trails the row's running maximum mx by at most kLazy (so
+  // p <= 2^kLazy, well inside fp16), and o, l are rescaled only when mx gets
+  // further ahead than that. The result is the same function; after the last
+  // page o and l are brought to m = mx once, so a split's m is its maximum.
   constexpr float kNoMax = -1e30f;
-  float m[NRT], l[NRT];
+  constexpr float kLazy = 8.0f;
+  float m[NRT], mx[NRT], l[NRT];
   f4_t o[NRT][NDT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     m[rt] = kNoMax;
+    mx[rt] = kNoMax;
     l[rt] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -233,6 +274,28 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
       }
     }
 
+    // The A operand of P.V (lane (s, c): V[4s + k][16 dt + c], k = 0..3) comes
+    // from the row-major tile with one transposing read per 16 dims: within
+    // each 16-lane group, ds_read_b64_tr_b16 hands lane i element i % 4 of the
+    // 8-byte rows addressed by lanes i/4 + 4k, so lane (s, c) points at row
+    // 4s + c/4, dims 16 dt + 4 (c % 4) .. + 3. Where registers allow, all
+    // reads are issued here, so their latency hides behind the scores and the
+    // softmax; the scheduling barrier keeps the compiler from sinking them
+    // next to their uses (which serializes one LDS round trip per read).
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+    auto read_va = [&](int dt) -> h4_t {
+      _Float16* src = vt + (4 * s + (c >> 2)) * LR + 16 * dt + 4 * (c & 3);
+      return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src));
+    };
+    h4_t va[kHoistV ? NDT : 1];
+    if constexpr (kHoistV) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) va[dt] = read_va(dt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     // Scores S^T[key 4s+i][row c] for every row tile.
     h8_t ka[NS];
 #pragma unroll
@@ -259,66 +322,73 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     }
 
     // Online softmax per row (lane-local row c; the max crosses lane groups).
-    bool rescale = false;
-    float alpha[NRT];
+    auto visible = [&](int rt, int i) {
+      const int j = j0 + 4 * s + i;
+      return j >= lo_c[rt] && j <= hi_c[rt];
+    };
+    bool behind = false;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      float mt;
+      if (full) {
+        mt = qk * max4(fmaxf(fmaxf(sc[rt][0], sc[rt][1]), fmaxf(sc[rt][2], sc[rt][3])));
+      } else {
+        mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, visible(rt, i) ? sc[rt][i] : -INFINITY);
+        mt = max4(mt);
+        mt = mt == -INFINITY ? kNoMax : qk * mt;
+      }
+      mx[rt] = fmaxf(mx[rt], mt);
+      behind |= mx[rt] > m[rt] + kLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(behind) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mx[rt]);
+        l[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
+        m[rt] = mx[rt];
+      }
+    }
     h4_t pb[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       float p[4];
-      if (full) {
-        float mt = fmaxf(fmaxf(sc[rt][0], sc[rt][1]), fmaxf(sc[rt][2], sc[rt][3]));
-        const float mn = fmaxf(m[rt], qk * max4(mt));
-        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mn);
-        rescale |= mn != m[rt];
-        m[rt] = mn;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -mn));
-      } else {
-        bool valid[4];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 4 * s + i;
-          valid[i] = j >= lo_c[rt] && j <= hi_c[rt];
-          mt = fmaxf(mt, valid[i] ? sc[rt][i] : -INFINITY);
-        }
-        mt = max4(mt);
-        const float mn = fmaxf(m[rt], mt == -INFINITY ? kNoMax : qk * mt);
-        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mn);
-        rescale |= mn != m[rt];
-        m[rt] = mn;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -mn));
-          p[i] = valid[i] ? e : 0.0f;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -m[rt]));
+        p[i] = (full || visible(rt, i)) ? e : 0.0f;
       }
-      l[rt] = __builtin_fmaf(l[rt], alpha[rt], (p[0] + p[1]) + (p[2] + p[3]));
+      l[rt] += (p[0] + p[1]) + (p[2] + p[3]);
       pb[rt] = h4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
     }
-    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha[rt];
-    }
 
-    // O^T[dims][rows] += V^T . P^T. The A operand (lane (s, c): V[4s + k][16 dt + c],
-    // k = 0..3) comes from the row-major LDS tile with one transposing read:
-    // within each 16-lane group, ds_read_b64_tr_b16 hands lane i element i % 4
-    // of the 8-byte rows addressed by lanes i/4 + 4k, so lane (s, c) points at
-    // row 4s + c/4, dims 16 dt + 4 (c % 4) .. + 3.
-    typedef short s4_t __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+    // O^T[dims][rows] += V^T . P^T. Without room to hold every V fragment,
+    // they are read in batches of 8 (4 with two row tiles), one LDS wait per
+    // batch.
+    if constexpr (kHoistV) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      _Float16* src = vt + (4 * s + (c >> 2)) * LR + 16 * dt + 4 * (c & 3);
-      const auto raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src);
-      const h4_t va = __builtin_bit_cast(h4_t, raw);
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[rt], o[rt][dt], 0, 0, 0);
+        for (int rt = 0; rt < NRT; ++rt)
+          o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[dt], pb[rt], o[rt][dt], 0, 0, 0);
+    } else {
+      constexpr int VB = NRT == 2 ? 4 : (NDT < 8 ? NDT : 8);
+#pragma unroll
+      for (int d0 = 0; d0 < NDT; d0 += VB) {
+        h4_t vb8[VB];
+#pragma unroll
+        for (int j = 0; j < VB; ++j) vb8[j] = read_va(d0 + j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < VB; ++j)
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            o[rt][d0 + j] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(vb8[j], pb[rt], o[rt][d0 + j], 0, 0, 0);
+      }
     }
   };
 
@@ -341,9 +411,18 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
       if (n_main + st < n) process_page(kb[st], vb[st], w_lo + n_main + st);
   }
 
-  // Denominators over the 4 lane groups; m is already the same in them.
+  // Bring o and l to the row maximum (m = mx unless the reference trails),
+  // then sum the denominators over the 4 lane groups; m and mx are already
+  // the same in them.
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) l[rt] = add4(l[rt]);
+  for (int rt = 0; rt < NRT; ++rt) {
+    const float alpha = __builtin_amdgcn_exp2f(m[rt] - mx[rt]);
+    l[rt] *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
+    m[rt] = mx[rt];
+    l[rt] = add4(l[rt]);
+  }
 
   // One wave per head: write the result from registers (lane (s, c) holds
   // row 16 rt + c, dims 16 dt + 4 s .. + 3).

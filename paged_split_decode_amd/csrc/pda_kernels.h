@@ -47,6 +47,9 @@ struct DecodeArgs {
   int32_t key_waves;           // waves sharing one KV head's key range
   int32_t heads_per_group;     // KV heads per workgroup (matrix kernel)
   int32_t direct;              // 1: write out (one split); 0: write partials
+  int32_t batch;               // B
+  int32_t longest_first;       // matrix kernel: grid row z takes the z-th longest
+                               // sequence (needs B <= 64)
   int32_t rows;                // G * max_q_len (matrix kernel)
   int32_t wave_lds_bytes;      // LDS bytes per wave (matrix kernel)
 };
@@ -74,11 +77,12 @@ hipError_t launch_decode_mfma_i8(int head_dim, int row_tiles, dim3 grid, int thr
                                  size_t lds, hipStream_t stream, const DecodeArgs& args);
 // Waves per SIMD the matrix kernel's register allocation leaves room for:
 // two wherever the working set fits in 256 registers (a second wave hides the
-// first one's memory and MFMA latency), one for fp16 at D=256 (its K+V ring
-// alone is 128 registers) and for two row tiles. A workgroup holds at most
-// 4 x this many waves.
+// first one's memory and MFMA latency); one for fp16 at D=256 (its K+V ring
+// alone is 128 registers) and for two row tiles except with 1-byte KV at
+// D=128. A workgroup holds at most 4 x this many waves.
 constexpr int mfma_waves_per_simd(int head_dim, int kv_kind, int row_tiles) {
-  return (row_tiles == 1 && !(head_dim == 256 && kv_kind == kKvF16)) ? 2 : 1;
+  if (row_tiles == 1) return (head_dim == 256 && kv_kind == kKvF16) ? 1 : 2;
+  return (head_dim == 128 && kv_kind != kKvF16) ? 2 : 1;
 }
 
 // LDS bytes one wave of the matrix kernel needs: its fp16 V tile (16 rows of

@@ -123,6 +123,20 @@ def test_kv_head_groups(Hkv, D, kv, G, Q, splits):
     assert_parity(run_gpu(c, kernel="matrix"), oracle_full(c), kv, repr(w))
 
 
+@pytest.mark.parametrize("D,kv,G,Q", [(128, "f16", 7, 3), (256, "f16", 6, 1),
+                                      (256, "int8", 4, 1)])
+@pytest.mark.parametrize("splits", [64, 200])
+def test_longest_first_order(D, kv, G, Q, splits):
+    """Grids of several rounds order their rows by sequence length (ragged
+    lengths with ties and empty sequences); every sequence must still get its
+    own rows."""
+    lens = (900, 0, 33, 900, 1, 410, 0, 77, 900, 256, 16, 17, 640, 5, 129, 900, 2, 300, 31, 64)
+    w = small(31, head_dim=D, kv_dtype=kv, num_q_heads=G * 4, num_kv_heads=4, q_len=Q,
+              seq_lens=lens, num_splits=splits, pool_pages=1024)
+    c = case_on_gpu(w)
+    assert_parity(run_gpu(c, kernel="matrix"), oracle_full(c), kv, repr(w))
+
+
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("G,Q", [(1, 1), (4, 1), (6, 1), (8, 1), (7, 3), (8, 4), (5, 2)])
