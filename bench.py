@@ -55,12 +55,17 @@ CELLS = [
 ]
 
 
+# Sources the decode step is built from (kernels, their launch plan, combine).
+DECODE_SOURCES = ("pda_kernels.h", "pda_decode_impl.h", "pda_decode_mfma.h", "pda_decode_f16.hip",
+                  "pda_decode_fp8.hip", "pda_decode_i8.hip", "pda_api.hip", "pda_combine.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of every HIP source of the library: counter figures recorded for
+    """Hash of the HIP sources of the decode step: counter figures recorded for
     one hash do not describe a kernel built from different sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_split_decode_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in DECODE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
