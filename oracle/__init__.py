@@ -18,3 +18,9 @@ from .attention import (  # noqa: F401
     paged_decode_attention_split,
     split_combine,
 )
+from .kv_writer import (  # noqa: F401
+    encode_e4m3fn,
+    encode_int8,
+    quantize,
+    write_kv_cache,
+)
