@@ -172,6 +172,44 @@ pda_status pda_split_combine(const float* partial_o, const float* partial_ml,
                              int32_t head_dim, int32_t num_splits,
                              hipStream_t stream);
 
+/* Sizes of a cache write. */
+typedef struct pda_cache_dims {
+  int32_t num_tokens;   /* T: rows of key / value (0: nothing to do) */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* D: a multiple of 8 */
+  int32_t page_size;    /* P >= 1 */
+  int32_t num_pages;    /* pages in each cache; num_pages * P must fit in int32 */
+  int32_t kv_dtype;     /* a pda_kv_dtype: the element type of both caches */
+} pda_cache_dims;
+
+/*
+ * KV-cache writer: stores the K and V rows of T new tokens in the paged
+ * caches, in the layout the decode entry points read (the cache writer's
+ * layout that PR #33's "Test Plan" checks the decode against; fp8 and int8
+ * caches as in its "Purpose" section).
+ *
+ *  key, value    fp16 [T, Hkv, D], 16-byte aligned.
+ *  slot_mapping  int32 [T]: token t goes to slot s = page * P + position,
+ *                i.e. row [s / P, s % P, :, :] of each cache. Tokens with
+ *                s < 0 (padding) or s >= num_pages * P are not written.
+ *  k_cache       [num_pages, P, Hkv, D] of kv_dtype, written in place; only
+ *  v_cache       the rows of written slots change. 16-byte aligned (fp16) or
+ *                8-byte aligned (fp8 / int8).
+ *  k_scale       fp32 [Hkv] for fp8 / int8 caches (NULL for fp16).
+ *  v_scale
+ *
+ * fp16 caches store the values unchanged. A quantized code is q = x / scale
+ * (fp32, IEEE division), clamped to the largest finite magnitude (448 for
+ * e4m3fn, 127 for int8; -128 is never written) and rounded to the nearest
+ * code, ties to even. Inputs must be finite. Two tokens mapped to the same
+ * slot race (either may win). One launch on `stream`.
+ */
+pda_status pda_write_kv_cache(const void* key, const void* value,
+                              const int32_t* slot_mapping, void* k_cache,
+                              void* v_cache, const float* k_scale,
+                              const float* v_scale, const pda_cache_dims* dims,
+                              hipStream_t stream);
+
 /* Split count a call with these sizes uses: `num_splits` itself when it is
  * >= 1, otherwise the automatic choice for a device with `num_cus` compute
  * units (num_cus <= 0: the current device's count). Host-only; no launch.

@@ -15,7 +15,7 @@ what the decode side reads:
 
   * layout [num_pages, P, Hkv, D] per cache; token t's rows go to page
     slot_mapping[t] // P, slot slot_mapping[t] % P; a negative slot means the
-    token is not written (padding);
+    token is not written (padding), and so does a slot past the pool's end;
   * fp16 caches store the fp16 inputs unchanged;
   * a quantized code is q = x / scale[h] computed in fp32 (the fp16 input
     widened exactly, IEEE division), then rounded to the nearest code with
@@ -89,7 +89,8 @@ def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, kv_dtype="f16",
     """Returns copies of (k_cache, v_cache) [num_pages, P, Hkv, D] with token
     t's rows key[t], value[t] ([T, Hkv, D] fp16) stored at slot
     slot_mapping[t] (page = slot // P, position in page = slot % P); tokens
-    with a negative slot are skipped. fp16 caches take the values as they
+    with a negative slot, or one past the pool's num_pages * P slots, are
+    skipped. fp16 caches take the values as they
     are; fp8/int8 caches take quantize(row, scale, kv_dtype) as uint8 codes."""
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
@@ -97,7 +98,7 @@ def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, kv_dtype="f16",
     key = np.asarray(key, dtype=np.float16)
     value = np.asarray(value, dtype=np.float16)
     for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
-        if slot < 0:
+        if slot < 0 or slot >= kc.shape[0] * P:
             continue
         page, pos = divmod(int(slot), P)
         if kv_dtype == "f16":

@@ -47,6 +47,11 @@ class DecodeDims(ctypes.Structure):
         "num_pages", "max_pages_per_seq", "max_q_len", "kv_dtype", "kernel")]
 
 
+class CacheDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "num_kv_heads", "head_dim", "page_size", "num_pages", "kv_dtype")]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 _VP, _I32P = ctypes.c_void_p, ctypes.c_void_p
@@ -65,6 +70,8 @@ _SIGNATURES = {
                                                    ctypes.c_int32]),
     "pda_decode_workspace_bytes": (ctypes.c_int64, [_DIMS, ctypes.c_int32, ctypes.c_int32]),
     "pda_decode_partials_bytes": (ctypes.c_int64, [_DIMS, ctypes.c_int32, ctypes.c_int32]),
+    "pda_write_kv_cache": (ctypes.c_int, [
+        _VP, _VP, _I32P, _VP, _VP, _VP, _VP, ctypes.POINTER(CacheDims), _VP]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -204,6 +211,32 @@ def split_combine(partial_o, partial_ml, out, num_splits: int, stream=None):
     T, Hq, D = out.shape
     _check(lib.pda_split_combine(_ptr(partial_o), _ptr(partial_ml), _ptr(out), T, Hq, D,
                                  int(num_splits), _stream(stream)))
+
+
+def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
+                   kv_dtype=None, stream=None):
+    """Store new tokens' rows key[t], value[t] (fp16 [T, Hkv, D]) at slot
+    slot_mapping[t] (int32 [T]; page * P + position, negative: skipped) of
+    the caches [num_pages, P, Hkv, D], quantizing to fp8-e4m3 / int8 codes
+    with the per-KV-head fp32 scales for quantized caches (see
+    include/pda.h). Writes the caches in place and returns None."""
+    lib = load_library()
+    _contig(key, value, slot_mapping, k_cache, v_cache, k_scale, v_scale)
+    if slot_mapping.dtype != torch.int32:
+        raise ValueError("slot_mapping must be int32")
+    if key.dtype != torch.float16 or value.dtype != torch.float16:
+        raise ValueError("key and value must be float16")
+    T, Hkv, D = key.shape
+    if tuple(value.shape) != (T, Hkv, D) or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("value must match key's shape and slot_mapping must be [T]")
+    num_pages, P, Hkv_c, D_c = k_cache.shape
+    if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [num_pages, P, Hkv, D] matching key")
+    dims = CacheDims(num_tokens=T, num_kv_heads=Hkv, head_dim=D, page_size=P,
+                     num_pages=num_pages, kv_dtype=_kv_code(k_cache, kv_dtype))
+    _check(lib.pda_write_kv_cache(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                  ctypes.byref(dims), _stream(stream)))
 
 
 def partials_views(workspace: torch.Tensor, num_tokens: int, num_q_heads: int,

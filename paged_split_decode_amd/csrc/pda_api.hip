@@ -12,11 +12,13 @@
 #include "pda.h"
 #include "pda_kernels.h"
 
+namespace pda {
+
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-pda_status fail(pda_status st, const char* fmt, ...) {
+int host_fail(int st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -24,6 +26,17 @@ pda_status fail(pda_status st, const char* fmt, ...) {
   va_end(ap);
   g_last_error = buf;
   return st;
+}
+
+const char* host_last_error() { return g_last_error.c_str(); }
+
+}  // namespace pda
+
+namespace {
+
+template <typename... Args>
+pda_status fail(pda_status st, const char* fmt, Args... args) {
+  return static_cast<pda_status>(pda::host_fail(st, fmt, args...));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -450,7 +463,7 @@ int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
   return st == PDA_OK ? attention_workspace_bytes(dims, splits) : st;
 }
 
-const char* pda_last_error(void) { return g_last_error.c_str(); }
+const char* pda_last_error(void) { return pda::host_last_error(); }
 
 const char* pda_version(void) { return "pda 0.1.0 gfx950"; }
 

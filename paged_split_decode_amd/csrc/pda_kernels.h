@@ -100,6 +100,11 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
   return (size_t)waves * rows_per_wave * (head_dim + 2) * sizeof(float);
 }
 
+// Host-side error state shared by every entry point: records a message for
+// pda_last_error() and returns `status`.
+int host_fail(int status, const char* fmt, ...);
+const char* host_last_error();
+
 hipError_t launch_combine(const float* part_o, const float* part_ml,
                           uint16_t* out, int rows, int head_dim, int num_splits,
                           hipStream_t stream);

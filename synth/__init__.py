@@ -13,4 +13,6 @@ from .workloads import (  # noqa: F401
     make_case,
     algorithmic_bytes,
     unit_subcase,
+    WriteCase,
+    make_write_case,
 )

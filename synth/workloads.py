@@ -291,3 +291,73 @@ def algorithmic_bytes(case: Case) -> int:
     keys = sum(visible_keys_of_sequence(int(L), int(Q), case.window)
                for L, Q in zip(case.seq_lens_host, case.q_lens_host))
     return keys * Hkv * D * e * 2 + case.num_tokens * Hq * D * 2 * 2
+
+
+# ---------------------------------------------------------------------------
+# Cache-writer inputs
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class WriteCase:
+    """Inputs of one cache write: new rows, their slots, poisoned caches."""
+    key: torch.Tensor           # fp16 [T, Hkv, D]
+    value: torch.Tensor         # fp16 [T, Hkv, D]
+    slot_mapping: torch.Tensor  # int32 [T]
+    k_cache: torch.Tensor       # [num_pages, P, Hkv, D] fp16 or uint8 codes
+    v_cache: torch.Tensor
+    k_scale: Optional[torch.Tensor]  # fp32 [Hkv] or None
+    v_scale: Optional[torch.Tensor]
+    kv_dtype: str
+
+    def host(self) -> dict:
+        np_ = lambda t: None if t is None else t.detach().cpu().numpy()
+        return dict(key=np_(self.key), value=np_(self.value), slot_mapping=np_(self.slot_mapping),
+                    k_cache=np_(self.k_cache), v_cache=np_(self.v_cache), kv_dtype=self.kv_dtype,
+                    k_scale=np_(self.k_scale), v_scale=np_(self.v_scale))
+
+
+def make_write_case(num_tokens, num_kv_heads, head_dim, page_size, num_pages, kv_dtype,
+                    seed, skip_frac=0.1, values=None, scale=None, device="cpu") -> WriteCase:
+    """Seeded writer inputs. Rows are N(0,1) fp16 (or `values`, an fp16 array
+    of T*Hkv*D elements laid out in order); slots are distinct and random in
+    the pool, with about `skip_frac` of them negative and a few past the
+    pool's end. Scales for quantized caches are `scale` (a number) or the
+    per-KV-head amax of the rows over the format's largest code. Caches start
+    poisoned (NaN / code 0x7F / 127)."""
+    rng = np.random.default_rng(seed)
+    T, Hkv, D, P = num_tokens, num_kv_heads, head_dim, page_size
+    if values is None:
+        key = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+        value = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    else:
+        key = np.asarray(values, np.float16).reshape(T, Hkv, D)
+        value = key[::-1].copy()
+    n_slots = num_pages * P
+    assert T <= n_slots, "distinct slots need num_pages * page_size >= num_tokens"
+    slots = rng.choice(n_slots, size=T, replace=False).astype(np.int64)
+    if T:
+        slots[rng.random(T) < skip_frac] = -1
+        slots[rng.random(T) < skip_frac / 4] = n_slots + int(rng.integers(0, 5))
+    k_scale = v_scale = None
+    if kv_dtype != "f16":
+        top = 448.0 if kv_dtype == "fp8_e4m3" else 127.0
+        if scale is None:
+            amax = lambda x: np.abs(x.astype(np.float32)).max(axis=(0, 2), initial=0.0)
+            k_scale = (amax(key) / top).astype(np.float32)
+            v_scale = (amax(value) / top).astype(np.float32)
+            k_scale[k_scale == 0] = 1.0
+            v_scale[v_scale == 0] = 1.0
+        else:
+            k_scale = np.full(Hkv, scale, np.float32)
+            v_scale = np.full(Hkv, scale, np.float32)
+    shape = (num_pages, P, Hkv, D)
+    if kv_dtype == "f16":
+        kc = np.full(shape, np.uint16(F16_NAN_BITS)).view(np.float16)
+    else:
+        kc = np.full(shape, _poison_value(kv_dtype), np.uint8)
+    vc = kc.copy()
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return WriteCase(key=t(key), value=t(value), slot_mapping=t(slots.astype(np.int32)),
+                     k_cache=t(kc), v_cache=t(vc), k_scale=t(k_scale), v_scale=t(v_scale),
+                     kv_dtype=kv_dtype)

@@ -105,3 +105,45 @@ def test_split_policy_and_workspace():
     assert pda.partials_bytes(d, 0, 1) == 8 * 32 * 1 * (128 + 2) * 4
     tiny = _dims(batch=1, num_tokens=1, max_pages_per_seq=1)
     assert pda.resolve_splits(tiny, 0, 0, 256) == 1
+
+
+def _cdims(**kw):
+    base = dict(num_tokens=4, num_kv_heads=8, head_dim=128, page_size=16, num_pages=64,
+                kv_dtype=0)
+    base.update(kw)
+    return pda.CacheDims(**base)
+
+
+def _wcall(dims, **over):
+    args = dict(key=FAKE, value=FAKE, slots=FAKE, kc=FAKE, vc=FAKE, ks=None, vs=None)
+    args.update(over)
+    return pda.load_library().pda_write_kv_cache(
+        args["key"], args["value"], args["slots"], args["kc"], args["vc"], args["ks"],
+        args["vs"], None if dims is None else ctypes.byref(dims), None)
+
+
+@pytest.mark.parametrize("dims_kw,over,status", [
+    (dict(head_dim=100), {}, -4),               # not a multiple of 8
+    (dict(kv_dtype=5), {}, -4),
+    (dict(num_kv_heads=0), {}, -2),
+    (dict(page_size=0), {}, -2),
+    (dict(num_tokens=-1), {}, -2),
+    (dict(num_pages=1 << 28, page_size=16), {}, -2),  # slots would overflow int32
+    ({}, dict(slots=None), -1),
+    ({}, dict(kc=None), -1),
+    (dict(kv_dtype=1), {}, -1),                 # fp8 without scales
+    (dict(kv_dtype=2), dict(ks=FAKE), -1),      # int8 with one scale missing
+    ({}, dict(ks=FAKE, vs=FAKE), -2),           # scales with fp16
+    ({}, dict(key=ctypes.c_void_p(0x100008)), -3),
+    ({}, dict(kc=ctypes.c_void_p(0x100008)), -3),  # fp16 cache needs 16 bytes
+])
+def test_writer_validation_errors(dims_kw, over, status):
+    st = _wcall(_cdims(**dims_kw), **over)
+    assert st == status, (st, pda.load_library().pda_last_error())
+    assert pda.load_library().pda_last_error()
+
+
+def test_writer_null_dims_and_empty_batch():
+    assert _wcall(None) == -1
+    # no tokens: nothing to write, no pointer is looked at
+    assert _wcall(_cdims(num_tokens=0), key=None, value=None, slots=None, kc=None, vc=None) == 0
