@@ -241,6 +241,58 @@ def cpu_baseline(case, budget_s: float = 12.0):
                       f"{el:.1f} s"}
 
 
+# Cache-writer cells: (tokens, KV heads, head dim, kv dtype): the new tokens of
+# the fp8 long-context decode step, and prefill-sized writes.
+WRITER_CELLS = [
+    (64, 4, 256, "fp8_e4m3"),
+    (32768, 8, 128, "f16"),
+    (32768, 4, 256, "fp8_e4m3"),
+    (32768, 4, 256, "int8"),
+]
+
+
+def measure_writer(T, Hkv, D, kv, steps, device):
+    """One pda_write_kv_cache call per step over seeded rows (replicated past
+    1 GiB so steps do not hit in the Infinity Cache). Bytes: the fp16 rows
+    read, the cache rows written, the slots."""
+    import torch
+
+    import paged_split_decode_amd as pda
+    from synth import make_write_case
+
+    P = 16
+    c = make_write_case(T, Hkv, D, P, num_pages=-(-T // P) + 1, kv_dtype=kv, seed=T + D,
+                        skip_frac=0.0, device=device)
+    e = 2 if kv == "f16" else 1
+    nbytes = T * Hkv * D * (2 + e) * 2 + T * 4
+    per = nbytes - T * 4
+    reps = max(1, min(16, math.ceil((1 << 30) / per)))
+    sets = [(c.key, c.value, c.k_cache, c.v_cache)]
+    for _ in range(reps - 1):
+        sets.append((c.key.clone(), c.value.clone(), c.k_cache.clone(), c.v_cache.clone()))
+
+    def run(i):
+        k, v, kc, vc = sets[i % reps]
+        pda.write_kv_cache(k, v, c.slot_mapping, kc, vc, c.k_scale, c.v_scale, kv_dtype=kv)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    _hold_gpu()
+    t0.record()
+    for i in range(steps):
+        run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / steps * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"op": "write_kv_cache", "tokens": T, "num_kv_heads": Hkv, "head_dim": D,
+            "kv_dtype": kv, "page_size": P, "us_per_call": round(us, 2), "GB_s": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
+
+
 def cell_record(name, w, m):
     us = m["ms_per_step"] * 1e3
     gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
@@ -332,6 +384,12 @@ def main(argv=None):
             del c
             torch.cuda.empty_cache()
         rec["cells"] = cells
+        rec["writer_cells"] = []
+        for (T, Hkv, D, kv) in WRITER_CELLS:
+            rw = measure_writer(T, Hkv, D, kv, max(10, args.steps // 4), device)
+            rec["writer_cells"].append(rw)
+            print(json.dumps({"writer_cell": rw}), file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
         case = make_case(w, device=device)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(case)
