@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     decode_int8,
     dequantize,
     visible_range,
+    as_nhd,
     paged_decode_attention,
     paged_decode_attention_split,
     split_combine,

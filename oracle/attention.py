@@ -32,7 +32,14 @@ brute force, torch's attention and invariants.
 
 Layouts (all contiguous):
     q            float16 [T, Hq, D], T = sum(q_lens), sequences packed in order
-    k_cache      [num_pages, P, Hkv, D]: float16, or uint8 codes for fp8/int8
+    k_cache      [num_pages, P, Hkv, D] ("NHD": page, slot, KV head, dim), or
+                 [num_pages, Hkv, P, D] ("HND": page, KV head, slot, dim) with
+                 kv_layout="HND": float16, or uint8 codes for fp8/int8. The
+                 pages name the cache writer's layout and a "dense" layout
+                 without defining either (pull request #33, "Test Plan"); NHD
+                 is the plainest reading of the writer's, HND the other common
+                 paged layout. Both hold the same key: HND is NHD with the
+                 slot and head axes exchanged, which is how it is read here.
     v_cache      same as k_cache
     block_table  int32 [B, max_pages_per_seq]
     seq_lens     int32 [B]
@@ -125,6 +132,16 @@ def _gather_keys(cache, block_table_row, seq_len, g, kv_dtype, scale):
     return dequantize(rows, kv_dtype, scale)
 
 
+def as_nhd(cache, kv_layout="NHD"):
+    """The cache seen as [num_pages, P, Hkv, D] (a view; HND swaps the slot
+    and head axes)."""
+    if kv_layout == "NHD":
+        return cache
+    if kv_layout == "HND":
+        return np.swapaxes(cache, 1, 2)
+    raise ValueError(kv_layout)
+
+
 def _check(q, k_cache, v_cache, block_table, seq_lens, q_lens):
     T, Hq, D = q.shape
     num_pages, P, Hkv, Dk = k_cache.shape
@@ -143,12 +160,13 @@ def _check(q, k_cache, v_cache, block_table, seq_lens, q_lens):
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens,
                            scale, window=0, kv_dtype="f16", k_scale=None,
-                           v_scale=None, units=None):
+                           v_scale=None, units=None, kv_layout="NHD"):
     """One-shot masked softmax attention over the gathered keys, in float64.
 
     Returns float64 [T, Hq, D]. ``units`` optionally restricts the work to a
     set of (b, g) pairs (sequence, KV head); rows of other units are NaN.
     """
+    k_cache, v_cache = as_nhd(k_cache, kv_layout), as_nhd(v_cache, kv_layout)
     T, Hq, D, P, Hkv, G, B, q_lens = _check(q, k_cache, v_cache, block_table,
                                              seq_lens, q_lens)
     q64 = decode_f16(q)
@@ -185,7 +203,8 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens,
 
 def paged_decode_attention_split(q, k_cache, v_cache, block_table, seq_lens,
                                  q_lens, scale, window=0, num_splits=1,
-                                 kv_dtype="f16", k_scale=None, v_scale=None):
+                                 kv_dtype="f16", k_scale=None, v_scale=None,
+                                 kv_layout="NHD"):
     """Split-K form of the same attention: the keys any token of a sequence
     can see, [lo of token 0, L), are cut into ``num_splits`` contiguous
     chunks (chunks may be empty); each chunk yields, per row, its running
@@ -195,6 +214,7 @@ def paged_decode_attention_split(q, k_cache, v_cache, block_table, seq_lens,
     across workgroups and merges the splits (pull request #33, "Purpose" and
     "Test Result"); this model exists to show that the result does not
     depend on the split count."""
+    k_cache, v_cache = as_nhd(k_cache, kv_layout), as_nhd(v_cache, kv_layout)
     T, Hq, D, P, Hkv, G, B, q_lens = _check(q, k_cache, v_cache, block_table,
                                              seq_lens, q_lens)
     S = int(num_splits)

@@ -28,6 +28,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .attention import as_nhd
+
 E4M3_MAX = 448.0
 E4M3_MIN_NORMAL_EXP = -6  # smallest normal exponent (bias 7, exponent field 1)
 E4M3_MANT_BITS = 3
@@ -85,15 +87,18 @@ def quantize(x_f16: np.ndarray, scale: np.ndarray, kv_dtype: str) -> np.ndarray:
 
 
 def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, kv_dtype="f16",
-                   k_scale=None, v_scale=None):
+                   k_scale=None, v_scale=None, kv_layout="NHD"):
     """Returns copies of (k_cache, v_cache) [num_pages, P, Hkv, D] with token
     t's rows key[t], value[t] ([T, Hkv, D] fp16) stored at slot
     slot_mapping[t] (page = slot // P, position in page = slot % P); tokens
     with a negative slot, or one past the pool's num_pages * P slots, are
     skipped. fp16 caches take the values as they
-    are; fp8/int8 caches take quantize(row, scale, kv_dtype) as uint8 codes."""
-    kc = np.array(k_cache, copy=True)
-    vc = np.array(v_cache, copy=True)
+    are; fp8/int8 caches take quantize(row, scale, kv_dtype) as uint8 codes.
+    With kv_layout="HND" the caches are [num_pages, Hkv, P, D] and are
+    written through the slot/head-swapped view."""
+    kc_out = np.array(k_cache, copy=True)
+    vc_out = np.array(v_cache, copy=True)
+    kc, vc = as_nhd(kc_out, kv_layout), as_nhd(vc_out, kv_layout)  # views
     P = kc.shape[1]
     key = np.asarray(key, dtype=np.float16)
     value = np.asarray(value, dtype=np.float16)
@@ -107,4 +112,4 @@ def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, kv_dtype="f16",
         else:
             kc[page, pos] = quantize(key[t][None], k_scale, kv_dtype)[0]
             vc[page, pos] = quantize(value[t][None], v_scale, kv_dtype)[0]
-    return kc, vc
+    return kc_out, vc_out

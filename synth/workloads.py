@@ -52,6 +52,8 @@ class Workload:
     table_pad: int = 1  # extra block-table columns past the longest sequence
     scale: Optional[float] = None  # default 1/sqrt(D)
     seed: int = 0
+    layout: str = "NHD"  # "NHD": [pages, P, Hkv, D]; "HND": [pages, Hkv, P, D]
+    identity_table: bool = False  # pages in pool order instead of a permutation
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -98,7 +100,8 @@ WORKLOADS = {
 @dataclass
 class Case:
     """One generated input set. Tensors live on ``device``; q is float16
-    [T, Hq, D]; caches are float16 or uint8 codes [num_pages, P, Hkv, D]."""
+    [T, Hq, D]; caches are float16 or uint8 codes [num_pages, P, Hkv, D]
+    (or [num_pages, Hkv, P, D] for the HND layout)."""
     workload: Workload
     q: torch.Tensor
     k_cache: torch.Tensor
@@ -117,6 +120,10 @@ class Case:
     @property
     def kv_dtype(self) -> str:
         return self.workload.kv_dtype
+
+    @property
+    def kv_layout(self) -> str:
+        return self.workload.layout
 
     @property
     def num_tokens(self) -> int:
@@ -140,7 +147,7 @@ class Case:
                     block_table=np_(self.block_table), seq_lens=np_(self.seq_lens),
                     q_lens=np_(self.q_lens), scale=self.scale, window=self.window,
                     kv_dtype=self.kv_dtype, k_scale=np_(self.k_scale),
-                    v_scale=np_(self.v_scale))
+                    v_scale=np_(self.v_scale), kv_layout=self.kv_layout)
 
 
 def _seq_lens(w: Workload, rng: np.random.Generator) -> np.ndarray:
@@ -204,6 +211,8 @@ def make_case(w: Workload, device="cpu") -> Case:
     max_pages = int(max(1, pages_per_seq.max(initial=0))) + w.table_pad
 
     perm = rng.permutation(num_pages)
+    if w.identity_table:
+        perm = np.arange(num_pages)
     poison_page = int(perm[-1])
     table = np.full((B, max_pages), poison_page, np.int64)
     cursor = 0
@@ -234,6 +243,11 @@ def make_case(w: Workload, device="cpu") -> Case:
             k_cache[last, L % P:] = poison
             v_cache[last, L % P:] = poison
 
+    if w.layout == "HND":
+        k_cache = k_cache.permute(0, 2, 1, 3).contiguous()
+        v_cache = v_cache.permute(0, 2, 1, 3).contiguous()
+    elif w.layout != "NHD":
+        raise ValueError(w.layout)
     scale = w.scale if w.scale is not None else 1.0 / math.sqrt(D)
     return Case(
         workload=w, q=q, k_cache=k_cache, v_cache=v_cache,
@@ -248,21 +262,26 @@ def make_case(w: Workload, device="cpu") -> Case:
 def unit_subcase(case: Case, b: int, g: int) -> dict:
     """Inputs of one (sequence b, KV head g) unit as a self-contained host
     problem for the oracle: that sequence's pages of KV head g only, an
-    identity block table, and its G query heads. Lets the oracle check
-    sampled outputs of a full-size case without copying the whole pool."""
-    P = case.k_cache.shape[1]
-    Hq, Hkv = case.q.shape[1], case.k_cache.shape[2]
+    identity block table, and its G query heads, always in the NHD layout.
+    Lets the oracle check sampled outputs of a full-size case without copying
+    the whole pool."""
+    hnd = case.kv_layout == "HND"
+    P = case.k_cache.shape[2 if hnd else 1]
+    Hq, Hkv = case.q.shape[1], case.k_cache.shape[1 if hnd else 2]
     G = Hq // Hkv
     L = int(case.seq_lens_host[b])
     Q = int(case.q_lens_host[b])
     off = int(case.q_lens_host[:b].sum())
     n = -(-L // P)
     pages = case.block_table[b, :n].long()
-    k = case.k_cache.index_select(0, pages)[:, :, g:g + 1].cpu().numpy()
-    v = case.v_cache.index_select(0, pages)[:, :, g:g + 1].cpu().numpy()
-    if n == 0:  # keep one (unread) page so that shapes stay valid
-        k = case.k_cache[:1, :, g:g + 1].cpu().numpy()
-        v = case.v_cache[:1, :, g:g + 1].cpu().numpy()
+    def head(cache, idx):
+        x = cache.index_select(0, idx)
+        x = x[:, g:g + 1].transpose(1, 2) if hnd else x[:, :, g:g + 1]
+        return x.contiguous().cpu().numpy()
+
+    first = torch.zeros(1, dtype=torch.long, device=case.k_cache.device)
+    k = head(case.k_cache, pages if n else first)  # one (unread) page if empty
+    v = head(case.v_cache, pages if n else first)
     q = case.q[off:off + Q, g * G:(g + 1) * G].cpu().numpy()
     sel = lambda t: None if t is None else t[g:g + 1].cpu().numpy()  # noqa: E731
     return dict(q=q, k_cache=k, v_cache=v,

@@ -383,3 +383,82 @@ def test_split_combine_equals_one_shot_softmax():
 def test_split_combine_all_empty_is_zero():
     got = oracle.split_combine(np.full((3, 5), np.nan), np.full(3, -np.inf), np.zeros(3))
     assert np.array_equal(got, np.zeros(5))
+
+
+# ---------------------------------------------------------------------------
+# Layout and page-size variants
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("P", [32, 64])
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+def test_large_pages_vs_sdpa(P, kv):
+    h = _tiny(71 + P, page_size=P, seq_lens=(0, 5, 100, 200), q_len=3, window=70,
+              head_dim=16, kv_dtype=kv)
+    np.testing.assert_allclose(run_oracle(h), sdpa_reference(h), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kv", ["f16", "int8"])
+def test_hnd_layout_against_dense_attention(kv):
+    """Keys placed into an HND pool ([page, head, slot, dim]) by explicit
+    index arithmetic must give dense attention."""
+    r = np.random.default_rng(8)
+    B, Hkv, G, D, P, Q = 2, 3, 2, 8, 4, 2
+    lens = [13, 6]
+    num_pages = 8
+    perm = r.permutation(num_pages)
+    table = np.zeros((B, 4), np.int32)
+    table[0, :4], table[1, :2] = perm[:4], perm[4:6]
+    shape = (num_pages, Hkv, P, D)
+    if kv == "f16":
+        kc = np.full(shape, np.nan, np.float16)
+        vc = kc.copy()
+        dk = [r.standard_normal((L, Hkv, D)).astype(np.float16) for L in lens]
+        dv = [r.standard_normal((L, Hkv, D)).astype(np.float16) for L in lens]
+        ks = vs = None
+        val = lambda x, s: x.astype(np.float64)  # noqa: E731
+    else:
+        kc = np.full(shape, 127, np.uint8)
+        vc = kc.copy()
+        dk = [r.integers(-127, 128, (L, Hkv, D)).astype(np.int8).view(np.uint8) for L in lens]
+        dv = [r.integers(-127, 128, (L, Hkv, D)).astype(np.int8).view(np.uint8) for L in lens]
+        ks, vs = np.float32([0.02, 0.03, 0.05]), np.float32([0.1, 0.07, 0.04])
+        val = lambda x, s: x.view(np.int8).astype(np.float64) * s[:, None]  # noqa: E731
+    for b, L in enumerate(lens):
+        for j in range(L):
+            for g in range(Hkv):
+                kc[table[b, j // P], g, j % P] = dk[b][j, g]
+                vc[table[b, j // P], g, j % P] = dv[b][j, g]
+    q = r.standard_normal((B * Q, Hkv * G, D)).astype(np.float16)
+    got = oracle.paged_decode_attention(q, kc, vc, table, np.int32(lens), np.int32([Q, Q]), 0.3,
+                                        kv_dtype=kv, k_scale=ks, v_scale=vs, kv_layout="HND")
+    for b, L in enumerate(lens):
+        K, V = val(dk[b], ks), val(dv[b], vs)
+        for i in range(Q):
+            t, p = b * Q + i, L - Q + i
+            for h in range(Hkv * G):
+                sc = float(np.float32(0.3))  # the caller's fp32 scale, widened
+                s = [sc * float(np.dot(q[t, h].astype(np.float64), K[j, h // G]))
+                     for j in range(p + 1)]
+                m = max(s)
+                w = np.array([math.exp(x - m) for x in s])
+                ref = (w[:, None] * V[:p + 1, h // G]).sum(0) / w.sum()
+                np.testing.assert_allclose(got[t, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_hnd_writer_places_rows_by_index():
+    r = np.random.default_rng(9)
+    num_pages, Hkv, P, D, T = 5, 2, 4, 8, 11
+    key = r.standard_normal((T, Hkv, D)).astype(np.float16)
+    val = r.standard_normal((T, Hkv, D)).astype(np.float16)
+    slots = r.choice(num_pages * P, T, replace=False)
+    slots[3] = -1
+    kc0 = np.zeros((num_pages, Hkv, P, D), np.float16)
+    kc, vc = oracle.write_kv_cache(key, val, slots, kc0, kc0.copy(), kv_layout="HND")
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        for g in range(Hkv):
+            assert kc[s // P, g, s % P].tobytes() == key[t, g].tobytes()
+            assert vc[s // P, g, s % P].tobytes() == val[t, g].tobytes()
+    assert np.count_nonzero(kc) == np.count_nonzero(key[slots >= 0])
