@@ -46,6 +46,11 @@ CELLS = [
     # the headline shape with a caller split count inside the 1..8 range its
     # configuration names for automatic splitting
     ("gqa4_d128_b8_l4096", dict(num_splits=8)),
+    # the headline shape in the other cache layouts: HND ([page, head, slot,
+    # dim]), 64-key pages, and an identity block table (pages in pool order)
+    ("gqa4_d128_b8_l4096", dict(layout="HND")),
+    ("gqa4_d128_b8_l4096", dict(page_size=64)),
+    ("gqa4_d128_b8_l4096", dict(identity_table=True)),
     # D=256 batch sweep, without and with a 4096-key sliding window
     *[("gqa6_d256_l16384", dict(batch=b, window=win))
       for win in (0, 4096) for b in (1, 2, 3, 8, 32)],
@@ -99,7 +104,7 @@ class Runner:
         self.case = case
         c = case
         self.dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
-                                    c.max_q_len, c.kv_dtype, kernel)
+                                    c.max_q_len, c.kv_dtype, kernel, c.kv_layout)
         self.S = pda.resolve_splits(self.dims, c.window, num_splits)
         T, Hq, D = c.q.shape
         self.T, self.Hq, self.D = T, Hq, D
@@ -298,7 +303,9 @@ def cell_record(name, w, m):
     gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
     dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
     return {"workload": name, "batch": w.batch, "window": w.window, "kv_dtype": w.kv_dtype,
-            "head_dim": w.head_dim, "splits": m["splits"], "us_per_call": round(us, 2),
+            "head_dim": w.head_dim, "page_size": w.page_size, "kv_layout": w.layout,
+            "identity_table": w.identity_table, "splits": m["splits"],
+            "us_per_call": round(us, 2),
             "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
             "decode_us": round(m["decode_ms"] * 1e3, 2), "decode_GB_s": round(dec_gbs, 1),

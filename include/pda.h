@@ -19,8 +19,9 @@
  * multi-token queries, split decode) are part of this contract.
  *
  * Work is split along the key axis into `num_splits` contiguous chunks per
- * (sequence, KV head); each chunk yields a partial (m, l, o) and a second
- * kernel merges the partials (the split-K combine of the same section).
+ * (sequence, KV head), aligned to 16 keys; each chunk yields a partial
+ * (m, l, o) and a second kernel merges the partials (the split-K combine of
+ * the same section).
  *
  * Conventions for every entry point
  *  - All tensors are contiguous, row-major, and live in device memory of the
@@ -70,6 +71,16 @@ typedef enum pda_kv_dtype {
   PDA_KV_INT8 = 2
 } pda_kv_dtype;
 
+/* Cache layout: where key j's row of KV head g sits inside its page.
+ *  PDA_LAYOUT_NHD: [num_pages, P, Hkv, D] (page, slot, KV head, dim), the
+ *    cache writer's layout (PR #33 "Test Plan").
+ *  PDA_LAYOUT_HND: [num_pages, Hkv, P, D] (page, KV head, slot, dim): each
+ *    head's rows of a page are contiguous. */
+typedef enum pda_kv_layout {
+  PDA_LAYOUT_NHD = 0,
+  PDA_LAYOUT_HND = 1
+} pda_kv_layout;
+
 /* Decode kernel family. Both compute the same function and are checked
  * against the same reference; they differ in where the arithmetic runs.
  *  PDA_KERNEL_VECTOR: scores with packed fp16 v_dot2 (fp32 accumulation) and
@@ -92,12 +103,14 @@ typedef struct pda_decode_dims {
   int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;      /* Hkv */
   int32_t head_dim;          /* D: 128 or 256 */
-  int32_t page_size;         /* P: keys per page; 16 */
+  int32_t page_size;         /* P: keys per page: 16, 32, 64, 128 or 256
+                                (16 only for PDA_KERNEL_VECTOR) */
   int32_t num_pages;         /* pages in each of the K and V pools */
   int32_t max_pages_per_seq; /* columns of block_table */
   int32_t max_q_len;         /* bound on q_lens[b]; 1 when q_lens is NULL */
   int32_t kv_dtype;          /* a pda_kv_dtype */
   int32_t kernel;            /* a pda_kernel: which decode kernel family runs */
+  int32_t kv_layout;         /* a pda_kv_layout (NHD only for PDA_KERNEL_VECTOR) */
 } pda_decode_dims;
 
 /* Largest (num_q_heads / num_kv_heads) * max_q_len a call accepts. */
@@ -110,8 +123,9 @@ typedef struct pda_decode_dims {
  *
  *  q            fp16 [T, Hq, D]; the tokens of sequence b are rows
  *               off_b .. off_b + q_lens[b] - 1, off_b = sum of q_lens[<b].
- *  k_cache      [num_pages, P, Hkv, D] of kv_dtype elements (page, slot,
- *  v_cache      KV head, dim): the cache writer's layout.
+ *  k_cache      [num_pages, P, Hkv, D] (NHD) or [num_pages, Hkv, P, D]
+ *  v_cache      (HND) of kv_dtype elements, per dims->kv_layout; one page
+ *               (P * Hkv * D elements) must be under 2 GiB.
  *  block_table  int32 [B, max_pages_per_seq]: key j of sequence b is slot
  *               j % P of page block_table[b][j / P].
  *  seq_lens     int32 [B]: keys held by each sequence, new tokens included.
@@ -180,6 +194,7 @@ typedef struct pda_cache_dims {
   int32_t page_size;    /* P >= 1 */
   int32_t num_pages;    /* pages in each cache; num_pages * P must fit in int32 */
   int32_t kv_dtype;     /* a pda_kv_dtype: the element type of both caches */
+  int32_t kv_layout;    /* a pda_kv_layout */
 } pda_cache_dims;
 
 /*
@@ -190,9 +205,11 @@ typedef struct pda_cache_dims {
  *
  *  key, value    fp16 [T, Hkv, D], 16-byte aligned.
  *  slot_mapping  int32 [T]: token t goes to slot s = page * P + position,
- *                i.e. row [s / P, s % P, :, :] of each cache. Tokens with
- *                s < 0 (padding) or s >= num_pages * P are not written.
- *  k_cache       [num_pages, P, Hkv, D] of kv_dtype, written in place; only
+ *                i.e. rows [s / P, s % P, :, :] (NHD) or [s / P, :, s % P, :]
+ *                (HND) of each cache. Tokens with s < 0 (padding) or
+ *                s >= num_pages * P are not written.
+ *  k_cache       [num_pages, P, Hkv, D] (NHD) or [num_pages, Hkv, P, D] (HND)
+ *                of kv_dtype, written in place; only
  *  v_cache       the rows of written slots change. 16-byte aligned (fp16) or
  *                8-byte aligned (fp8 / int8).
  *  k_scale       fp32 [Hkv] for fp8 / int8 caches (NULL for fp16).

@@ -29,6 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 KV_DTYPES = {"f16": 0, "fp8_e4m3": 1, "int8": 2}
 KERNELS = {"auto": 0, "vector": 1, "matrix": 2}
+KV_LAYOUTS = {"NHD": 0, "HND": 1}
 PDA_MAX_ROWS = 32
 PDA_MAX_SPLITS = 256
 STATUS = {0: "PDA_OK", -1: "PDA_ERR_NULL", -2: "PDA_ERR_SHAPE", -3: "PDA_ERR_ALIGN",
@@ -44,12 +45,13 @@ class PdaError(RuntimeError):
 class DecodeDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_tokens", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
-        "num_pages", "max_pages_per_seq", "max_q_len", "kv_dtype", "kernel")]
+        "num_pages", "max_pages_per_seq", "max_q_len", "kv_dtype", "kernel", "kv_layout")]
 
 
 class CacheDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_tokens", "num_kv_heads", "head_dim", "page_size", "num_pages", "kv_dtype")]
+        "num_tokens", "num_kv_heads", "head_dim", "page_size", "num_pages", "kv_dtype",
+        "kv_layout")]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -121,19 +123,24 @@ def _kv_code(k_cache: torch.Tensor, kv_dtype: Optional[str]) -> int:
 
 
 def decode_dims(q, k_cache, block_table, seq_lens, q_lens=None, max_q_len=None,
-                kv_dtype=None, kernel="auto") -> DecodeDims:
+                kv_dtype=None, kernel="auto", kv_layout="NHD") -> DecodeDims:
     """Sizes of one call, read from tensor shapes. ``max_q_len`` defaults to
     1 without q_lens; with q_lens it must be given (reading q_lens would need
-    a device synchronization)."""
+    a device synchronization). ``kv_layout``: "NHD" caches are
+    [num_pages, P, Hkv, D], "HND" caches [num_pages, Hkv, P, D]."""
     T, Hq, D = q.shape
-    num_pages, P, Hkv, Dk = k_cache.shape
+    if kv_layout == "HND":
+        num_pages, Hkv, P, Dk = k_cache.shape
+    else:
+        num_pages, P, Hkv, Dk = k_cache.shape
     if q_lens is not None and max_q_len is None:
         raise ValueError("max_q_len is required when q_lens is given")
     return DecodeDims(batch=seq_lens.shape[0], num_tokens=T, num_q_heads=Hq,
                       num_kv_heads=Hkv, head_dim=D, page_size=P, num_pages=num_pages,
                       max_pages_per_seq=block_table.shape[1],
                       max_q_len=1 if q_lens is None else int(max_q_len),
-                      kv_dtype=_kv_code(k_cache, kv_dtype), kernel=KERNELS[kernel])
+                      kv_dtype=_kv_code(k_cache, kv_dtype), kernel=KERNELS[kernel],
+                      kv_layout=KV_LAYOUTS[kv_layout])
 
 
 def _contig(*ts):
@@ -167,13 +174,14 @@ def partials_bytes(dims: DecodeDims, window: int = 0, num_splits: int = 0) -> in
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                            window, num_splits, out, k_scale=None, v_scale=None,
                            kv_dtype=None, max_q_len=None, workspace=None, stream=None,
-                           kernel="auto"):
+                           kernel="auto", kv_layout="NHD"):
     """out[t, h] = softmax(scale q.K^T) V over each token's visible keys (see
     include/pda.h). Writes ``out`` (fp16 [T, Hq, D]) and returns None.
     ``kernel``: "auto", "vector" (v_dot2) or "matrix" (MFMA)."""
     lib = load_library()
     _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, out, k_scale, v_scale)
-    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel,
+                       kv_layout)
     need = workspace_bytes(dims, window, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -187,13 +195,15 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, s
 
 def paged_decode_partials(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                           window, num_splits, workspace, k_scale=None, v_scale=None,
-                          kv_dtype=None, max_q_len=None, stream=None, kernel="auto") -> int:
+                          kv_dtype=None, max_q_len=None, stream=None, kernel="auto",
+                          kv_layout="NHD") -> int:
     """The decode stage alone: writes split partials into ``workspace`` (a
     float32 or uint8 tensor of at least partials_bytes(...) bytes). Returns
     the split count used."""
     lib = load_library()
     _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, workspace, k_scale, v_scale)
-    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel,
+                       kv_layout)
     S = resolve_splits(dims, window, num_splits)
     _check(lib.pda_paged_decode_partials(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
@@ -214,7 +224,7 @@ def split_combine(partial_o, partial_ml, out, num_splits: int, stream=None):
 
 
 def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
-                   kv_dtype=None, stream=None):
+                   kv_dtype=None, stream=None, kv_layout="NHD"):
     """Store new tokens' rows key[t], value[t] (fp16 [T, Hkv, D]) at slot
     slot_mapping[t] (int32 [T]; page * P + position, negative: skipped) of
     the caches [num_pages, P, Hkv, D], quantizing to fp8-e4m3 / int8 codes
@@ -229,11 +239,16 @@ def write_kv_cache(key, value, slot_mapping, k_cache, v_cache, k_scale=None, v_s
     T, Hkv, D = key.shape
     if tuple(value.shape) != (T, Hkv, D) or tuple(slot_mapping.shape) != (T,):
         raise ValueError("value must match key's shape and slot_mapping must be [T]")
-    num_pages, P, Hkv_c, D_c = k_cache.shape
+    if kv_layout == "HND":
+        num_pages, Hkv_c, P, D_c = k_cache.shape
+    else:
+        num_pages, P, Hkv_c, D_c = k_cache.shape
     if (Hkv_c, D_c) != (Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("caches must be [num_pages, P, Hkv, D] matching key")
+        raise ValueError("caches must be [num_pages, P, Hkv, D] (NHD) or "
+                         "[num_pages, Hkv, P, D] (HND) matching key")
     dims = CacheDims(num_tokens=T, num_kv_heads=Hkv, head_dim=D, page_size=P,
-                     num_pages=num_pages, kv_dtype=_kv_code(k_cache, kv_dtype))
+                     num_pages=num_pages, kv_dtype=_kv_code(k_cache, kv_dtype),
+                     kv_layout=KV_LAYOUTS[kv_layout])
     _check(lib.pda_write_kv_cache(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache),
                                   _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                   ctypes.byref(dims), _stream(stream)))

@@ -94,9 +94,14 @@ pda_status check_dims(const pda_decode_dims* d) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->head_dim != 128 && d->head_dim != 256)
     return fail(PDA_ERR_UNSUPPORTED, "head_dim %d: compiled for 128 and 256", d->head_dim);
-  if (d->page_size != pda::kPageSize)
-    return fail(PDA_ERR_UNSUPPORTED, "page_size %d: compiled for %d", d->page_size,
-                pda::kPageSize);
+  if (d->page_size < pda::kPageSize || d->page_size > 256 ||
+      (d->page_size & (d->page_size - 1)))
+    return fail(PDA_ERR_UNSUPPORTED, "page_size %d: 16, 32, 64, 128 or 256", d->page_size);
+  if (d->kv_layout != PDA_LAYOUT_NHD && d->kv_layout != PDA_LAYOUT_HND)
+    return fail(PDA_ERR_UNSUPPORTED, "kv_layout %d is not a pda_kv_layout", d->kv_layout);
+  if (d->kernel == PDA_KERNEL_VECTOR &&
+      (d->page_size != pda::kPageSize || d->kv_layout != PDA_LAYOUT_NHD))
+    return fail(PDA_ERR_UNSUPPORTED, "the vector kernel reads 16-key pages in the NHD layout");
   if (d->num_pages <= 0 || d->max_pages_per_seq <= 0)
     return fail(PDA_ERR_SHAPE, "num_pages (%d) and max_pages_per_seq (%d) must be > 0",
                 d->num_pages, d->max_pages_per_seq);
@@ -111,6 +116,8 @@ pda_status check_dims(const pda_decode_dims* d) {
                 (long long)rows, PDA_MAX_ROWS);
   if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX / 2)
     return fail(PDA_ERR_SHAPE, "max_pages_per_seq * page_size too large");
+  if ((int64_t)d->page_size * d->num_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
+    return fail(PDA_ERR_SHAPE, "one page (page_size * num_kv_heads * head_dim) must be < 2 GiB");
   return PDA_OK;
 }
 
@@ -126,11 +133,12 @@ int auto_splits(const pda_decode_dims* d, int window, int uk, int key_waves, int
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, PDA_MAX_SPLITS));
 }
 
-// Pages of keys a call's longest sequence can have visible.
-int64_t visible_pages(const pda_decode_dims* d, int window) {
+// 16-key tiles a call's longest sequence can have visible.
+int64_t visible_tiles(const pda_decode_dims* d, int window) {
   int64_t keys = (int64_t)d->max_pages_per_seq * d->page_size;
-  if (window > 0) keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + d->page_size);
-  return (keys + d->page_size - 1) / d->page_size;
+  if (window > 0)
+    keys = std::min<int64_t>(keys, (int64_t)window + d->max_q_len - 1 + pda::kPageSize);
+  return (keys + pda::kPageSize - 1) / pda::kPageSize;
 }
 
 // Workgroup shape and split count of the matrix kernel.
@@ -144,7 +152,7 @@ int64_t visible_pages(const pda_decode_dims* d, int window) {
 //    cover every compute unit, and key_waves grows to fill the wave slots.
 void matrix_plan(const pda_decode_dims* d, int window, int num_splits, int num_cus,
                  int waves_per_simd, int max_waves, Plan* p) {
-  const int64_t pages = visible_pages(d, window);
+  const int64_t pages = visible_tiles(d, window);  // in 16-key tiles
   const int64_t B = std::max(1, d->batch);
   const int Hkv = d->num_kv_heads;
   auto groups = [&](int h) { return (int64_t)((Hkv + h - 1) / h); };
@@ -322,6 +330,12 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.heads_per_group = p.heads_per_group;
   a.batch = d->batch;
   a.longest_first = p.longest_first;
+  const uint32_t row = (uint32_t)d->head_dim * (d->kv_dtype == PDA_KV_F16 ? 2u : 1u);
+  const bool hnd = d->kv_layout == PDA_LAYOUT_HND;
+  a.key_stride = hnd ? row : row * (uint32_t)d->num_kv_heads;
+  a.head_stride = hnd ? row * (uint32_t)d->page_size : row;
+  a.page_bytes = (uint64_t)row * d->num_kv_heads * d->page_size;
+  a.tile_shift = __builtin_ctz((unsigned)(d->page_size / pda::kPageSize));
   a.rows = p.rows;
   a.wave_lds_bytes = (int32_t)p.wave_lds;
   return a;

@@ -170,22 +170,33 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     hi_c[rt] = active ? pos : -1;
   }
 
-  // Addresses.
-  const uint32_t key_stride = (uint32_t)a.num_kv_heads * Mg::kRowBytes;
-  const size_t page_bytes = (size_t)kPageSize * key_stride;
-  const uint32_t koff = (uint32_t)c * key_stride + (uint32_t)g * Mg::kRowBytes + 16u * s;
+  // Addresses. A "page" of this loop is a tile of 16 keys; a pool page of
+  // 16 * 2^tile_shift keys holds 2^tile_shift consecutive tiles. Within a
+  // page, slot j of head g starts at j * key_stride + g * head_stride (NHD:
+  // key_stride = Hkv * row, head_stride = row; HND: key_stride = row,
+  // head_stride = P * row).
+  const uint32_t key_stride = a.key_stride;
+  const uint32_t head_off = (uint32_t)g * a.head_stride;
+  const size_t page_bytes = a.page_bytes;
+  const int tshift = a.tile_shift;
+  const int tmask = (1 << tshift) - 1;
+  const uint32_t koff = (uint32_t)c * key_stride + head_off + 16u * s;
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    voff[i] = (uint32_t)(s + 4 * i) * key_stride + (uint32_t)g * Mg::kRowBytes +
-              lane_piece_offset<D, KV>(c);
+    voff[i] = (uint32_t)(s + 4 * i) * key_stride + head_off + lane_piece_offset<D, KV>(c);
   typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
   const bt_ptr_t bt = (bt_ptr_t)(a.block_table + (size_t)b * a.max_pages);
-  auto pid_of = [&](int k) -> int { return bt[w_lo + min(k, n - 1)]; };
+  // Byte offset of the k-th tile of this wave's run (clamped to the last).
+  auto pid_of = [&](int k) -> size_t {
+    const int u = w_lo + min(k, n - 1);
+    return (size_t)bt[u >> tshift] * page_bytes +
+           (size_t)((u & tmask) * kPageSize) * key_stride;
+  };
 
-  auto load_page = [&](uint32_t (&kr)[NKL][4], uint32_t (&vr)[4][VR], int pid) {
-    const uint8_t* kp = a.k + (size_t)pid * page_bytes;
-    const uint8_t* vp = a.v + (size_t)pid * page_bytes;
+  auto load_page = [&](uint32_t (&kr)[NKL][4], uint32_t (&vr)[4][VR], size_t base) {
+    const uint8_t* kp = a.k + base;
+    const uint8_t* vp = a.v + base;
 #pragma unroll
     for (int t = 0; t < NKL; ++t) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(kp + koff + 64 * t);
@@ -393,7 +404,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   };
 
   if (n > 0) {
-    int pid_s[NB];
+    size_t pid_s[NB];
 #pragma unroll
     for (int st = 0; st < NB; ++st) pid_s[st] = pid_of(NB - 1 + st);
     const int n_main = n - n % NB;

@@ -9,7 +9,9 @@ namespace pda {
 
 enum KvKind : int { kKvF16 = 0, kKvFp8 = 1, kKvI8 = 2 };
 
-constexpr int kPageSize = 16;     // keys per page (the only compiled size)
+constexpr int kPageSize = 16;     // keys per tile: the page size of the vector
+                                  // kernel; the matrix kernel takes pages of
+                                  // 16 * 2^k keys as runs of such tiles
 constexpr int kLanesPerKey = 16;  // lanes sharing one key row in a wave
 constexpr int kMaxRowsPerWave = 8;
 
@@ -50,6 +52,10 @@ struct DecodeArgs {
   int32_t batch;               // B
   int32_t longest_first;       // matrix kernel: grid row z takes the z-th longest
                                // sequence (needs B <= 64)
+  uint32_t key_stride;         // matrix kernel: bytes between slots of one head
+  uint32_t head_stride;        // matrix kernel: bytes between heads within a page
+  uint64_t page_bytes;         // matrix kernel: bytes of one page (all heads)
+  int32_t tile_shift;          // matrix kernel: log2(page_size / 16)
   int32_t rows;                // G * max_q_len (matrix kernel)
   int32_t wave_lds_bytes;      // LDS bytes per wave (matrix kernel)
 };

@@ -73,7 +73,8 @@ pda_write_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict
                     const int32_t* __restrict__ slot_mapping, uint8_t* __restrict__ k_cache,
                     uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
                     const float* __restrict__ v_scale, int64_t chunks, int row_chunks,
-                    int num_kv_heads, int head_dim, int64_t num_slots) {
+                    int num_kv_heads, int head_dim, int page_size, int hnd,
+                    int64_t num_slots) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= chunks) return;
   const int64_t per_token = (int64_t)num_kv_heads * row_chunks;
@@ -85,7 +86,11 @@ pda_write_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict
   if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool: not written
 
   const size_t src = ((size_t)t * num_kv_heads + h) * head_dim + 8 * c;          // elements
-  const size_t dst = ((size_t)slot * num_kv_heads + h) * head_dim + 8 * c;       // elements
+  // destination row: NHD [page][pos][h][:] is slot-major; HND [page][h][pos][:]
+  const size_t dst_row =
+      hnd ? ((size_t)(slot / page_size) * num_kv_heads + h) * page_size + (size_t)(slot % page_size)
+          : (size_t)slot * num_kv_heads + h;
+  const size_t dst = dst_row * head_dim + 8 * c;  // elements
   const u32x4_w kx = *reinterpret_cast<const u32x4_w*>(key + src);
   const u32x4_w vx = *reinterpret_cast<const u32x4_w*>(value + src);
   if constexpr (KV == kKvF16) {
@@ -124,6 +129,8 @@ extern "C" pda_status pda_write_kv_cache(const void* key, const void* value,
     return wfail(PDA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 (16-byte rows)");
   if (d.kv_dtype != PDA_KV_F16 && d.kv_dtype != PDA_KV_FP8_E4M3 && d.kv_dtype != PDA_KV_INT8)
     return wfail(PDA_ERR_UNSUPPORTED, "kv_dtype is not a pda_kv_dtype");
+  if (d.kv_layout != PDA_LAYOUT_NHD && d.kv_layout != PDA_LAYOUT_HND)
+    return wfail(PDA_ERR_UNSUPPORTED, "kv_layout is not a pda_kv_layout");
   if ((int64_t)d.num_pages * d.page_size > INT32_MAX)
     return wfail(PDA_ERR_SHAPE, "num_pages * page_size must fit in int32 (slot indices)");
   if (d.num_tokens == 0) return PDA_OK;
@@ -144,6 +151,7 @@ extern "C" pda_status pda_write_kv_cache(const void* key, const void* value,
   const int64_t blocks = (chunks + 255) / 256;
   if (blocks > INT32_MAX) return wfail(PDA_ERR_SHAPE, "too many tokens for one launch");
   const int64_t num_slots = (int64_t)d.num_pages * d.page_size;
+  const int hnd = d.kv_layout == PDA_LAYOUT_HND;
   const dim3 grid((unsigned)blocks), block(256);
   auto k = static_cast<const uint16_t*>(key);
   auto v = static_cast<const uint16_t*>(value);
@@ -153,17 +161,17 @@ extern "C" pda_status pda_write_kv_cache(const void* key, const void* value,
     case PDA_KV_F16:
       hipLaunchKernelGGL(pda::pda_write_kv_kernel<pda::kKvF16>, grid, block, 0, stream, k, v,
                          slot_mapping, kc, vc, k_scale, v_scale, chunks, row_chunks,
-                         d.num_kv_heads, d.head_dim, num_slots);
+                         d.num_kv_heads, d.head_dim, d.page_size, hnd, num_slots);
       break;
     case PDA_KV_FP8_E4M3:
       hipLaunchKernelGGL(pda::pda_write_kv_kernel<pda::kKvFp8>, grid, block, 0, stream, k, v,
                          slot_mapping, kc, vc, k_scale, v_scale, chunks, row_chunks,
-                         d.num_kv_heads, d.head_dim, num_slots);
+                         d.num_kv_heads, d.head_dim, d.page_size, hnd, num_slots);
       break;
     default:
       hipLaunchKernelGGL(pda::pda_write_kv_kernel<pda::kKvI8>, grid, block, 0, stream, k, v,
                          slot_mapping, kc, vc, k_scale, v_scale, chunks, row_chunks,
-                         d.num_kv_heads, d.head_dim, num_slots);
+                         d.num_kv_heads, d.head_dim, d.page_size, hnd, num_slots);
       break;
   }
   const hipError_t e = hipGetLastError();

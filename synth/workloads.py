@@ -328,16 +328,19 @@ class WriteCase:
     k_scale: Optional[torch.Tensor]  # fp32 [Hkv] or None
     v_scale: Optional[torch.Tensor]
     kv_dtype: str
+    kv_layout: str = "NHD"  # "HND": caches [num_pages, Hkv, P, D]
 
     def host(self) -> dict:
-        np_ = lambda t: None if t is None else t.detach().cpu().numpy()
+        np_ = lambda t: None if t is None else t.detach().cpu().numpy()  # noqa: E731
         return dict(key=np_(self.key), value=np_(self.value), slot_mapping=np_(self.slot_mapping),
                     k_cache=np_(self.k_cache), v_cache=np_(self.v_cache), kv_dtype=self.kv_dtype,
-                    k_scale=np_(self.k_scale), v_scale=np_(self.v_scale))
+                    k_scale=np_(self.k_scale), v_scale=np_(self.v_scale),
+                    kv_layout=self.kv_layout)
 
 
 def make_write_case(num_tokens, num_kv_heads, head_dim, page_size, num_pages, kv_dtype,
-                    seed, skip_frac=0.1, values=None, scale=None, device="cpu") -> WriteCase:
+                    seed, skip_frac=0.1, values=None, scale=None, device="cpu",
+                    layout="NHD") -> WriteCase:
     """Seeded writer inputs. Rows are N(0,1) fp16 (or `values`, an fp16 array
     of T*Hkv*D elements laid out in order); slots are distinct and random in
     the pool, with about `skip_frac` of them negative and a few past the
@@ -370,7 +373,7 @@ def make_write_case(num_tokens, num_kv_heads, head_dim, page_size, num_pages, kv
         else:
             k_scale = np.full(Hkv, scale, np.float32)
             v_scale = np.full(Hkv, scale, np.float32)
-    shape = (num_pages, P, Hkv, D)
+    shape = (num_pages, Hkv, P, D) if layout == "HND" else (num_pages, P, Hkv, D)
     if kv_dtype == "f16":
         kc = np.full(shape, np.uint16(F16_NAN_BITS)).view(np.float16)
     else:
@@ -379,4 +382,4 @@ def make_write_case(num_tokens, num_kv_heads, head_dim, page_size, num_pages, kv
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return WriteCase(key=t(key), value=t(value), slot_mapping=t(slots.astype(np.int32)),
                      k_cache=t(kc), v_cache=t(vc), k_scale=t(k_scale), v_scale=t(v_scale),
-                     kv_dtype=kv_dtype)
+                     kv_dtype=kv_dtype, kv_layout=layout)

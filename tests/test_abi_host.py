@@ -51,7 +51,12 @@ def _call(dims, **over):
 
 @pytest.mark.parametrize("dims_kw,over,status", [
     (dict(head_dim=64), {}, -4),
-    (dict(page_size=32), {}, -4),
+    (dict(page_size=48), {}, -4),
+    (dict(page_size=512), {}, -4),
+    (dict(page_size=8), {}, -4),
+    (dict(kv_layout=2), {}, -4),
+    (dict(kernel=1, page_size=32), {}, -4),  # the vector kernel reads 16-key pages
+    (dict(kernel=1, kv_layout=1), {}, -4),   # ... in the NHD layout
     (dict(num_q_heads=30), {}, -2),
     (dict(num_kv_heads=0), {}, -2),
     (dict(kv_dtype=7), {}, -4),
@@ -125,6 +130,7 @@ def _wcall(dims, **over):
 @pytest.mark.parametrize("dims_kw,over,status", [
     (dict(head_dim=100), {}, -4),               # not a multiple of 8
     (dict(kv_dtype=5), {}, -4),
+    (dict(kv_layout=3), {}, -4),
     (dict(num_kv_heads=0), {}, -2),
     (dict(page_size=0), {}, -2),
     (dict(num_tokens=-1), {}, -2),

@@ -38,7 +38,8 @@ def run_gpu(case, num_splits=None, scale=None, window=None, out=None, use_q_lens
         case.window if window is None else window,
         case.workload.num_splits if num_splits is None else num_splits, out,
         k_scale=case.k_scale, v_scale=case.v_scale, kv_dtype=case.kv_dtype,
-        max_q_len=case.max_q_len if use_q_lens else None, kernel=kernel)
+        max_q_len=case.max_q_len if use_q_lens else None, kernel=kernel,
+        kv_layout=case.kv_layout)
     torch.cuda.synchronize()
     return out
 
@@ -121,6 +122,29 @@ def test_kv_head_groups(Hkv, D, kv, G, Q, splits):
               seq_lens=(0, 45, 700, 129), num_splits=splits)
     c = case_on_gpu(w)
     assert_parity(run_gpu(c, kernel="matrix"), oracle_full(c), kv, repr(w))
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("P", [16, 32, 64, 256])
+@pytest.mark.parametrize("D,kv,G,Q,W", [(128, "f16", 4, 1, 0), (256, "fp8_e4m3", 6, 2, 100),
+                                        (128, "int8", 7, 3, 0), (256, "f16", 1, 1, 37)])
+@pytest.mark.parametrize("splits", [1, 5])
+def test_layouts_and_page_sizes(layout, P, D, kv, G, Q, W, splits):
+    """Pages of 16 * 2^k keys and the HND layout ([page, head, slot, dim])
+    on the matrix kernel; lengths end inside, at and across page edges."""
+    w = small(41 + P, head_dim=D, kv_dtype=kv, num_q_heads=G * 3, num_kv_heads=3, q_len=Q,
+              seq_lens=(0, P - 1, P, 2 * P + 17, 700), page_size=P, layout=layout,
+              window=W, num_splits=splits, pool_pages=0)
+    c = case_on_gpu(w)
+    assert_parity(run_gpu(c, kernel="matrix"), oracle_full(c), kv, repr(w))
+
+
+@pytest.mark.parametrize("layout,kernel", [("NHD", "auto"), ("HND", "auto"), ("NHD", "vector")])
+def test_identity_table(layout, kernel):
+    """Pages in pool order (the "dense" reading of the pages' layout flag)."""
+    w = small(43, seq_lens=(300, 17, 129), layout=layout, num_splits=3, identity_table=True)
+    c = case_on_gpu(w)
+    assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), "f16", repr(w))
 
 
 @pytest.mark.parametrize("D,kv,G,Q", [(128, "f16", 7, 3), (256, "f16", 6, 1),
@@ -343,7 +367,7 @@ def test_split_combine_vs_oracle(D, S):
 def sampled_parity(c, units, kernel):
     got = run_gpu(c, kernel=kernel)
     assert torch.isfinite(got.float()).all()
-    G = c.q.shape[1] // c.k_cache.shape[2]
+    G = c.q.shape[1] // c.workload.num_kv_heads
     worst = 0.0
     for b, g in units:
         sub = unit_subcase(c, b, g)
@@ -360,6 +384,15 @@ def test_full_gqa4_d128_b8_l4096(kernel):
     c = case_on_gpu(WORKLOADS["gqa4_d128_b8_l4096"])
     got = run_gpu(c, kernel=kernel)
     assert_parity(got, oracle_full(c), "f16", "gqa4 full")
+
+
+@pytest.mark.parametrize("over", [dict(layout="HND"), dict(page_size=64),
+                                  dict(identity_table=True), dict(num_splits=8)])
+def test_full_gqa4_d128_b8_l4096_variants(over):
+    """The headline shape in the bench's variant cells (HND layout, 64-key
+    pages, identity table, a caller's 8 splits), full comparison."""
+    c = case_on_gpu(WORKLOADS["gqa4_d128_b8_l4096"].with_(**over))
+    assert_parity(run_gpu(c), oracle_full(c), "f16", f"gqa4 {over}")
 
 
 @pytest.mark.parametrize("window", [0, 4096])

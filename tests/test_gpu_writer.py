@@ -20,13 +20,15 @@ DEV = "cuda"
 
 def run_writer(c):
     pda.write_kv_cache(c.key, c.value, c.slot_mapping, c.k_cache, c.v_cache,
-                       k_scale=c.k_scale, v_scale=c.v_scale, kv_dtype=c.kv_dtype)
+                       k_scale=c.k_scale, v_scale=c.v_scale, kv_dtype=c.kv_dtype,
+                       kv_layout=c.kv_layout)
     torch.cuda.synchronize()
 
 
 def assert_cache_equal(c, h):
     want_k, want_v = oracle.write_kv_cache(h["key"], h["value"], h["slot_mapping"], h["k_cache"],
-                                           h["v_cache"], h["kv_dtype"], h["k_scale"], h["v_scale"])
+                                           h["v_cache"], h["kv_dtype"], h["k_scale"], h["v_scale"],
+                                           h["kv_layout"])
     got_k = c.k_cache.cpu().numpy()
     got_v = c.v_cache.cpu().numpy()
     assert got_k.tobytes() == want_k.tobytes(), "K cache bytes differ"
@@ -39,6 +41,16 @@ def assert_cache_equal(c, h):
 def test_writer_bit_exact(kv, D, P, Hkv, T):
     c = make_write_case(T, Hkv, D, P, num_pages=64 + T, kv_dtype=kv, seed=T * 7 + D + P,
                         device=DEV)
+    h = c.host()
+    run_writer(c)
+    assert_cache_equal(c, h)
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
+@pytest.mark.parametrize("P", [16, 64, 3])
+def test_writer_hnd_layout(kv, P):
+    c = make_write_case(200, 4, 128, P, num_pages=200 // P + 9, kv_dtype=kv, seed=P + 3,
+                        device=DEV, layout="HND")
     h = c.host()
     run_writer(c)
     assert_cache_equal(c, h)
