@@ -63,6 +63,7 @@ CELLS = [
 # Sources the decode step is built from (kernels, their launch plan, combine).
 DECODE_SOURCES = ("pda_kernels.h", "pda_decode_impl.h", "pda_decode_mfma.h", "pda_decode_f16.hip",
                   "pda_decode_fp8.hip", "pda_decode_i8.hip", "pda_api.hip", "pda_combine.hip")
+# (pda_prefill*.hip/h and pda_writer.hip are other kernels: not hashed)
 
 
 def kernel_source_hash() -> str:

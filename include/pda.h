@@ -88,12 +88,18 @@ typedef enum pda_kv_layout {
  *    fdot2" design (section "Purpose") carried to wave64.
  *  PDA_KERNEL_MATRIX: Q.K^T and P.V on the MFMA units (fp16 operands, fp32
  *    accumulation; P rounded to fp16 for the P.V product).
- *  PDA_KERNEL_AUTO: the library's choice (currently the matrix kernel, the
- *    faster of the two on every measured shape). */
+ *  PDA_KERNEL_PREFILL: the long-query kernel: one workgroup per block of
+ *    new tokens of a sequence and KV head (128 query rows), K/V staged once
+ *    per workgroup through LDS for all its rows, MFMA for both products.
+ *    For prefill, chunked prefill and long verification runs; always one
+ *    split (num_splits 0 or 1).
+ *  PDA_KERNEL_AUTO: the matrix kernel while (Hq / Hkv) * max_q_len <=
+ *    PDA_MAX_ROWS, the prefill kernel above that. */
 typedef enum pda_kernel {
   PDA_KERNEL_AUTO = 0,
   PDA_KERNEL_VECTOR = 1,
-  PDA_KERNEL_MATRIX = 2
+  PDA_KERNEL_MATRIX = 2,
+  PDA_KERNEL_PREFILL = 3
 } pda_kernel;
 
 /* Sizes of one call. */
@@ -113,8 +119,11 @@ typedef struct pda_decode_dims {
   int32_t kv_layout;         /* a pda_kv_layout (NHD only for PDA_KERNEL_VECTOR) */
 } pda_decode_dims;
 
-/* Largest (num_q_heads / num_kv_heads) * max_q_len a call accepts. */
+/* Largest (num_q_heads / num_kv_heads) * max_q_len of the decode kernels
+ * (vector, matrix); larger calls run the prefill kernel, which takes any
+ * max_q_len with num_q_heads / num_kv_heads <= PDA_MAX_GROUP. */
 #define PDA_MAX_ROWS 32
+#define PDA_MAX_GROUP 128
 /* Largest number of key splits. */
 #define PDA_MAX_SPLITS 256
 

@@ -28,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 KV_DTYPES = {"f16": 0, "fp8_e4m3": 1, "int8": 2}
-KERNELS = {"auto": 0, "vector": 1, "matrix": 2}
+KERNELS = {"auto": 0, "vector": 1, "matrix": 2, "prefill": 3}
 KV_LAYOUTS = {"NHD": 0, "HND": 1}
 PDA_MAX_ROWS = 32
 PDA_MAX_SPLITS = 256

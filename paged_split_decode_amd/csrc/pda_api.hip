@@ -69,6 +69,7 @@ int kv_kind(int32_t kv_dtype) {
 
 // Launch shape for one call.
 struct Plan {
+  int prefill;     // 1: long-query kernel (one split, direct output)
   int matrix;      // 1: MFMA kernel, 0: v_dot2 kernel
   int row_tiles;   // MFMA kernel: 16-row tiles
   size_t wave_lds; // MFMA kernel: LDS bytes per wave
@@ -108,12 +109,15 @@ pda_status check_dims(const pda_decode_dims* d) {
   if (d->max_q_len < 1) return fail(PDA_ERR_SHAPE, "max_q_len %d must be >= 1", d->max_q_len);
   if (kv_kind(d->kv_dtype) < 0)
     return fail(PDA_ERR_UNSUPPORTED, "kv_dtype %d is not a pda_kv_dtype", d->kv_dtype);
-  if (d->kernel < PDA_KERNEL_AUTO || d->kernel > PDA_KERNEL_MATRIX)
+  if (d->kernel < PDA_KERNEL_AUTO || d->kernel > PDA_KERNEL_PREFILL)
     return fail(PDA_ERR_UNSUPPORTED, "kernel %d is not a pda_kernel", d->kernel);
   const int64_t rows = (int64_t)(d->num_q_heads / d->num_kv_heads) * d->max_q_len;
-  if (rows > PDA_MAX_ROWS)
-    return fail(PDA_ERR_UNSUPPORTED, "(num_q_heads/num_kv_heads)*max_q_len = %lld exceeds %d",
+  if (rows > PDA_MAX_ROWS && (d->kernel == PDA_KERNEL_VECTOR || d->kernel == PDA_KERNEL_MATRIX))
+    return fail(PDA_ERR_UNSUPPORTED,
+                "(num_q_heads/num_kv_heads)*max_q_len = %lld exceeds %d for the decode kernels",
                 (long long)rows, PDA_MAX_ROWS);
+  if (d->num_q_heads / d->num_kv_heads > PDA_MAX_GROUP)
+    return fail(PDA_ERR_UNSUPPORTED, "num_q_heads/num_kv_heads exceeds %d", PDA_MAX_GROUP);
   if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX / 2)
     return fail(PDA_ERR_SHAPE, "max_pages_per_seq * page_size too large");
   if ((int64_t)d->page_size * d->num_kv_heads * d->head_dim * 2 >= ((int64_t)1 << 31))
@@ -190,6 +194,28 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
     return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
   p->rows = (d->num_q_heads / d->num_kv_heads) * d->max_q_len;
+  p->prefill = d->kernel == PDA_KERNEL_PREFILL ||
+               (d->kernel == PDA_KERNEL_AUTO && p->rows > PDA_MAX_ROWS);
+  if (p->prefill) {
+    if (num_splits > 1)
+      return fail(PDA_ERR_UNSUPPORTED, "the prefill kernel runs one split (num_splits 0 or 1)");
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const int bq = pda::kPrefillRows / G;  // tokens per workgroup
+    p->rows = bq * G;                      // rows per workgroup
+    p->row_tiles = (d->max_q_len + bq - 1) / bq;  // grid x: token blocks
+    p->matrix = 1;
+    p->splits = 1;
+    p->threads = 256;
+    p->lds = pda::prefill_lds_bytes(d->head_dim);
+    p->wave_lds = 0;
+    p->rows_per_wave = 32;
+    p->row_groups = 4;
+    p->key_waves = 1;
+    p->heads_per_group = 1;
+    p->head_groups = d->num_kv_heads;
+    p->longest_first = 0;
+    return PDA_OK;
+  }
   // The matrix-core kernel is faster on every measured shape; the v_dot2
   // kernel stays selectable.
   p->matrix = d->kernel != PDA_KERNEL_VECTOR;
@@ -231,11 +257,23 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   return PDA_OK;
 }
 
+// Whether a (valid) call runs the long-query kernel.
+bool routes_to_prefill(const pda_decode_dims* d) {
+  const int64_t rows = (int64_t)(d->num_q_heads / d->num_kv_heads) * d->max_q_len;
+  return d->kernel == PDA_KERNEL_PREFILL || (d->kernel == PDA_KERNEL_AUTO && rows > PDA_MAX_ROWS);
+}
+
 // The split count alone (for size queries): a caller's count needs no device.
 pda_status resolve_split_count(const pda_decode_dims* d, int32_t window, int32_t num_splits,
                                int num_cus, int* splits) {
   pda_status st = check_dims(d);
   if (st != PDA_OK) return st;
+  if (routes_to_prefill(d)) {
+    if (num_splits > 1)
+      return fail(PDA_ERR_UNSUPPORTED, "the prefill kernel runs one split (num_splits 0 or 1)");
+    *splits = 1;
+    return PDA_OK;
+  }
   if (num_splits >= 1 && num_splits <= PDA_MAX_SPLITS) {
     *splits = num_splits;
     return PDA_OK;
@@ -272,8 +310,18 @@ pda_status check_pointers(const void* q, const void* k, const void* v, const int
 
 pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArgs& args,
                          hipStream_t stream) {
-  const dim3 grid(p.splits, p.head_groups, d->batch);
   hipError_t e;
+  if (p.prefill) {
+    const dim3 pgrid(p.row_tiles, d->num_kv_heads, d->batch);
+    switch (kv_kind(d->kv_dtype)) {
+      case pda::kKvF16: e = pda::launch_prefill_f16(d->head_dim, pgrid, p.lds, stream, args); break;
+      case pda::kKvFp8: e = pda::launch_prefill_fp8(d->head_dim, pgrid, p.lds, stream, args); break;
+      default: e = pda::launch_prefill_i8(d->head_dim, pgrid, p.lds, stream, args); break;
+    }
+    if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
+    return PDA_OK;
+  }
+  const dim3 grid(p.splits, p.head_groups, d->batch);
   if (p.matrix) {
     switch (kv_kind(d->kv_dtype)) {
       case pda::kKvF16:
@@ -416,6 +464,9 @@ pda_status pda_paged_decode_partials(const void* q, const void* k_cache, const v
   if ((st = check_q_lens(q_lens, dims))) return st;
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
     return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
+  if (routes_to_prefill(dims))
+    return fail(PDA_ERR_UNSUPPORTED, "partials come from the decode kernels only "
+                "((num_q_heads/num_kv_heads)*max_q_len <= %d, kernel not PREFILL)", PDA_MAX_ROWS);
   if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
   int splits = 0;
   if ((st = resolve_split_count(dims, window, num_splits, 0, &splits))) return st;

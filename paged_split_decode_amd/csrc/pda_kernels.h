@@ -106,6 +106,21 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
   return (size_t)waves * rows_per_wave * (head_dim + 2) * sizeof(float);
 }
 
+// Long-query (prefill) kernel: 128 (token, head) rows per workgroup of 4
+// waves; K/V staged through LDS prefill_tiles(D) 16-key tiles at a time, in
+// two buffers of fp16 rows of D + 8 halves.
+constexpr int kPrefillRows = 128;
+constexpr int prefill_tiles(int head_dim) { return head_dim == 256 ? 1 : 2; }  // <= 64 KiB LDS
+inline size_t prefill_lds_bytes(int head_dim) {
+  return (size_t)2 * prefill_tiles(head_dim) * 2 * 16 * (head_dim + 8) * 2;
+}
+hipError_t launch_prefill_f16(int head_dim, dim3 grid, size_t lds, hipStream_t stream,
+                              const DecodeArgs& args);
+hipError_t launch_prefill_fp8(int head_dim, dim3 grid, size_t lds, hipStream_t stream,
+                              const DecodeArgs& args);
+hipError_t launch_prefill_i8(int head_dim, dim3 grid, size_t lds, hipStream_t stream,
+                             const DecodeArgs& args);
+
 // Host-side error state shared by every entry point: records a message for
 // pda_last_error() and returns `status`.
 int host_fail(int status, const char* fmt, ...);

@@ -61,9 +61,13 @@ def _call(dims, **over):
     (dict(num_kv_heads=0), {}, -2),
     (dict(kv_dtype=7), {}, -4),
     (dict(max_q_len=0), {}, -2),
-    (dict(num_q_heads=64, num_kv_heads=1), {}, -4),  # 64 rows > PDA_MAX_ROWS
+    (dict(num_q_heads=64, num_kv_heads=1, kernel=2), {}, -4),  # decode kernels: <= 32 rows
+    (dict(num_q_heads=64, num_kv_heads=1, kernel=1), {}, -4),
+    (dict(num_q_heads=256, num_kv_heads=1), {}, -4),  # group > PDA_MAX_GROUP
+    (dict(num_q_heads=64, num_kv_heads=1), dict(splits=4), -4),  # prefill: one split
+    (dict(kernel=3), dict(splits=2), -4),
+    (dict(kernel=4), {}, -4),
     (dict(num_pages=0), {}, -2),
-    (dict(kernel=3), {}, -4),
     ({}, dict(q=None), -1),
     ({}, dict(out=None), -1),
     ({}, dict(q=ctypes.c_void_p(0x100004)), -3),
@@ -153,3 +157,14 @@ def test_writer_null_dims_and_empty_batch():
     assert _wcall(None) == -1
     # no tokens: nothing to write, no pointer is looked at
     assert _wcall(_cdims(num_tokens=0), key=None, value=None, slots=None, kc=None, vc=None) == 0
+
+
+def test_prefill_split_policy_and_no_partials():
+    d = _dims(num_q_heads=64, num_kv_heads=1)   # 64 rows per KV head: prefill kernel
+    assert pda.resolve_splits(d, 0, 0, 256) == 1
+    assert pda.resolve_splits(d, 0, 1, 256) == 1
+    assert pda.workspace_bytes(d, 0, 0) == 0
+    lib = pda.load_library()
+    st = lib.pda_paged_decode_partials(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, 0, 0, None, None,
+                                       ctypes.byref(d), FAKE, 1 << 20, None)
+    assert st == -4 and b"decode kernels" in lib.pda_last_error()

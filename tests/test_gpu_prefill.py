@@ -1,0 +1,102 @@
+"""The long-query (prefill) kernel through the C ABI against the fp64 oracle.
+It computes the same function as the decode kernels: multi-token causal
+attention over the paged cache, here with hundreds of new tokens per
+sequence. Tolerances as for decode (2e-3 fp16 KV, 2e-2 fp8/int8)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, Workload, make_case, unit_subcase
+from tests.test_gpu_parity import DEV, TOL, assert_parity, oracle_full, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+
+
+def _ragged(seed, q_lens, ctx, **kw):
+    """Sequences with their own query counts (q_lens ragged)."""
+    lens = [int(c + q) for c, q in zip(ctx, q_lens)]
+    base = dict(name="prefill", batch=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                seq_lens=tuple(lens), q_len=max(q_lens), seed=seed, num_splits=1)
+    base.update(kw)
+    c = make_case(Workload(**base), device=DEV)
+    ql = np.array(q_lens, np.int32)
+    G, D = c.q.shape[1], c.q.shape[2]
+    q = torch.randn((int(ql.sum()), G, D), generator=torch.Generator(device=DEV).manual_seed(seed),
+                    device=DEV).to(torch.float16)
+    import dataclasses
+    return dataclasses.replace(c, q=q, q_lens=torch.from_numpy(ql).to(DEV), q_lens_host=ql)
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("G", [1, 4, 7])
+def test_prefill_parity(kv, D, G):
+    # ragged query runs; the second sequence has fewer keys than queries
+    # (its first rows see nothing), the third a long cached context
+    c = _ragged(3 * G + D, q_lens=[37, 130, 300], ctx=[0, -100, 900], head_dim=D, kv_dtype=kv,
+                num_q_heads=2 * G, num_kv_heads=2)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv, f"prefill D={D} {kv} G={G}")
+
+
+@pytest.mark.parametrize("window", [1, 64, 300])
+@pytest.mark.parametrize("layout,P", [("NHD", 16), ("HND", 64)])
+def test_prefill_window_layouts(window, layout, P):
+    c = _ragged(window + P, q_lens=[200, 50], ctx=[500, 7], window=window, layout=layout,
+                page_size=P, num_q_heads=12, num_kv_heads=3)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill W={window} {layout}")
+
+
+@pytest.mark.parametrize("kv", ["f16", "int8"])
+def test_prefill_kernel_on_short_queries_matches_decode(kv):
+    """Forced on a decode-sized call, the prefill kernel must give the decode
+    kernel's function."""
+    w = Workload("short", batch=5, num_q_heads=8, num_kv_heads=2, head_dim=128, q_len=3,
+                 seq_lens=(1, 40, 300, 0, 999), kv_dtype=kv, seed=12, num_splits=1)
+    c = make_case(w, device=DEV)
+    want = oracle_full(c)
+    a = run_gpu(c, kernel="prefill", num_splits=1)
+    b = run_gpu(c, kernel="matrix", num_splits=1)
+    assert_parity(a, want, kv, "prefill kernel")
+    assert (a.float() - b.float()).abs().max().item() <= 2 * TOL[kv]
+
+
+def test_prefill_rejects_splits():
+    import paged_split_decode_amd as pda
+    c = _ragged(5, q_lens=[100], ctx=[10])
+    with pytest.raises(pda.PdaError):
+        run_gpu(c, num_splits=4)
+
+
+def sampled_tokens(c, n_per_seq, seed):
+    """GPU rows of sampled (sequence, KV head, token) triples against the
+    oracle on the single-token problem each one is: token i of sequence b
+    attends like a one-token decode of the sequence cut at its position."""
+    got = run_gpu(c, num_splits=1)
+    assert torch.isfinite(got.float()).all()
+    r = np.random.default_rng(seed)
+    Hkv = c.workload.num_kv_heads
+    G = c.q.shape[1] // Hkv
+    worst = 0.0
+    for b in range(len(c.seq_lens_host)):
+        Q, L = int(c.q_lens_host[b]), int(c.seq_lens_host[b])
+        off = int(c.q_lens_host[:b].sum())
+        for i in r.choice(Q, size=min(n_per_seq, Q), replace=False):
+            g = int(r.integers(Hkv))
+            sub = unit_subcase(c, b, g)
+            p = L - Q + int(i)
+            sub.update(q=sub["q"][i:i + 1], seq_lens=np.array([p + 1], np.int32),
+                       q_lens=np.array([1], np.int32))
+            want = oracle.paged_decode_attention(**sub)
+            part = got[off + i:off + i + 1, g * G:(g + 1) * G]
+            worst = max(worst, assert_parity(part, want, c.kv_dtype, f"({b},{g},{i})"))
+    return worst
+
+
+@pytest.mark.parametrize("name", ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512"])
+def test_prefill_workloads_sampled(name):
+    c = make_case(WORKLOADS[name], device=DEV)
+    sampled_tokens(c, 12, seed=len(name))
