@@ -247,6 +247,27 @@ def cpu_baseline(case, budget_s: float = 12.0):
                       f"{el:.1f} s"}
 
 
+# Long-query (prefill kernel) cells: a fresh prefill and a chunked prefill.
+PREFILL_CELLS = ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512"]
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, AMD published
+
+
+def prefill_record(name, case, m):
+    from synth import visible_pairs
+
+    flops = 4 * case.workload.head_dim * visible_pairs(case)
+    us = m["ms_per_step"] * 1e3
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": name, "op": "prefill", "batch": case.workload.batch,
+            "q_len": case.workload.q_len, "seq_len": case.workload.seq_len,
+            "us_per_call": round(us, 2), "TFLOP_s": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)},
+            "flops": flops, "GB_s": round(m["bytes"] / (us * 1e-6) / 1e9, 1),
+            "algorithmic_bytes": m["bytes"]}
+
+
 # Cache-writer cells: (tokens, KV heads, head dim, kv dtype): the new tokens of
 # the fp8 long-context decode step, and prefill-sized writes.
 WRITER_CELLS = [
@@ -392,6 +413,15 @@ def main(argv=None):
             del c
             torch.cuda.empty_cache()
         rec["cells"] = cells
+        rec["prefill_cells"] = []
+        for name in PREFILL_CELLS:
+            c = make_case(WORKLOADS[name], device=device)
+            mc = measure(c, max(10, args.steps // 4), 3, 1, device, args.kernel)
+            rec["prefill_cells"].append(prefill_record(name, c, mc))
+            print(json.dumps({"prefill_cell": rec["prefill_cells"][-1]}), file=sys.stderr,
+                  flush=True)
+            del c
+            torch.cuda.empty_cache()
         rec["writer_cells"] = []
         for (T, Hkv, D, kv) in WRITER_CELLS:
             rw = measure_writer(T, Hkv, D, kv, max(10, args.steps // 4), device)

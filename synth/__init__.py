@@ -15,4 +15,5 @@ from .workloads import (  # noqa: F401
     unit_subcase,
     WriteCase,
     make_write_case,
+    visible_pairs,
 )

@@ -392,3 +392,19 @@ def make_write_case(num_tokens, num_kv_heads, head_dim, page_size, num_pages, kv
     return WriteCase(key=t(key), value=t(value), slot_mapping=t(slots.astype(np.int32)),
                      k_cache=t(kc), v_cache=t(vc), k_scale=t(k_scale), v_scale=t(v_scale),
                      kv_dtype=kv_dtype, kv_layout=layout)
+
+
+def visible_pairs(case: Case) -> int:
+    """(query row, key) pairs one call scores: for every new token, the keys
+    it can see, times the query heads. The flop count of a call is
+    4 * head_dim * visible_pairs (2 D for q.k, 2 D for p.v)."""
+    W = case.window
+    total = 0
+    for L, Q in zip(case.seq_lens_host.tolist(), case.q_lens_host.tolist()):
+        for i in range(Q):
+            p = L - Q + i
+            if p < 0:
+                continue
+            lo = max(0, p - W + 1) if W > 0 else 0
+            total += p - lo + 1
+    return total * case.workload.num_q_heads
