@@ -113,59 +113,63 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     return (size_t)bt[u >> tshift] * a.page_bytes + (size_t)((u & tmask) * kPageSize) * key_stride;
   };
 
-  // Staging: thread piece p < NPIECE: kv = p / (KT*16*PIECES), then tile,
-  // key row, 16-byte piece.
+  // Staging: thread piece p = tid + 256 l (< NPIECE) is K or V (kv), tile tt
+  // of the step, key row, 16-byte piece; all of that is fixed per thread, so
+  // its byte offset within a tile and its LDS position are computed once.
+  // Each step only moves the (scalar) tile bases.
+  static_assert(NPIECE % 256 == 0, "every thread stages whole pieces");
+  uint32_t src_off[LOADS];
+  uint32_t lds_off[LOADS];  // in halves
+  int row_of[LOADS], tt_of[LOADS];
+  bool is_v[LOADS];
+#pragma unroll
+  for (int l = 0; l < LOADS; ++l) {
+    const int p = tid + 256 * l;
+    const int kv = p / (KT * 16 * PIECES);
+    const int rem = p - kv * (KT * 16 * PIECES);
+    tt_of[l] = rem / (16 * PIECES);
+    row_of[l] = (rem / PIECES) % 16;
+    const int piece = rem % PIECES;
+    is_v[l] = kv != 0;
+    src_off[l] = (uint32_t)row_of[l] * key_stride + head_off + 16u * piece;
+    lds_off[l] = (uint32_t)((kv * KT + tt_of[l]) * TILE + row_of[l] * LR + piece * (16 / EB));
+  }
   uint32_t stage[LOADS][4];
   auto stage_load = [&](int step) {
     const int u0 = t_lo + step * KT;
+    size_t base[KT];
+#pragma unroll
+    for (int tt = 0; tt < KT; ++tt) base[tt] = tile_base(min(u0 + tt, t_lo + n_tiles - 1));
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
-      const int p = tid + 256 * l;
-      if (NPIECE % 256 == 0 || p < NPIECE) {
-        const int kv = p / (KT * 16 * PIECES);
-        const int rem = p - kv * (KT * 16 * PIECES);
-        const int tt = rem / (16 * PIECES);
-        const int row = (rem / PIECES) % 16;
-        const int piece = rem % PIECES;
-        const int u = min(u0 + tt, t_lo + n_tiles - 1);  // clamp past the range (never used)
-        const uint8_t* base = (kv ? a.v : a.k) + tile_base(u);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(base + (size_t)row * key_stride +
-                                                        head_off + 16u * piece);
+      const uint8_t* src = (is_v[l] ? a.v : a.k) + base[tt_of[l]] + src_off[l];
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) stage[l][e] = x[e];
-      }
+      for (int e = 0; e < 4; ++e) stage[l][e] = x[e];
     }
   };
   auto stage_store = [&](int step, int buf) {
-    const int u0 = t_lo + step * KT;
+    const int j0 = (t_lo + step * KT) * kPageSize;
     _Float16* dst0 = lds + (size_t)buf * 2 * KT * TILE;
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
-      const int p = tid + 256 * l;
-      if (NPIECE % 256 == 0 || p < NPIECE) {
-        const int kv = p / (KT * 16 * PIECES);
-        const int rem = p - kv * (KT * 16 * PIECES);
-        const int tt = rem / (16 * PIECES);
-        const int row = (rem / PIECES) % 16;
-        const int piece = rem % PIECES;
-        // slots past the sequence (arbitrary contents) become zeros
-        const bool live = (u0 + tt) * kPageSize + row < L;
-        _Float16* dst = dst0 + (size_t)(kv * KT + tt) * TILE + row * LR + piece * (16 / EB);
-        if constexpr (KV == kKvF16) {
+      // slots past the sequence (arbitrary contents) become zeros
+      const bool live = j0 + tt_of[l] * kPageSize + row_of[l] < L;
+      _Float16* dst = dst0 + lds_off[l];
+      if constexpr (KV == kKvF16) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = live ? stage[l][e] : 0u;
+        *reinterpret_cast<u32x4*>(dst) = w;
+      } else {
+        h2_t hv[8];
+        to_pairs<KV>(stage[l], hv);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
           u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = live ? stage[l][e] : 0u;
-          *reinterpret_cast<u32x4*>(dst) = w;
-        } else {
-          h2_t hv[8];
-          to_pairs<KV>(stage[l], hv);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = live ? __builtin_bit_cast(uint32_t, hv[4 * hh + e]) : 0u;
-            *reinterpret_cast<u32x4*>(dst + 8 * hh) = w;
-          }
+          for (int e = 0; e < 4; ++e) w[e] = live ? __builtin_bit_cast(uint32_t, hv[4 * hh + e]) : 0u;
+          *reinterpret_cast<u32x4*>(dst + 8 * hh) = w;
         }
       }
     }
@@ -231,25 +235,37 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       for (int t = 0; t < NS; ++t)
         sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t], qb[rt][t], sc[rt], 0, 0, 0);
     }
-    auto visible = [&](int rt, int i) {
-      const int j = j0 + 4 * s + i;
-      return j >= lo_c[rt] && j <= hi_c[rt];
-    };
+    // Online softmax. Unmasked tiles (every key visible to every row of the
+    // wave) and masked ones take separate, wave-uniform branches.
+    float pv[NRT][4];
+    uint32_t vis[NRT];  // bit i: key j0 + 4 s + i visible to this lane's row
     bool behind = false;
+    if (full) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      float mt;
-      if (full) {
-        mt = qk * max4(fmaxf(fmaxf(sc[rt][0], sc[rt][1]), fmaxf(sc[rt][2], sc[rt][3])));
-      } else {
-        mt = -INFINITY;
+      for (int rt = 0; rt < NRT; ++rt) {
+        const float mt =
+            qk * max4(fmaxf(fmaxf(sc[rt][0], sc[rt][1]), fmaxf(sc[rt][2], sc[rt][3])));
+        mx[rt] = fmaxf(mx[rt], mt);
+        behind |= mx[rt] > m[rt] + kLazy;
+        vis[rt] = 0xFu;
+      }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, visible(rt, i) ? sc[rt][i] : -INFINITY);
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int j = j0 + 4 * s;
+        float mt = -INFINITY;
+        vis[rt] = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool v = j + i >= lo_c[rt] && j + i <= hi_c[rt];
+          vis[rt] |= v ? 1u << i : 0u;
+          mt = fmaxf(mt, v ? sc[rt][i] : -INFINITY);
+        }
         mt = max4(mt);
         mt = mt == -INFINITY ? kNoMax : qk * mt;
+        mx[rt] = fmaxf(mx[rt], mt);
+        behind |= mx[rt] > m[rt] + kLazy;
       }
-      mx[rt] = fmaxf(mx[rt], mt);
-      behind |= mx[rt] > m[rt] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(behind) != 0) {
 #pragma unroll
@@ -264,14 +280,13 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     h4_t pb[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -m[rt]));
-        p[i] = (full || visible(rt, i)) ? e : 0.0f;
+        pv[rt][i] = (vis[rt] >> i) & 1u ? e : 0.0f;
       }
-      l[rt] += (p[0] + p[1]) + (p[2] + p[3]);
-      pb[rt] = h4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      l[rt] += (pv[rt][0] + pv[rt][1]) + (pv[rt][2] + pv[rt][3]);
+      pb[rt] = h4_t{(_Float16)pv[rt][0], (_Float16)pv[rt][1], (_Float16)pv[rt][2], (_Float16)pv[rt][3]};
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
