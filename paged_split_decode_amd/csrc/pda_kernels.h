@@ -110,7 +110,7 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
 // waves; K/V staged through LDS prefill_tiles(D) 16-key tiles at a time, in
 // two buffers of fp16 rows of D + 8 halves.
 constexpr int kPrefillRows = 128;
-constexpr int prefill_tiles(int head_dim) { return head_dim == 256 ? 1 : 2; }  // <= 64 KiB LDS
+constexpr int prefill_tiles(int) { return 2; }  // 32 keys per step
 inline size_t prefill_lds_bytes(int head_dim) {
   return (size_t)2 * prefill_tiles(head_dim) * 2 * 16 * (head_dim + 8) * 2;
 }

@@ -24,12 +24,11 @@
 
 namespace pda {
 
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+
 template <int D, int KV>
 __global__ void __launch_bounds__(256, D == 128 ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
-  constexpr int NS = D / 32;       // QK k-steps of 32 dims
-  constexpr int NDT = D / 16;      // PV output tiles of 16 dims
-  constexpr int NRT = 2;           // row tiles per wave
   constexpr int LR = D + 8;        // LDS row stride, halves
   constexpr int TILE = 16 * LR;    // halves of one 16-key tile
   constexpr int KT = prefill_tiles(D);
@@ -45,8 +44,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int s = lane >> 4;
-  const int c = lane & 15;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int blk = gridDim.x - 1 - blockIdx.x;  // the most keys first
@@ -78,7 +75,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 
   // This wave's rows (16 rt + c of its 32): bounds per lane, and wave-uniform
   // summaries for the skip / unmasked tests.
-  int lo_c[NRT], hi_c[NRT];
   int lo_min = 0x7fffffff, lo_max = 0, hi_min = 0x7fffffff, hi_max = -1;
   for (int r = 32 * wave; r < 32 * wave + 32 && r < a.rows; ++r) {
     const int i = i0 + r / G;
@@ -89,15 +85,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       hi_min = min(hi_min, pos);
       hi_max = max(hi_max, pos);
     }
-  }
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int r = 32 * wave + 16 * rt + c;
-    const int i = i0 + r / G;
-    const int pos = pos0 + i;
-    const bool active = r < a.rows && i < Qb && pos >= 0;
-    lo_c[rt] = active ? lo_of(pos) : 0;
-    hi_c[rt] = active ? pos : -1;
   }
 
   // Cache addressing (as in the decode kernel): tile u of sequence b starts
@@ -153,8 +140,10 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     _Float16* dst0 = lds + (size_t)buf * 2 * KT * TILE;
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
-      // slots past the sequence (arbitrary contents) become zeros
-      const bool live = j0 + tt_of[l] * kPageSize + row_of[l] < L;
+      // slots past the sequence (arbitrary contents), and tiles past this
+      // workgroup's range (staged from a clamped tile), become zeros
+      const int u = t_lo + step * KT + tt_of[l];
+      const bool live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
       _Float16* dst = dst0 + lds_off[l];
       if constexpr (KV == kKvF16) {
         u32x4 w;
@@ -175,124 +164,127 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     }
   };
 
-  // Q rows as the B operand: lane (s, c) holds row 16 rt + c, dims
-  // 32 t + 8 s .. + 7 of step t. A negative scale flips q's sign.
+  // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
+  // with h = l / 32; B: column l % 32, same k; C: column l % 32, rows
+  // 8 j + 4 h + i in element 4 j + i). So lane l works on query row rr = l % 32
+  // of this wave's 32 rows; lanes l and l + 32 share the row.
+  const int rr = lane & 31;
+  const int hh = lane >> 5;
+  const int myr = 32 * wave + rr;  // the workgroup row of this lane
+  const int my_i = i0 + myr / G;
+  const bool my_row = myr < a.rows && my_i < Qb;
+  const int my_pos = pos0 + my_i;
+  const int my_lo = (my_row && my_pos >= 0) ? lo_of(my_pos) : 0;
+  const int my_hi = (my_row && my_pos >= 0) ? my_pos : -1;
+
+  // Q^T as the B operand: lane l holds row rr, dims 16 t + 8 hh .. + 7 of
+  // k-step t. A negative scale flips q's sign.
   float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
   const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
   qk = fabsf(qk);
-  h8_t qb[NRT][NS];
+  constexpr int NK = D / 16;   // QK k-steps
+  constexpr int NDT = D / 32;  // 32-dim output tiles
+  h8_t qb[NK];
+  {
+    const uint8_t* qrow =
+        a.q + ((size_t)(off + my_i) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int r = 32 * wave + 16 * rt + c;
-    const int i = i0 + r / G;
-    const bool exists = r < a.rows && i < Qb;
-    const uint8_t* qrow = a.q + ((size_t)(off + i) * Hq + g * G + (r - (r / G) * G)) * (D * 2);
-#pragma unroll
-    for (int t = 0; t < NS; ++t) {
+    for (int t = 0; t < NK; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (exists) x = *reinterpret_cast<const u32x4*>(qrow + 64 * t + 16 * s);
+      if (my_row) x = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] ^= qflip;
-      qb[rt][t] = __builtin_bit_cast(h8_t, x);
+      qb[t] = __builtin_bit_cast(h8_t, x);
     }
   }
 
   constexpr float kNoMax = -1e30f;
   constexpr float kLazy = 8.0f;
-  float m[NRT], mx[NRT], l[NRT];
-  f4_t o[NRT][NDT];
+  float m = kNoMax, mx = kNoMax, lsum = 0.0f;
+  f16v_t o[NDT];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    m[rt] = kNoMax;
-    mx[rt] = kNoMax;
-    l[rt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[rt][dt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f16v_t{};
 
   typedef short s4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+  auto tr_read = [&](const _Float16* src) {
+    return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src));
+  };
+  const int q16 = lane >> 4, i16 = lane & 15;  // 16-lane group and lane in it
 
-  auto compute_tile = [&](const _Float16* kt, const _Float16* vt, int u) {
-    const int j0 = u * kPageSize;
-    if (hi_max < 0 || j0 > hi_max || j0 + kPageSize - 1 < lo_min) return;  // wave-uniform
-    const bool full = j0 >= lo_max && j0 + kPageSize - 1 <= hi_min;
-    h4_t va[NDT];
+  // One step of 32 keys (K rows kb[0..31], V rows vb[0..31] in LDS).
+  auto compute_step = [&](const _Float16* kb, const _Float16* vb, int key0) {
+    if (hi_max < 0 || key0 > hi_max || key0 + 31 < lo_min) return;  // wave-uniform
+    const bool full = key0 >= lo_max && key0 + 31 <= hi_min;
+    // S^T[key][row]: lane l gets row rr, keys 8 j + 4 hh + i in st[4 j + i].
+    f16v_t st = {};
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const _Float16* src = vt + (4 * s + (c >> 2)) * LR + 16 * dt + 4 * (c & 3);
-      va[dt] = __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src));
+    for (int t = 0; t < NK; ++t) {
+      const h8_t ka = *reinterpret_cast<const h8_t*>(kb + rr * LR + 16 * t + 8 * hh);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[t], st, 0, 0, 0);
     }
-    h8_t ka[NS];
-#pragma unroll
-    for (int t = 0; t < NS; ++t) ka[t] = *reinterpret_cast<const h8_t*>(kt + c * LR + 32 * t + 8 * s);
-    f4_t sc[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      sc[rt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int t = 0; t < NS; ++t)
-        sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t], qb[rt][t], sc[rt], 0, 0, 0);
-    }
-    // Online softmax. Unmasked tiles (every key visible to every row of the
-    // wave) and masked ones take separate, wave-uniform branches.
-    float pv[NRT][4];
-    uint32_t vis[NRT];  // bit i: key j0 + 4 s + i visible to this lane's row
-    bool behind = false;
+    uint32_t vis = 0xFFFFu;  // bit 4 j + i: key key0 + 8 j + 4 hh + i visible to row rr
+    float mt;
     if (full) {
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const float mt =
-            qk * max4(fmaxf(fmaxf(sc[rt][0], sc[rt][1]), fmaxf(sc[rt][2], sc[rt][3])));
-        mx[rt] = fmaxf(mx[rt], mt);
-        behind |= mx[rt] > m[rt] + kLazy;
-        vis[rt] = 0xFu;
-      }
+      float a0 = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+      float a1 = fmaxf(fmaxf(st[4], st[5]), fmaxf(st[6], st[7]));
+      float a2 = fmaxf(fmaxf(st[8], st[9]), fmaxf(st[10], st[11]));
+      float a3 = fmaxf(fmaxf(st[12], st[13]), fmaxf(st[14], st[15]));
+      mt = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
     } else {
+      vis = 0u;
+      mt = -INFINITY;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int j = j0 + 4 * s;
-        float mt = -INFINITY;
-        vis[rt] = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool v = j + i >= lo_c[rt] && j + i <= hi_c[rt];
-          vis[rt] |= v ? 1u << i : 0u;
-          mt = fmaxf(mt, v ? sc[rt][i] : -INFINITY);
-        }
-        mt = max4(mt);
-        mt = mt == -INFINITY ? kNoMax : qk * mt;
-        mx[rt] = fmaxf(mx[rt], mt);
-        behind |= mx[rt] > m[rt] + kLazy;
+      for (int v = 0; v < 16; ++v) {
+        const int j = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const bool ok = j >= my_lo && j <= my_hi;
+        vis |= ok ? 1u << v : 0u;
+        mt = fmaxf(mt, ok ? st[v] : -INFINITY);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(behind) != 0) {
+    {  // the other half of the row's keys sits in lane l ^ 32
+      auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mt),
+                                                 __builtin_bit_cast(int, mt), false, false);
+      mt = fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+    }
+    mt = mt == -INFINITY ? kNoMax : qk * mt;
+    mx = fmaxf(mx, mt);
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mx);
+      lsum *= alpha;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mx[rt]);
-        l[rt] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m = mx;
+    }
+    float p[16];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[rt][dt] *= alpha;
-        m[rt] = mx[rt];
+    for (int v = 0; v < 16; ++v) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], qk, -m));
+      p[v] = (vis >> v) & 1u ? e : 0.0f;
+      lsum += p[v];
+    }
+    // O^T[dim][row] += V^T . P^T over two 16-key k-steps. k-step ks takes the
+    // lane's keys of j = 2 ks, 2 ks + 1 (slots 8 hh + e: key 16 ks + 4 hh + e,
+    // then 16 ks + 8 + 4 hh + e); V^T's A operand uses the same key order:
+    // two transposing reads of 4 consecutive key rows at this lane's dim.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      h8_t pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = (_Float16)p[8 * ks + e];
+        pb[4 + e] = (_Float16)p[8 * ks + 4 + e];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int col = 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3);
+        const h4_t lo = tr_read(vb + (16 * ks + 4 * hh + (i16 >> 2)) * LR + col);
+        const h4_t hi = tr_read(vb + (16 * ks + 8 + 4 * hh + (i16 >> 2)) * LR + col);
+        const h8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[dt], 0, 0, 0);
       }
     }
-    h4_t pb[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -m[rt]));
-        pv[rt][i] = (vis[rt] >> i) & 1u ? e : 0.0f;
-      }
-      l[rt] += (pv[rt][0] + pv[rt][1]) + (pv[rt][2] + pv[rt][3]);
-      pb[rt] = h4_t{(_Float16)pv[rt][0], (_Float16)pv[rt][1], (_Float16)pv[rt][2], (_Float16)pv[rt][3]};
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[dt], pb[rt], o[rt][dt], 0, 0, 0);
   };
 
   if (n_steps > 0) {
@@ -303,36 +295,35 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       const int buf = step & 1;
       if (step + 1 < n_steps) stage_load(step + 1);
       const _Float16* kb = lds + (size_t)buf * 2 * KT * TILE;
-#pragma unroll
-      for (int tt = 0; tt < KT; ++tt) {
-        const int u = t_lo + step * KT + tt;
-        if (u < t_lo + n_tiles) compute_tile(kb + tt * TILE, kb + (KT + tt) * TILE, u);
-      }
+      compute_step(kb, kb + KT * TILE, (t_lo + step * KT) * kPageSize);
       if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1);
       __syncthreads();
     }
   }
 
-  // Rows of this wave: bring o, l to the row maximum, sum l over the 4 lane
-  // groups, write fp16 out (a row that sees no key is 0).
-  const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const float alpha = __builtin_amdgcn_exp2f(m[rt] - mx[rt]);
-    l[rt] = add4(l[rt] * alpha);
-    const int r = 32 * wave + 16 * rt + c;
-    const int i = i0 + r / G;
-    if (r >= a.rows || i >= Qb) continue;
-    const size_t hrow = (size_t)(off + i) * Hq + g * G + (r - (r / G) * G);
-    uint16_t* dst = a.out + hrow * D + 4 * s;
-    const float lsum = l[rt];
+  // Bring o, l to the row maximum, add the two lane halves' l, write fp16 out
+  // (a row that sees no key is 0). Lane l writes dims 32 dt + 8 j + 4 hh .. + 3.
+  const float alpha = __builtin_amdgcn_exp2f(m - mx);
+  lsum *= alpha;
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, lsum),
+                                               __builtin_bit_cast(int, lsum), false, false);
+    lsum = __builtin_bit_cast(float, (int)sw[0]) + __builtin_bit_cast(float, (int)sw[1]);
+  }
+  if (my_row) {
+    const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
+    const size_t hrow = (size_t)(off + my_i) * Hq + g * G + (myr - (myr / G) * G);
+    uint16_t* dst = a.out + hrow * D + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      h4_t y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        y[e] = lsum > 0.0f ? (_Float16)((o[rt][dt][e] * alpha * vs) / lsum) : (_Float16)0.0f;
-      *reinterpret_cast<h4_t*>(dst + 16 * dt) = y;
+      for (int j = 0; j < 4; ++j) {
+        h4_t y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[e] = lsum > 0.0f ? (_Float16)((o[dt][4 * j + e] * alpha * vs) / lsum) : (_Float16)0.0f;
+        *reinterpret_cast<h4_t*>(dst + 32 * dt + 8 * j) = y;
+      }
     }
   }
 }
