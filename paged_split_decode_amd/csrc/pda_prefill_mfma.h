@@ -29,7 +29,9 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 template <int D, int KV>
 __global__ void __launch_bounds__(256, D == 128 ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
-  constexpr int LR = D + 8;        // LDS row stride, halves
+  constexpr int LR = D + 16;       // LDS row stride, halves (72 dwords at D=128:
+                                   // the 4 rows of a transposing read hit
+                                   // disjoint banks)
   constexpr int TILE = 16 * LR;    // halves of one 16-key tile
   constexpr int KT = prefill_tiles(D);
   constexpr int EB = KV == kKvF16 ? 2 : 1;
