@@ -260,12 +260,18 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       m = mx;
     }
     float p[16];
+    if (full) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], qk, -m));
-      p[v] = (vis >> v) & 1u ? e : 0.0f;
-      lsum += p[v];
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], qk, -m));
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], qk, -m));
+        p[v] = (vis >> v) & 1u ? e : 0.0f;
+      }
     }
+#pragma unroll
+    for (int v = 0; v < 16; v += 4) lsum += (p[v] + p[v + 1]) + (p[v + 2] + p[v + 3]);
     // O^T[dim][row] += V^T . P^T over two 16-key k-steps. k-step ks takes the
     // lane's keys of j = 2 ks, 2 ks + 1 (slots 8 hh + e: key 16 ks + 4 hh + e,
     // then 16 ks + 8 + 4 hh + e); V^T's A operand uses the same key order:
