@@ -96,10 +96,10 @@ def test_empty_batch_is_ok_without_launch():
 
 def test_split_policy_and_workspace():
     d = _dims()
-    # matrix kernel: 8 sequences x 2 groups of 4 KV heads per split; one
-    # four-wave workgroup per CU on 256 CUs -> 16 splits
-    assert pda.resolve_splits(d, 0, 0, 256) == 16
-    assert pda.resolve_splits(d, 0, 0, 128) == 8
+    # matrix kernel: 8 sequences x 2 groups of 4 KV heads per split; 2 wave
+    # slots per SIMD on 256 CUs -> 512 four-wave workgroups -> 32 splits
+    assert pda.resolve_splits(d, 0, 0, 256) == 32
+    assert pda.resolve_splits(d, 0, 0, 128) == 16
     # v_dot2 kernel: 64 (sequence, KV head) units, about one workgroup per CU
     assert pda.resolve_splits(_dims(kernel=1), 0, 0, 256) == 4
     assert pda.resolve_splits(d, 0, 3, 256) == 3
