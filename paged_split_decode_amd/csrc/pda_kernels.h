@@ -108,11 +108,11 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
 
 // Long-query (prefill) kernel: 128 (token, head) rows per workgroup of 4
 // waves; K/V staged through LDS prefill_tiles(D) 16-key tiles at a time, in
-// two buffers of fp16 rows of D + 16 halves.
+// two buffers of fp16 rows (K: D + 8 halves, V: D + 16).
 constexpr int kPrefillRows = 128;
-constexpr int prefill_tiles(int) { return 2; }  // 32 keys per step
+constexpr int prefill_tiles(int) { return 4; }  // 64 keys per LDS step (two halves of 32)
 inline size_t prefill_lds_bytes(int head_dim) {
-  return (size_t)2 * prefill_tiles(head_dim) * 2 * 16 * (head_dim + 16) * 2;
+  return (size_t)2 * prefill_tiles(head_dim) * 16 * ((head_dim + 8) + (head_dim + 16)) * 2;
 }
 hipError_t launch_prefill_f16(int head_dim, dim3 grid, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);

@@ -29,10 +29,13 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 template <int D, int KV>
 __global__ void __launch_bounds__(256, D == 128 ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
-  constexpr int LR = D + 16;       // LDS row stride, halves (72 dwords at D=128:
-                                   // the 4 rows of a transposing read hit
-                                   // disjoint banks)
-  constexpr int TILE = 16 * LR;    // halves of one 16-key tile
+  // LDS row strides (halves): K rows D + 8 (4 dwords mod 64: the 16 rows of a
+  // 128-bit fragment read pass hit disjoint banks), V rows D + 16 (8 dwords
+  // mod 64: the 4 rows of a transposing read hit disjoint banks).
+  constexpr int LRK = D + 8;
+  constexpr int LRV = D + 16;
+  constexpr int TILEK = 16 * LRK;  // halves of one 16-key K tile
+  constexpr int TILEV = 16 * LRV;
   constexpr int KT = prefill_tiles(D);
   constexpr int EB = KV == kKvF16 ? 2 : 1;
   constexpr int PIECES = D * EB / 16;                // 16-byte pieces of a cache row
@@ -41,7 +44,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);
-  // buffer x: K tiles at lds + x * 2 * KT * TILE, V tiles KT * TILE later
+  // buffer x: K tiles at lds + x * KT * (TILEK + TILEV), V tiles KT * TILEK later
+  constexpr int BUF = KT * (TILEK + TILEV);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,7 +125,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     const int piece = rem % PIECES;
     is_v[l] = kv != 0;
     src_off[l] = (uint32_t)row_of[l] * key_stride + head_off + 16u * piece;
-    lds_off[l] = (uint32_t)((kv * KT + tt_of[l]) * TILE + row_of[l] * LR + piece * (16 / EB));
+    lds_off[l] = (uint32_t)(kv ? KT * TILEK + tt_of[l] * TILEV + row_of[l] * LRV
+                               : tt_of[l] * TILEK + row_of[l] * LRK) + piece * (16 / EB);
   }
   uint32_t stage[LOADS][4];
   auto stage_load = [&](int step) {
@@ -139,7 +144,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   };
   auto stage_store = [&](int step, int buf) {
     const int j0 = (t_lo + step * KT) * kPageSize;
-    _Float16* dst0 = lds + (size_t)buf * 2 * KT * TILE;
+    _Float16* dst0 = lds + (size_t)buf * BUF;
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
       // slots past the sequence (arbitrary contents), and tiles past this
@@ -216,16 +221,21 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int q16 = lane >> 4, i16 = lane & 15;  // 16-lane group and lane in it
 
   // One step of 32 keys (K rows kb[0..31], V rows vb[0..31] in LDS).
-  auto compute_step = [&](const _Float16* kb, const _Float16* vb, int key0) {
-    if (hi_max < 0 || key0 > hi_max || key0 + 31 < lo_min) return;  // wave-uniform
-    const bool full = key0 >= lo_max && key0 + 31 <= hi_min;
-    // S^T[key][row]: lane l gets row rr, keys 8 j + 4 hh + i in st[4 j + i].
+  // Whether this wave has work on the 32 keys from key0 (wave-uniform).
+  auto active = [&](int key0) { return hi_max >= 0 && key0 <= hi_max && key0 + 31 >= lo_min; };
+  // S^T[key][row] of 32 keys: lane l gets row rr, keys 8 j + 4 hh + i in st[4 j + i].
+  auto scores = [&](const _Float16* kb) {
     f16v_t st = {};
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
-      const h8_t ka = *reinterpret_cast<const h8_t*>(kb + rr * LR + 16 * t + 8 * hh);
+      const h8_t ka = *reinterpret_cast<const h8_t*>(kb + rr * LRK + 16 * t + 8 * hh);
       st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[t], st, 0, 0, 0);
     }
+    return st;
+  };
+  // Softmax and P.V of 32 keys from key0 whose scores are st.
+  auto softmax_pv = [&](f16v_t st, const _Float16* vb, int key0) {
+    const bool full = key0 >= lo_max && key0 + 31 <= hi_min;
     uint32_t vis = 0xFFFFu;  // bit 4 j + i: key key0 + 8 j + 4 hh + i visible to row rr
     float mt;
     if (full) {
@@ -287,8 +297,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int col = 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3);
-        const h4_t lo = tr_read(vb + (16 * ks + 4 * hh + (i16 >> 2)) * LR + col);
-        const h4_t hi = tr_read(vb + (16 * ks + 8 + 4 * hh + (i16 >> 2)) * LR + col);
+        const h4_t lo = tr_read(vb + (16 * ks + 4 * hh + (i16 >> 2)) * LRV + col);
+        const h4_t hi = tr_read(vb + (16 * ks + 8 + 4 * hh + (i16 >> 2)) * LRV + col);
         const h8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[dt], 0, 0, 0);
       }
@@ -302,8 +312,17 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     for (int step = 0; step < n_steps; ++step) {
       const int buf = step & 1;
       if (step + 1 < n_steps) stage_load(step + 1);
-      const _Float16* kb = lds + (size_t)buf * 2 * KT * TILE;
-      compute_step(kb, kb + KT * TILE, (t_lo + step * KT) * kPageSize);
+      const _Float16* kb = lds + (size_t)buf * BUF;
+      const _Float16* vb = kb + KT * TILEK;
+      const int key0 = (t_lo + step * KT) * kPageSize;
+      // Both halves' scores first: the second half's MFMAs can run under the
+      // first half's softmax.
+      const bool a0 = active(key0), a1 = active(key0 + 32);
+      f16v_t st0 = {}, st1 = {};
+      if (a0) st0 = scores(kb);
+      if (a1) st1 = scores(kb + 2 * TILEK);
+      if (a0) softmax_pv(st0, vb, key0);
+      if (a1) softmax_pv(st1, vb + 2 * TILEV, key0 + 32);
       if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1);
       __syncthreads();
     }
