@@ -168,3 +168,11 @@ def test_prefill_split_policy_and_no_partials():
     st = lib.pda_paged_decode_partials(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, 0, 0, None, None,
                                        ctypes.byref(d), FAKE, 1 << 20, None)
     assert st == -4 and b"decode kernels" in lib.pda_last_error()
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No fallback: a missing libpda.so is an error, not a silent CPU path."""
+    monkeypatch.setattr(pda, "_lib", None)
+    monkeypatch.setattr(pda, "_LIB_PATH", str(tmp_path / "libpda.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        pda.load_library()
