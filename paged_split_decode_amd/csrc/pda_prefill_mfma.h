@@ -3,21 +3,21 @@
 // kernels, for many new tokens per sequence.
 //
 // A workgroup takes a block of new tokens of one sequence and all G query
-// heads of one KV head: 128 (token, head) rows, 32 per wave as two 16-row
-// tiles. K and V go through LDS once per workgroup and serve all 4 waves:
-// each step the 256 threads gather 32 keys (16 at D=256) of K and V
-// from the paged cache with 16-byte loads, convert 1-byte codes to fp16
-// (exactly), and write them to one of two fp16 LDS buffers while the waves
-// compute on the other; one barrier per step.
+// heads of one KV head: 128 (token, head) rows, 32 per wave. K and V go
+// through LDS once per workgroup and serve all 4 waves: each step the 256
+// threads gather 64 keys (four 16-key tiles) of K and V from the paged cache
+// with 16-byte loads, convert 1-byte codes to fp16 (exactly), and write them
+// to one of two fp16 LDS buffers while the waves compute on the other; one
+// barrier per step.
 //
-// Per wave and tile the arithmetic is the decode kernel's: S^T = K . Q^T with
-// v_mfma_f32_16x16x32_f16 (K fragments read from the LDS tile, the wave's Q
-// rows as the B operand), an online softmax with a lazily moved reference,
-// and O^T += V^T . P^T with v_mfma_f32_16x16x16_f16, V fragments read with
-// ds_read_b64_tr_b16. Each row has its own causal limit (its position) and
-// window; a tile after all of a wave's rows, or before all their windows, is
-// skipped by that wave. Workgroups with the most keys (the last token
-// blocks) are dispatched first.
+// Per wave and 32 keys: S^T = K . Q^T with v_mfma_f32_32x32x16_f16 (K
+// fragments read from the LDS tile, the wave's 32 Q rows as the B operand;
+// lane l then holds 16 scores of query row l % 32), an online softmax with a
+// lazily moved reference, and O^T += V^T . P^T with the same instruction: P
+// from the score registers, V^T from ds_read_b64_tr_b16. Each row has its own
+// causal limit (its position) and window; 32 keys after all of a wave's rows,
+// or before all their windows, are skipped by that wave. Workgroups with the
+// most keys (the last token blocks) are dispatched first.
 #pragma once
 
 #include "pda_decode_mfma.h"
