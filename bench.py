@@ -67,12 +67,13 @@ DECODE_SOURCES = ("pda_kernels.h", "pda_decode_impl.h", "pda_decode_mfma.h", "pd
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources of the decode step: counter figures recorded for
-    one hash do not describe a kernel built from different sources."""
+    """Hash of the HIP sources of the decode step and of the build script that
+    sets their compiler flags: counter figures recorded for one hash do not
+    describe a kernel built from different sources or flags."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_split_decode_amd", "csrc")
-    for f in DECODE_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
+    pkg = os.path.join(ROOT, "paged_split_decode_amd")
+    for f in (*(os.path.join("csrc", s) for s in DECODE_SOURCES), "build.py"):
+        with open(os.path.join(pkg, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 

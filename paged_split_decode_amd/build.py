@@ -43,8 +43,13 @@ def _hipcc() -> str:
 
 # Per-source flags. The prefill kernel's staged K/V are finite by construction
 # (slots past a sequence are zeroed), so its max operations need no NaN
-# canonicalization.
-EXTRA = {"pda_prefill.hip": ["-fno-honor-nans"]}
+# canonicalization. The decode kernels take the VGPR form of the MFMA
+# instructions: at one wave per SIMD the compiler otherwise keeps the score and
+# output accumulators in AGPRs and copies all of them to VGPRs on every page,
+# for a rescale that is rarely taken.
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"pda_prefill.hip": ["-fno-honor-nans"], "pda_decode_f16.hip": _VGPR_MFMA,
+         "pda_decode_fp8.hip": _VGPR_MFMA, "pda_decode_i8.hip": _VGPR_MFMA}
 
 
 def _compile(src: str) -> str:

@@ -366,11 +366,15 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     h4_t pb[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
+      // Every p is computed; only partial pages then zero the hidden ones
+      // (a wave-uniform branch around selects, none on full pages).
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -m[rt]));
-        p[i] = (full || visible(rt, i)) ? e : 0.0f;
+      for (int i = 0; i < 4; ++i)
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rt][i], qk, -m[rt]));
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = visible(rt, i) ? p[i] : 0.0f;
       }
       l[rt] += (p[0] + p[1]) + (p[2] + p[3]);
       pb[rt] = h4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
