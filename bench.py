@@ -60,21 +60,28 @@ CELLS = [
 ]
 
 
-# Sources the decode step is built from (kernels, their launch plan, combine).
+# Sources the decode step is built from (kernels, their launch plan, combine),
+# and those of the prefill kernel.
 DECODE_SOURCES = ("pda_kernels.h", "pda_decode_impl.h", "pda_decode_mfma.h", "pda_decode_f16.hip",
                   "pda_decode_fp8.hip", "pda_decode_i8.hip", "pda_api.hip", "pda_combine.hip")
-# (pda_prefill*.hip/h and pda_writer.hip are other kernels: not hashed)
+PREFILL_SOURCES = ("pda_kernels.h", "pda_decode_impl.h", "pda_decode_mfma.h",
+                   "pda_prefill_mfma.h", "pda_prefill.hip", "pda_api.hip")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources of the decode step and of the build script that
-    sets their compiler flags: counter figures recorded for one hash do not
-    describe a kernel built from different sources or flags."""
+def kernel_source_hash(kernel: str = "decode_mfma") -> str:
+    """Hash of the HIP sources of a kernel (the decode step, or the prefill
+    kernel when `kernel` starts with "prefill") and of the compiler flags they
+    are built with: counter figures recorded for one hash do not describe a
+    kernel built from different sources or flags."""
+    from paged_split_decode_amd import build as pda_build
+
     h = hashlib.sha256()
-    pkg = os.path.join(ROOT, "paged_split_decode_amd")
-    for f in (*(os.path.join("csrc", s) for s in DECODE_SOURCES), "build.py"):
-        with open(os.path.join(pkg, f), "rb") as fh:
+    csrc = os.path.join(ROOT, "paged_split_decode_amd", "csrc")
+    for f in PREFILL_SOURCES if kernel.startswith("prefill") else DECODE_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+        h.update(" ".join(pda_build.EXTRA.get(f, [])).encode())
+    h.update(" ".join(a for a in pda_build.COMMON if not a.startswith("/")).encode())
     return h.hexdigest()[:16]
 
 
@@ -87,7 +94,7 @@ def traffic_for(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(rec.get("kernel", "decode_mfma")):
         return None
     return rec.get("hbm_bytes_per_launch")
 

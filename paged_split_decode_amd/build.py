@@ -43,12 +43,12 @@ def _hipcc() -> str:
 
 # Per-source flags. The prefill kernel's staged K/V are finite by construction
 # (slots past a sequence are zeroed), so its max operations need no NaN
-# canonicalization. The decode kernels take the VGPR form of the MFMA
+# canonicalization. The attention kernels take the VGPR form of the MFMA
 # instructions: at one wave per SIMD the compiler otherwise keeps the score and
 # output accumulators in AGPRs and copies all of them to VGPRs on every page,
-# for a rescale that is rarely taken.
+# for a rescale that is rarely taken (AGPRs remain in use as spill space).
 _VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-EXTRA = {"pda_prefill.hip": ["-fno-honor-nans"], "pda_decode_f16.hip": _VGPR_MFMA,
+EXTRA = {"pda_prefill.hip": ["-fno-honor-nans", *_VGPR_MFMA], "pda_decode_f16.hip": _VGPR_MFMA,
          "pda_decode_fp8.hip": _VGPR_MFMA, "pda_decode_i8.hip": _VGPR_MFMA}
 
 

@@ -26,6 +26,12 @@ namespace pda {
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
+// A compile-time bool carried by value (selects a lambda body variant).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 template <int D, int KV>
 __global__ void __launch_bounds__(256, D == 128 ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
@@ -145,30 +151,41 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   auto stage_store = [&](int step, int buf) {
     const int j0 = (t_lo + step * KT) * kPageSize;
     _Float16* dst0 = lds + (size_t)buf * BUF;
+    // Slots past the sequence (arbitrary contents), and tiles past this
+    // workgroup's range (staged from a clamped tile), become zeros. Only a
+    // step that reaches past either needs the per-slot test (wave-uniform).
+    auto put = [&](auto checked) {
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      // slots past the sequence (arbitrary contents), and tiles past this
-      // workgroup's range (staged from a clamped tile), become zeros
-      const int u = t_lo + step * KT + tt_of[l];
-      const bool live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
-      _Float16* dst = dst0 + lds_off[l];
-      if constexpr (KV == kKvF16) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = live ? stage[l][e] : 0u;
-        *reinterpret_cast<u32x4*>(dst) = w;
-      } else {
-        h2_t hv[8];
-        to_pairs<KV>(stage[l], hv);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+      for (int l = 0; l < LOADS; ++l) {
+        bool live = true;
+        if constexpr (decltype(checked)::value) {
+          const int u = t_lo + step * KT + tt_of[l];
+          live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
+        }
+        _Float16* dst = dst0 + lds_off[l];
+        if constexpr (KV == kKvF16) {
           u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = live ? __builtin_bit_cast(uint32_t, hv[4 * hh + e]) : 0u;
-          *reinterpret_cast<u32x4*>(dst + 8 * hh) = w;
+          for (int e = 0; e < 4; ++e) w[e] = live ? stage[l][e] : 0u;
+          *reinterpret_cast<u32x4*>(dst) = w;
+        } else {
+          h2_t hv[8];
+          to_pairs<KV>(stage[l], hv);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] = live ? __builtin_bit_cast(uint32_t, hv[4 * hh + e]) : 0u;
+            *reinterpret_cast<u32x4*>(dst + 8 * hh) = w;
+          }
         }
       }
-    }
+    };
+    if ((step + 1) * KT <= n_tiles && j0 + KT * kPageSize <= L)
+      put(BoolC<false>{});
+    else
+      put(BoolC<true>{});
   };
 
   // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
@@ -223,15 +240,37 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // One step of 32 keys (K rows kb[0..31], V rows vb[0..31] in LDS).
   // Whether this wave has work on the 32 keys from key0 (wave-uniform).
   auto active = [&](int key0) { return hi_max >= 0 && key0 <= hi_max && key0 + 31 >= lo_min; };
-  // S^T[key][row] of 32 keys: lane l gets row rr, keys 8 j + 4 hh + i in st[4 j + i].
+  // S^T[key][row] of 32 keys: lane l gets row rr, keys 8 j + 4 hh + i in
+  // st[4 j + i]. At D=128 the two halves' chains of dependent MFMAs are
+  // interleaved (scores2), with each k-step's K fragments read one step
+  // ahead; D=256 (one wave per SIMD, no registers to spare) runs the halves
+  // one after the other.
+  auto frag = [&](const _Float16* kb, int t) {
+    return *reinterpret_cast<const h8_t*>(kb + rr * LRK + 16 * t + 8 * hh);
+  };
   auto scores = [&](const _Float16* kb) {
     f16v_t st = {};
 #pragma unroll
-    for (int t = 0; t < NK; ++t) {
-      const h8_t ka = *reinterpret_cast<const h8_t*>(kb + rr * LRK + 16 * t + 8 * hh);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[t], st, 0, 0, 0);
-    }
+    for (int t = 0; t < NK; ++t)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag(kb, t), qb[t], st, 0, 0, 0);
     return st;
+  };
+  auto scores2 = [&](const _Float16* kb0, const _Float16* kb1, f16v_t& s0, f16v_t& s1) {
+    h8_t k0 = frag(kb0, 0), k1 = frag(kb1, 0);
+    s0 = f16v_t{};
+    s1 = f16v_t{};
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      h8_t n0 = k0, n1 = k1;
+      if (t + 1 < NK) {
+        n0 = frag(kb0, t + 1);
+        n1 = frag(kb1, t + 1);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qb[t], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qb[t], s1, 0, 0, 0);
+      k0 = n0;
+      k1 = n1;
+    }
   };
   // Softmax and P.V of 32 keys from key0 whose scores are st.
   auto softmax_pv = [&](f16v_t st, const _Float16* vb, int key0) {
@@ -316,11 +355,17 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       const _Float16* vb = kb + KT * TILEK;
       const int key0 = (t_lo + step * KT) * kPageSize;
       // Both halves' scores first: the second half's MFMAs can run under the
-      // first half's softmax.
+      // first half's softmax. (At D=128 a half that no row of the wave sees
+      // still gets scores, from finite LDS data, when the other half is
+      // needed; its softmax and P.V are skipped.)
       const bool a0 = active(key0), a1 = active(key0 + 32);
       f16v_t st0 = {}, st1 = {};
-      if (a0) st0 = scores(kb);
-      if (a1) st1 = scores(kb + 2 * TILEK);
+      if constexpr (D == 128) {
+        if (a0 || a1) scores2(kb, kb + 2 * TILEK, st0, st1);
+      } else {
+        if (a0) st0 = scores(kb);
+        if (a1) st1 = scores(kb + 2 * TILEK);
+      }
       if (a0) softmax_pv(st0, vb, key0);
       if (a1) softmax_pv(st1, vb + 2 * TILEV, key0 + 32);
       if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1);
