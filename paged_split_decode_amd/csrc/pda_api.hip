@@ -447,9 +447,10 @@ pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const 
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = a.part_o + (size_t)dims->num_tokens * dims->num_q_heads * p.splits * dims->head_dim;
   if ((st = launch_decode(p, dims, a, stream))) return st;
-  const hipError_t e = pda::launch_combine(a.part_o, a.part_ml, static_cast<uint16_t*>(out),
-                                           dims->num_tokens * dims->num_q_heads,
-                                           dims->head_dim, p.splits, stream);
+  const int rows = dims->num_tokens * dims->num_q_heads;
+  const hipError_t e = pda::launch_combine(
+      a.part_o, a.part_ml, static_cast<uint16_t*>(out), rows, dims->head_dim, p.splits,
+      pda::combine_dim_parts(rows, dims->head_dim, device_cu_count()), stream);
   if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "combine launch: %s", hipGetErrorString(e));
   return PDA_OK;
 }
@@ -505,8 +506,9 @@ pda_status pda_split_combine(const float* partial_o, const float* partial_ml, vo
   if (num_tokens == 0) return PDA_OK;
   const int64_t rows = (int64_t)num_tokens * num_q_heads;
   if (rows > INT32_MAX) return fail(PDA_ERR_SHAPE, "num_tokens * num_q_heads too large");
-  const hipError_t e = pda::launch_combine(partial_o, partial_ml, static_cast<uint16_t*>(out),
-                                           (int)rows, head_dim, num_splits, stream);
+  const hipError_t e = pda::launch_combine(
+      partial_o, partial_ml, static_cast<uint16_t*>(out), (int)rows, head_dim, num_splits,
+      pda::combine_dim_parts((int)rows, head_dim, device_cu_count()), stream);
   if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "combine launch: %s", hipGetErrorString(e));
   return PDA_OK;
 }

@@ -4,10 +4,12 @@
 // scores on every wave and 4 barriers per tile"), sections "Purpose" and
 // "Test Result" (split-K combine).
 //
-// One workgroup per row with ceil(S / 16) waves; wave w owns splits
-// 16w .. 16w + 15 and issues all of their o loads at once (lane = D/64
-// contiguous dims of a split row), so the partials cost about one memory
-// round trip whatever S is. Every wave reads all (m, l) pairs into lanes
+// One workgroup per row and slice of D / DP dims, with ceil(S / 16) waves;
+// wave w owns splits 16w .. 16w + 15 and issues all of their o loads at once
+// (lane = D / (64 DP) contiguous dims of a split row), so the partials cost
+// about one memory round trip whatever S is. With few rows (small batches)
+// the dims are cut into DP slices so that more compute units share the
+// loads. Every wave reads all (m, l) pairs into lanes
 // (split s in lane s % 64, slot s / 64) to get the global max M and the
 // denominator; a split's weight is 2^(m_s - M). Several waves add up through
 // LDS. A split with l = 0 (no visible key) has weight 0 and its o is never
@@ -20,17 +22,20 @@ constexpr int kSplitsPerWave = 16;
 constexpr int kMaxSplitSlots = 4;  // (m, l) slots per lane: 4 x 64 >= PDA_MAX_SPLITS
 constexpr int kMaxCombineWaves = 64 * kMaxSplitSlots / kSplitsPerWave;
 
-template <int D>
+template <int D, int DP>
 __global__ void __launch_bounds__(64 * kMaxCombineWaves)
 pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                    uint16_t* __restrict__ out, int S) {
-  constexpr int DT = D / 64;
+  constexpr int DW = D / DP;  // dims of this workgroup's slice
+  constexpr int DT = DW / 64;
+  static_assert(DT >= 1, "a lane holds at least one dim");
   typedef float fv_t __attribute__((ext_vector_type(DT)));
-  extern __shared__ float red[];  // [waves][D] when there are several waves
+  extern __shared__ float red[];  // [waves][DW] when there are several waves
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const size_t row = blockIdx.x;
+  const int d0 = DW * blockIdx.y;
   const float* ml = part_ml + row * S * 2;
 
   float mv[kMaxSplitSlots], lv[kMaxSplitSlots];
@@ -50,7 +55,7 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   // This wave's o rows, all loads in flight before any is used.
   const int s0 = kSplitsPerWave * wave;
   const int n = min(kSplitsPerWave, S - s0);
-  const float* src = part_o + (row * S + s0) * D + lane * DT;
+  const float* src = part_o + (row * S + s0) * D + d0 + lane * DT;
   fv_t x[kSplitsPerWave];
 #pragma unroll
   for (int j = 0; j < kSplitsPerWave; ++j)
@@ -85,35 +90,45 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
     hv_t y;
 #pragma unroll
     for (int e = 0; e < DT; ++e) y[e] = den > 0.0f ? (_Float16)(acc[e] / den) : (_Float16)0.0f;
-    *reinterpret_cast<hv_t*>(out + row * D + lane * DT) = y;
+    *reinterpret_cast<hv_t*>(out + row * D + d0 + lane * DT) = y;
     return;
   }
-  *reinterpret_cast<fv_t*>(red + wave * D + lane * DT) = acc;
+  *reinterpret_cast<fv_t*>(red + wave * DW + lane * DT) = acc;
   __syncthreads();
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+  for (int d = threadIdx.x; d < DW; d += blockDim.x) {
     float o = 0.0f;
-    for (int w = 0; w < nwaves; ++w) o += red[w * D + d];
+    for (int w = 0; w < nwaves; ++w) o += red[w * DW + d];
     const _Float16 y = den > 0.0f ? (_Float16)(o / den) : (_Float16)0.0f;
-    out[row * D + d] = __builtin_bit_cast(uint16_t, y);
+    out[row * D + d0 + d] = __builtin_bit_cast(uint16_t, y);
   }
 }
 
+int combine_dim_parts(int rows, int head_dim, int num_cus) {
+  int dp = 1;
+  while (2 * dp * 64 <= head_dim && (int64_t)rows * dp < num_cus) dp *= 2;
+  return dp;
+}
+
 hipError_t launch_combine(const float* part_o, const float* part_ml, uint16_t* out,
-                          int rows, int head_dim, int num_splits, hipStream_t stream) {
+                          int rows, int head_dim, int num_splits, int dim_parts,
+                          hipStream_t stream) {
   if (num_splits < 1 || num_splits > 64 * kMaxSplitSlots) return hipErrorInvalidValue;
   const int waves = (num_splits + kSplitsPerWave - 1) / kSplitsPerWave;
-  const dim3 grid(rows), block(64 * waves);
-  const size_t lds = waves > 1 ? (size_t)waves * head_dim * sizeof(float) : 0;
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(pda_combine_kernel<128>, grid, block, lds, stream, part_o, part_ml, out,
-                       num_splits);
-  } else if (head_dim == 256) {
-    hipLaunchKernelGGL(pda_combine_kernel<256>, grid, block, lds, stream, part_o, part_ml, out,
-                       num_splits);
-  } else {
-    return hipErrorInvalidValue;
+  const dim3 grid(rows, dim_parts), block(64 * waves);
+  const size_t lds = waves > 1 ? (size_t)waves * (head_dim / dim_parts) * sizeof(float) : 0;
+#define PDA_CCASE(DD, PP)                                                                  \
+  if (head_dim == DD && dim_parts == PP) {                                                 \
+    hipLaunchKernelGGL((pda_combine_kernel<DD, PP>), grid, block, lds, stream, part_o,     \
+                       part_ml, out, num_splits);                                          \
+    return hipGetLastError();                                                              \
   }
-  return hipGetLastError();
+  PDA_CCASE(128, 1)
+  PDA_CCASE(128, 2)
+  PDA_CCASE(256, 1)
+  PDA_CCASE(256, 2)
+  PDA_CCASE(256, 4)
+#undef PDA_CCASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pda

@@ -126,8 +126,13 @@ hipError_t launch_prefill_i8(int head_dim, dim3 grid, size_t lds, hipStream_t st
 int host_fail(int status, const char* fmt, ...);
 const char* host_last_error();
 
+// Slices of the head dim the combine cuts each row into (1, 2 or 4, at
+// least 64 dims each) so that rows x slices workgroups cover the compute
+// units when there are few rows.
+int combine_dim_parts(int rows, int head_dim, int num_cus);
+
 hipError_t launch_combine(const float* part_o, const float* part_ml,
                           uint16_t* out, int rows, int head_dim, int num_splits,
-                          hipStream_t stream);
+                          int dim_parts, hipStream_t stream);
 
 }  // namespace pda
