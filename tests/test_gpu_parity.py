@@ -335,11 +335,14 @@ def test_workspace_reuse(kernel, D):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
+@pytest.mark.parametrize("T", [5, 90])
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("S", [1, 2, 7, 16, 17, 64, 65, 200, 256])
-def test_split_combine_vs_oracle(D, S):
-    g = torch.Generator(device=DEV).manual_seed(S * D)
-    T, Hq = 5, 3
+def test_split_combine_vs_oracle(D, S, T):
+    # 15 rows: each row's dims are cut into the most slices (2 at D=128, 4 at
+    # D=256); 270 rows (more than the compute units): one slice per row
+    g = torch.Generator(device=DEV).manual_seed(S * D + T)
+    Hq = 3
     m = torch.randn(T, Hq, S, generator=g, device=DEV) * 4
     l = torch.rand(T, Hq, S, generator=g, device=DEV) * 3 + 0.1
     # o_s = l_s * (a softmax-weighted mean of N(0,1) values), as a split writes it
