@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -68,6 +69,16 @@ PREFILL_SOURCES = ("pda_kernels.h", "pda_decode_impl.h", "pda_decode_mfma.h",
                    "pda_prefill_mfma.h", "pda_prefill.hip", "pda_api.hip")
 
 
+_TOKEN = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with whitespace collapsed (string
+    literals kept), so that a comment edit does not count as a kernel change."""
+    text = _TOKEN.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel: str = "decode_mfma") -> str:
     """Hash of the HIP sources of a kernel (the decode step, or the prefill
     kernel when `kernel` starts with "prefill") and of the compiler flags they
@@ -78,8 +89,8 @@ def kernel_source_hash(kernel: str = "decode_mfma") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_split_decode_amd", "csrc")
     for f in PREFILL_SOURCES if kernel.startswith("prefill") else DECODE_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
         h.update(" ".join(pda_build.EXTRA.get(f, [])).encode())
     h.update(" ".join(a for a in pda_build.COMMON if not a.startswith("/")).encode())
     return h.hexdigest()[:16]
