@@ -204,12 +204,14 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
     if (num_splits > 1)
       return fail(PDA_ERR_UNSUPPORTED, "the prefill kernel runs one split (num_splits 0 or 1)");
     const int G = d->num_q_heads / d->num_kv_heads;
-    const int bq = pda::kPrefillRows / G;  // tokens per workgroup
+    const int waves = pda::prefill_waves(d->head_dim, d->max_q_len,
+                                         (int64_t)d->max_pages_per_seq * d->page_size);
+    const int bq = 32 * waves / G;         // tokens per workgroup
     p->rows = bq * G;                      // rows per workgroup
     p->row_tiles = (d->max_q_len + bq - 1) / bq;  // grid x: token blocks
     p->matrix = 1;
     p->splits = 1;
-    p->threads = 256;
+    p->threads = 64 * waves;
     p->lds = pda::prefill_lds_bytes(d->head_dim);
     p->wave_lds = 0;
     p->rows_per_wave = 32;
@@ -317,10 +319,17 @@ pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArg
   hipError_t e;
   if (p.prefill) {
     const dim3 pgrid(p.row_tiles, d->num_kv_heads, d->batch);
+    const int waves = p.threads / 64;
     switch (kv_kind(d->kv_dtype)) {
-      case pda::kKvF16: e = pda::launch_prefill_f16(d->head_dim, pgrid, p.lds, stream, args); break;
-      case pda::kKvFp8: e = pda::launch_prefill_fp8(d->head_dim, pgrid, p.lds, stream, args); break;
-      default: e = pda::launch_prefill_i8(d->head_dim, pgrid, p.lds, stream, args); break;
+      case pda::kKvF16:
+        e = pda::launch_prefill_f16(d->head_dim, waves, pgrid, p.lds, stream, args);
+        break;
+      case pda::kKvFp8:
+        e = pda::launch_prefill_fp8(d->head_dim, waves, pgrid, p.lds, stream, args);
+        break;
+      default:
+        e = pda::launch_prefill_i8(d->head_dim, waves, pgrid, p.lds, stream, args);
+        break;
     }
     if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
     return PDA_OK;

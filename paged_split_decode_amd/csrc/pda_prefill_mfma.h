@@ -3,12 +3,15 @@
 // kernels, for many new tokens per sequence.
 //
 // A workgroup takes a block of new tokens of one sequence and all G query
-// heads of one KV head: 128 (token, head) rows, 32 per wave. K and V go
-// through LDS once per workgroup and serve all 4 waves: each step the 256
+// heads of one KV head: 32 (token, head) rows per wave, 4 or 8 waves (8 at
+// D=128 when the keys before the new tokens are long: chunked prefill). K and
+// V go through LDS once per workgroup and serve all its waves: each step the
 // threads gather 64 keys (four 16-key tiles) of K and V from the paged cache
 // with 16-byte loads, convert 1-byte codes to fp16 (exactly), and write them
 // to one of two fp16 LDS buffers while the waves compute on the other; one
-// barrier per step.
+// barrier per step. A step's loads are issued when the step before the one
+// that stores them ends (NREG = 1), or one step earlier still with 8 waves
+// (NREG = 2: each thread stages half as much, so two register sets fit).
 //
 // Per wave and 32 keys: S^T = K . Q^T with v_mfma_f32_32x32x16_f16 (K
 // fragments read from the LDS tile, the wave's 32 Q rows as the B operand;
@@ -32,8 +35,13 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-template <int D, int KV>
-__global__ void __launch_bounds__(256, D == 128 ? 2 : 1)
+template <int I>
+struct IntC {
+  static constexpr int value = I;
+};
+
+template <int D, int KV, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, D == 128 ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
   // LDS row strides (halves): K rows D + 8 (4 dwords mod 64: the 16 rows of a
   // 128-bit fragment read pass hit disjoint banks), V rows D + 16 (8 dwords
@@ -46,7 +54,12 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   constexpr int EB = KV == kKvF16 ? 2 : 1;
   constexpr int PIECES = D * EB / 16;                // 16-byte pieces of a cache row
   constexpr int NPIECE = 2 * KT * 16 * PIECES;      // K and V pieces of one step
-  constexpr int LOADS = (NPIECE + 255) / 256;        // per thread
+  constexpr int NTHREADS = 64 * WAVES;
+  constexpr int LOADS = NPIECE / NTHREADS;           // per thread and step
+  // Steps whose loads are in flight in registers (each in its own set): the
+  // loads of step s + NREG + 1 are issued when step s ends and go to LDS when
+  // step s + NREG ends.
+  constexpr int NREG = WAVES == 8 ? 2 : 1;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);
@@ -112,18 +125,18 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     return (size_t)bt[u >> tshift] * a.page_bytes + (size_t)((u & tmask) * kPageSize) * key_stride;
   };
 
-  // Staging: thread piece p = tid + 256 l (< NPIECE) is K or V (kv), tile tt
-  // of the step, key row, 16-byte piece; all of that is fixed per thread, so
-  // its byte offset within a tile and its LDS position are computed once.
-  // Each step only moves the (scalar) tile bases.
-  static_assert(NPIECE % 256 == 0, "every thread stages whole pieces");
+  // Staging: thread piece p = tid + NTHREADS l (< NPIECE) is K or V (kv),
+  // tile tt of the step, key row, 16-byte piece; all of that is fixed per
+  // thread, so its byte offset within a tile and its LDS position are computed
+  // once. Each step only moves the (scalar) tile bases.
+  static_assert(NPIECE % NTHREADS == 0, "every thread stages whole pieces");
   uint32_t src_off[LOADS];
   uint32_t lds_off[LOADS];  // in halves
   int row_of[LOADS], tt_of[LOADS];
   bool is_v[LOADS];
 #pragma unroll
   for (int l = 0; l < LOADS; ++l) {
-    const int p = tid + 256 * l;
+    const int p = tid + NTHREADS * l;
     const int kv = p / (KT * 16 * PIECES);
     const int rem = p - kv * (KT * 16 * PIECES);
     tt_of[l] = rem / (16 * PIECES);
@@ -134,8 +147,9 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     lds_off[l] = (uint32_t)(kv ? KT * TILEK + tt_of[l] * TILEV + row_of[l] * LRV
                                : tt_of[l] * TILEK + row_of[l] * LRK) + piece * (16 / EB);
   }
-  uint32_t stage[LOADS][4];
-  auto stage_load = [&](int step) {
+  uint32_t stage_regs[NREG][LOADS][4];
+  auto stage_load = [&](int step, auto set_c) __attribute__((always_inline)) {
+    auto& stage = stage_regs[decltype(set_c)::value];
     const int u0 = t_lo + step * KT;
     size_t base[KT];
 #pragma unroll
@@ -148,13 +162,14 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       for (int e = 0; e < 4; ++e) stage[l][e] = x[e];
     }
   };
-  auto stage_store = [&](int step, int buf) {
+  auto stage_store = [&](int step, int buf, auto set_c) __attribute__((always_inline)) {
+    auto& stage = stage_regs[decltype(set_c)::value];
     const int j0 = (t_lo + step * KT) * kPageSize;
     _Float16* dst0 = lds + (size_t)buf * BUF;
     // Slots past the sequence (arbitrary contents), and tiles past this
     // workgroup's range (staged from a clamped tile), become zeros. Only a
     // step that reaches past either needs the per-slot test (wave-uniform).
-    auto put = [&](auto checked) {
+    auto put = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
       for (int l = 0; l < LOADS; ++l) {
         bool live = true;
@@ -231,7 +246,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 
   typedef short s4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4_t lds_s4_t;
-  auto tr_read = [&](const _Float16* src) {
+  auto tr_read = [&](const _Float16* src) __attribute__((always_inline)) {
     return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src));
   };
@@ -245,17 +260,17 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // interleaved (scores2), with each k-step's K fragments read one step
   // ahead; D=256 (one wave per SIMD, no registers to spare) runs the halves
   // one after the other.
-  auto frag = [&](const _Float16* kb, int t) {
+  auto frag = [&](const _Float16* kb, int t) __attribute__((always_inline)) {
     return *reinterpret_cast<const h8_t*>(kb + rr * LRK + 16 * t + 8 * hh);
   };
-  auto scores = [&](const _Float16* kb) {
+  auto scores = [&](const _Float16* kb) __attribute__((always_inline)) {
     f16v_t st = {};
 #pragma unroll
     for (int t = 0; t < NK; ++t)
       st = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag(kb, t), qb[t], st, 0, 0, 0);
     return st;
   };
-  auto scores2 = [&](const _Float16* kb0, const _Float16* kb1, f16v_t& s0, f16v_t& s1) {
+  auto scores2 = [&](const _Float16* kb0, const _Float16* kb1, f16v_t& s0, f16v_t& s1) __attribute__((always_inline)) {
     h8_t k0 = frag(kb0, 0), k1 = frag(kb1, 0);
     s0 = f16v_t{};
     s1 = f16v_t{};
@@ -273,7 +288,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     }
   };
   // Softmax and P.V of 32 keys from key0 whose scores are st.
-  auto softmax_pv = [&](f16v_t st, const _Float16* vb, int key0) {
+  auto softmax_pv = [&](f16v_t st, const _Float16* vb, int key0) __attribute__((always_inline)) {
     const bool full = key0 >= lo_max && key0 + 31 <= hi_min;
     uint32_t vis = 0xFFFFu;  // bit 4 j + i: key key0 + 8 j + 4 hh + i visible to row rr
     float mt;
@@ -345,12 +360,16 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   };
 
   if (n_steps > 0) {
-    stage_load(0);
-    stage_store(0, 0);
+    stage_load(0, IntC<0>{});
+    stage_store(0, 0, IntC<0>{});
+    if (n_steps > 1) stage_load(1, IntC<0>{});
+    if constexpr (NREG == 2) {
+      if (n_steps > 2) stage_load(2, IntC<1>{});
+    }
     __syncthreads();
-    for (int step = 0; step < n_steps; ++step) {
+    // Step `step` reads LDS buffer step & 1; register set SET holds step + 1.
+    auto step_body = [&](int step, auto set_c) __attribute__((always_inline)) {
       const int buf = step & 1;
-      if (step + 1 < n_steps) stage_load(step + 1);
       const _Float16* kb = lds + (size_t)buf * BUF;
       const _Float16* vb = kb + KT * TILEK;
       const int key0 = (t_lo + step * KT) * kPageSize;
@@ -368,8 +387,15 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       }
       if (a0) softmax_pv(st0, vb, key0);
       if (a1) softmax_pv(st1, vb + 2 * TILEV, key0 + 32);
-      if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1);
+      if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1, set_c);
+      if (step + 1 + NREG < n_steps) stage_load(step + 1 + NREG, set_c);
       __syncthreads();
+    };
+    for (int step = 0; step < n_steps; step += NREG) {
+      step_body(step, IntC<0>{});
+      if constexpr (NREG == 2) {
+        if (step + 1 < n_steps) step_body(step + 1, IntC<1>{});
+      }
     }
   }
 
@@ -401,16 +427,18 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 }
 
 template <int KV>
-hipError_t launch_prefill_kv(int head_dim, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_kv(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
                              const DecodeArgs& args) {
-  if (head_dim == 128) {
-    hipLaunchKernelGGL((pda_prefill_mfma_kernel<128, KV>), grid, dim3(256), lds, stream, args);
-    return hipGetLastError();
+#define PDA_PCASE(DD, WW)                                                                      \
+  if (head_dim == DD && waves == WW) {                                                         \
+    hipLaunchKernelGGL((pda_prefill_mfma_kernel<DD, KV, WW>), grid, dim3(64 * WW), lds, stream, \
+                       args);                                                                  \
+    return hipGetLastError();                                                                  \
   }
-  if (head_dim == 256) {
-    hipLaunchKernelGGL((pda_prefill_mfma_kernel<256, KV>), grid, dim3(256), lds, stream, args);
-    return hipGetLastError();
-  }
+  PDA_PCASE(128, 4)
+  PDA_PCASE(128, 8)
+  PDA_PCASE(256, 4)
+#undef PDA_PCASE
   return hipErrorInvalidValue;
 }
 

@@ -42,6 +42,19 @@ def test_prefill_parity(kv, D, G):
     assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv, f"prefill D={D} {kv} G={G}")
 
 
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+@pytest.mark.parametrize("table_pad", [1, 200])
+def test_prefill_both_workgroup_shapes(kv, table_pad):
+    # The same batch through a tight block table (capacity 320 keys < 4 x 300
+    # new tokens: 4-wave workgroups) and a roomy one (3504 keys: 8-wave
+    # workgroups at D=128, with two steps of loads in flight).
+    c = _ragged(77, q_lens=[300, 61, 190], ctx=[0, 40, 10], kv_dtype=kv, table_pad=table_pad,
+                num_q_heads=16, num_kv_heads=4)
+    cap = c.block_table.shape[1] * c.workload.page_size
+    assert (4 * 300 <= cap) == (table_pad == 200)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv, f"prefill pad={table_pad} {kv}")
+
+
 @pytest.mark.parametrize("window", [1, 64, 300])
 @pytest.mark.parametrize("layout,P", [("NHD", 16), ("HND", 64)])
 def test_prefill_window_layouts(window, layout, P):
