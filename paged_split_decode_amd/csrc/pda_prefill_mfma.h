@@ -59,7 +59,12 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // Steps whose loads are in flight in registers (each in its own set): the
   // loads of step s + NREG + 1 are issued when step s ends and go to LDS when
   // step s + NREG ends.
+#ifdef PDA_PREFILL_NREG8
+  constexpr int NREG = WAVES == 8 ? PDA_PREFILL_NREG8 : 1;  // tuning override
+#else
   constexpr int NREG = WAVES == 8 ? 2 : 1;
+#endif
+  static_assert(NREG >= 1 && NREG <= 3, "one to three register sets");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
   _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);
@@ -363,8 +368,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     stage_load(0, IntC<0>{});
     stage_store(0, 0, IntC<0>{});
     if (n_steps > 1) stage_load(1, IntC<0>{});
-    if constexpr (NREG == 2) {
+    if constexpr (NREG >= 2) {
       if (n_steps > 2) stage_load(2, IntC<1>{});
+    }
+    if constexpr (NREG >= 3) {
+      if (n_steps > 3) stage_load(3, IntC<2>{});
     }
     __syncthreads();
     // Step `step` reads LDS buffer step & 1; register set SET holds step + 1.
@@ -393,8 +401,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     };
     for (int step = 0; step < n_steps; step += NREG) {
       step_body(step, IntC<0>{});
-      if constexpr (NREG == 2) {
+      if constexpr (NREG >= 2) {
         if (step + 1 < n_steps) step_body(step + 1, IntC<1>{});
+      }
+      if constexpr (NREG >= 3) {
+        if (step + 2 < n_steps) step_body(step + 2, IntC<2>{});
       }
     }
   }
