@@ -277,6 +277,38 @@ def test_uniform_v_returns_v_bit_exact(splits, kernel):
     assert torch.all(got == torch.tensor(0.7, dtype=torch.float16)).item()
 
 
+def _shape_scores(c, a_of_j):
+    """Keys k_j = a_j * ones and queries 0.25 * ones, so that key j scores
+    scale * 0.25 * D * a_j for every row: the running maximum can be made to
+    climb page after page (a rescale of the accumulators on every page), to
+    fall (none after the first), or to jump between pages."""
+    P = c.workload.page_size
+    D = c.q.shape[-1]
+    c.q = torch.full_like(c.q, 0.25)
+    for b, L in enumerate(c.seq_lens_host.tolist()):
+        j = torch.arange(L)
+        pages = c.block_table[b].cpu()[j // P].long()
+        a = torch.tensor([a_of_j(int(x), L) for x in j], dtype=torch.float32)
+        rows = (a[:, None, None] * torch.ones(1, c.k_cache.shape[2], D)).to(torch.float16)
+        c.k_cache[pages.to(DEV), (j % P).to(DEV)] = rows.to(DEV)
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "zigzag"])
+@pytest.mark.parametrize("splits", [1, 5])
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_score_ramps_exercise_the_rescale(pattern, splits, D, kernel):
+    # about 150 natural-log units of score over the sequence: 8 or more per
+    # 16-key page when rising, beyond the lazy reference's slack of 8 (base 2)
+    top = 150.0 / (0.25 * D / np.sqrt(D))
+    fn = {"rising": lambda j, L: top * j / L,
+          "falling": lambda j, L: top * (1 - j / L),
+          "zigzag": lambda j, L: top * ((j // 16) % 2) * (0.5 + 0.5 * j / L)}[pattern]
+    c = case_on_gpu(small(23, seq_lens=(300, 47, 1), head_dim=D, q_len=2, num_splits=splits))
+    _shape_scores(c, fn)
+    assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), "f16", f"{pattern} D={D}")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_q_lens_null_equals_ones(kernel):
     c = case_on_gpu(small(20, num_splits=2))
