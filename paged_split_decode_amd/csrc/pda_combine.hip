@@ -22,6 +22,46 @@ constexpr int kSplitsPerWave = 16;
 constexpr int kMaxSplitSlots = 4;  // (m, l) slots per lane: 4 x 64 >= PDA_MAX_SPLITS
 constexpr int kMaxCombineWaves = 64 * kMaxSplitSlots / kSplitsPerWave;
 
+// Wave-wide max and sum without LDS: DPP within each 16-lane row (swap
+// neighbours, then pairs, then mirror 8- and 16-lane halves), then the row
+// pairs and halves of the wave through permlane16/32 swaps. Every lane ends
+// with the result.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_get(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swap16(float v, bool sum) {
+  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                            false, false);
+  const float x = __builtin_bit_cast(float, (int)a[0]), y = __builtin_bit_cast(float, (int)a[1]);
+  return sum ? x + y : fmaxf(x, y);
+}
+__device__ __forceinline__ float swap32(float v, bool sum) {
+  auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                            false, false);
+  const float x = __builtin_bit_cast(float, (int)a[0]), y = __builtin_bit_cast(float, (int)a[1]);
+  return sum ? x + y : fmaxf(x, y);
+}
+constexpr int kQuadSwap1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int kRowMirror = 0x140;   // lane i <-> 15 - i within each 16 lanes
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_get<kQuadSwap1>(v));
+  v = fmaxf(v, dpp_get<kQuadSwap2>(v));
+  v = fmaxf(v, dpp_get<kHalfMirror>(v));
+  v = fmaxf(v, dpp_get<kRowMirror>(v));
+  return swap32(swap16(v, false), false);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_get<kQuadSwap1>(v);
+  v += dpp_get<kQuadSwap2>(v);
+  v += dpp_get<kHalfMirror>(v);
+  v += dpp_get<kRowMirror>(v);
+  return swap32(swap16(v, true), true);
+}
+
 template <int D, int DP>
 __global__ void __launch_bounds__(64 * kMaxCombineWaves)
 pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -30,6 +70,7 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   constexpr int DT = DW / 64;
   static_assert(DT >= 1, "a lane holds at least one dim");
   typedef float fv_t __attribute__((ext_vector_type(DT)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
   extern __shared__ float red[];  // [waves][DW] when there are several waves
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -38,51 +79,55 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   const int d0 = DW * blockIdx.y;
   const float* ml = part_ml + row * S * 2;
 
-  float mv[kMaxSplitSlots], lv[kMaxSplitSlots];
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kMaxSplitSlots; ++k) {
-    const int s = lane + 64 * k;
-    mv[k] = -INFINITY;
-    lv[k] = 0.0f;
-    if (s < S) {
-      mv[k] = ml[2 * s];
-      lv[k] = ml[2 * s + 1];
-    }
-    if (lv[k] > 0.0f) M = fmaxf(M, mv[k]);
-  }
-
-  // This wave's o rows, all loads in flight before any is used.
+  // Every load is issued before any is used, with no branches between them:
+  // indexes past the last split are clamped to it (in bounds) and their
+  // weight is 0. First this wave's o rows (splits s0 .. s0 + 15) ...
   const int s0 = kSplitsPerWave * wave;
-  const int n = min(kSplitsPerWave, S - s0);
+  const int n = min(kSplitsPerWave, S - s0);  // >= 1: the waves cover S exactly
   const float* src = part_o + (row * S + s0) * D + d0 + lane * DT;
   fv_t x[kSplitsPerWave];
 #pragma unroll
   for (int j = 0; j < kSplitsPerWave; ++j)
-    if (j < n) x[j] = *reinterpret_cast<const fv_t*>(src + (size_t)j * D);
+    x[j] = *reinterpret_cast<const fv_t*>(src + (size_t)min(j, n - 1) * D);
+  // ... then every split's (m, l): split lane + 64 k in slot k of the lane.
+  f2_t p[kMaxSplitSlots];
+#pragma unroll
+  for (int k = 0; k < kMaxSplitSlots; ++k)
+    p[k] = *reinterpret_cast<const f2_t*>(ml + 2 * min(lane + 64 * k, S - 1));
 
-  for (int k = 32; k >= 1; k >>= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+  float mv[kMaxSplitSlots], lv[kMaxSplitSlots];
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxSplitSlots; ++k) {
+    const bool live = lane + 64 * k < S && p[k][1] > 0.0f;
+    mv[k] = live ? p[k][0] : -INFINITY;
+    lv[k] = live ? p[k][1] : 0.0f;
+    M = fmaxf(M, mv[k]);
+  }
+  M = wave_max(M);
   float wv[kMaxSplitSlots];
   float den = 0.0f;
 #pragma unroll
   for (int k = 0; k < kMaxSplitSlots; ++k) {
-    wv[k] = (lv[k] > 0.0f) ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.0f;
+    wv[k] = lv[k] > 0.0f ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.0f;
     den += wv[k] * lv[k];
   }
-  for (int k = 32; k >= 1; k >>= 1) den += __shfl_xor(den, k, 64);
+  den = wave_sum(den);
 
-  // Weights of splits s0 .. s0 + 15: slot s0 / 64, lanes s0 % 64 + j.
+  // Weights of splits s0 .. s0 + 15: slot s0 / 64, lanes s0 % 64 + j. A
+  // split with weight 0 (no visible key, or past S) is never added: its o may
+  // hold anything.
   const int slot = s0 >> 6;
   const float wsel = slot == 0 ? wv[0] : slot == 1 ? wv[1] : slot == 2 ? wv[2] : wv[3];
   const int lane0 = s0 & 63;
   fv_t acc = {};
 #pragma unroll
   for (int j = 0; j < kSplitsPerWave; ++j) {
-    if (j < n) {
-      const float w = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsel), lane0 + j));
-      if (w > 0.0f) acc += w * x[j];
-    }
+    const float w = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsel), lane0 + j));
+    const fv_t t = acc + w * x[j];
+#pragma unroll
+    for (int e = 0; e < DT; ++e) acc[e] = w > 0.0f ? t[e] : acc[e];
   }
 
   if (nwaves == 1) {
