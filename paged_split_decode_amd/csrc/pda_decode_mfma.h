@@ -55,8 +55,9 @@ struct MGeom {
 };
 
 // Pages in a wave's load ring (NB - 1 pages in flight while one is used).
-// Deeper rings measured no faster: a wave is issue-bound before it runs out
-// of bytes in flight. PDA_RING overrides it when tuning.
+// Deeper rings measured no faster (the full grid keeps enough bytes in flight
+// for the gather rate; deeper ones only add registers). PDA_RING overrides it
+// when tuning.
 template <int D, int KV, int NRT>
 constexpr int mfma_ring_depth() {
 #ifdef PDA_RING
