@@ -55,6 +55,16 @@ def test_prefill_both_workgroup_shapes(kv, table_pad):
     assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv, f"prefill pad={table_pad} {kv}")
 
 
+@pytest.mark.parametrize("G", [16, 48, 128])
+@pytest.mark.parametrize("table_pad", [1, 300])
+def test_prefill_large_groups(G, table_pad):
+    # Workgroups whose last waves have some or no rows (G = 48: 240 of 256
+    # rows with 8 waves, 96 of 128 with 4; G = 128: two tokens per workgroup).
+    c = _ragged(G + table_pad, q_lens=[70, 9], ctx=[30, 200], table_pad=table_pad,
+                num_q_heads=2 * G, num_kv_heads=2)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill G={G}")
+
+
 @pytest.mark.parametrize("window", [1, 64, 300])
 @pytest.mark.parametrize("layout,P", [("NHD", 16), ("HND", 64)])
 def test_prefill_window_layouts(window, layout, P):
