@@ -56,6 +56,8 @@ CELLS = [
     *[("gqa6_d256_l16384", dict(batch=b, window=win))
       for win in (0, 4096) for b in (1, 2, 3, 8, 32)],
     ("verify_q3_d128_b32", {}),
+    # the same ragged batch with automatic splits (balanced per sequence)
+    ("verify_q3_d128_b32", dict(num_splits=0)),
     ("quant_fp8_d256_b64_l32768", {}),
     ("quant_int8_d256_b64_l32768", {}),
 ]
@@ -125,18 +127,14 @@ class Runner:
         c = case
         self.dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens,
                                     c.max_q_len, c.kv_dtype, kernel, c.kv_layout)
-        self.S = pda.resolve_splits(self.dims, c.window, num_splits)
+        # 0 stays 0 (automatic: split counts balanced per sequence where the
+        # matrix kernel can); a caller's count is used as given.
+        self.S = num_splits
         T, Hq, D = c.q.shape
         self.T, self.Hq, self.D = T, Hq, D
         self.out = torch.empty((T, Hq, D), dtype=torch.float16, device=device)
-        # One-call path workspace, and the decode-stage-only path's partials.
         nws = pda.workspace_bytes(self.dims, c.window, self.S)
         self.ws_all = torch.empty(max(nws, 16), dtype=torch.uint8, device=device)
-        nbytes = pda.partials_bytes(self.dims, c.window, self.S)
-        self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
-        self.po, self.pml = pda.partials_views(self.ws, T, Hq, self.S, D)
-        # With several splits a step is two launches (decode, then combine).
-        self.two_launches = self.S > 1
         # Replicas of everything a step reads, so consecutive steps do not
         # hit in the Infinity Cache.
         self.reps = [(c.q, c.k_cache, c.v_cache)]
@@ -150,9 +148,7 @@ class Runner:
         self.scales = (None if c.k_scale is None else P(c.k_scale.data_ptr()),
                        None if c.v_scale is None else P(c.v_scale.data_ptr()))
         self.dims_ref = ctypes.byref(self.dims)
-        self.ws_ptr, self.ws_bytes = P(self.ws.data_ptr()), nbytes
         self.wsa_ptr, self.wsa_bytes = P(self.ws_all.data_ptr()), self.ws_all.numel()
-        self.po_ptr, self.pml_ptr = P(self.po.data_ptr()), P(self.pml.data_ptr())
         self.out_ptr = P(self.out.data_ptr())
         self.rep_ptrs = [tuple(P(t.data_ptr()) for t in r) for r in self.reps]
 
@@ -166,14 +162,12 @@ class Runner:
             raise RuntimeError(self.lib.pda_last_error().decode())
 
     def decode(self, i: int):
-        """The dominant kernel alone: the decode stage of a two-launch step,
-        otherwise the step's single launch."""
-        if not self.two_launches:
-            return self.step(i)
+        """The dominant kernel alone: the decode stage of the same call (the
+        step's first launch; its only one with one split)."""
         q, k, v = self.rep_ptrs[i % len(self.rep_ptrs)]
-        st = self.lib.pda_paged_decode_partials(
-            q, k, v, *self.common, *self.scales, self.dims_ref, self.ws_ptr,
-            self.ws_bytes, self.stream)
+        st = self.lib.pda_attention_decode_stage(
+            q, k, v, *self.common, self.out_ptr, *self.scales, self.dims_ref, self.wsa_ptr,
+            self.wsa_bytes, self.stream)
         if st != 0:
             raise RuntimeError(self.lib.pda_last_error().decode())
 
@@ -233,7 +227,7 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     torch.cuda.synchronize()
     decode_ms = t0.elapsed_time(t1) / steps
     return dict(ms_per_step=ms_step, ms_eager=ms_eager, decode_ms=decode_ms, bytes=nbytes,
-                splits=r.S, replicas=replicas)
+                splits=r.S if r.S >= 1 else "auto", replicas=replicas)
 
 
 def cpu_baseline(case, budget_s: float = 12.0):

@@ -141,8 +141,8 @@ typedef struct pda_decode_dims {
  *  q_lens       int32 [B], or NULL: every sequence has one new token.
  *  scale        multiplier of q.k (fp32), e.g. 1/sqrt(D).
  *  window       sliding window in keys; <= 0: none.
- *  num_splits   key splits per (sequence, KV head); 0: chosen by
- *               pda_decode_resolve_splits; otherwise 1..PDA_MAX_SPLITS.
+ *  num_splits   key splits per (sequence, KV head), 1..PDA_MAX_SPLITS; or 0
+ *               for an automatic choice (below).
  *  out          fp16 [T, Hq, D], fully overwritten.
  *  k_scale      fp32 [Hkv] for fp8/int8 KV (NULL for fp16).
  *  v_scale      fp32 [Hkv] for fp8/int8 KV (NULL for fp16).
@@ -154,6 +154,19 @@ typedef struct pda_decode_dims {
  * With one split the decode kernel writes `out` directly; with more, it
  * writes partials and a second launch (the combine kernel) merges them. Both
  * launches go on `stream`.
+ *
+ * Automatic splits (num_splits 0) with the matrix kernel balance the work
+ * over the batch when it has fewer sequences than the workgroups that fit on
+ * the device at once: the decode kernel reads seq_lens and q_lens and cuts
+ * every sequence into chunks of one common size (in 16-key tiles), the
+ * smallest size whose chunks all fit in one round of workgroups, so a ragged
+ * batch's long sequences get proportionally more splits (at most
+ * PDA_MAX_SPLITS per row). A sequence that gets one chunk is written to `out`
+ * by the decode kernel; the combine merges the others. A uniform batch gets
+ * the same chunks as a fixed count would give it. Otherwise (vector kernel,
+ * or a batch as large as one round) the automatic count is
+ * pda_decode_resolve_splits's, the same for every sequence. The result does
+ * not depend on the split choice beyond fp32 rounding.
  */
 pda_status pda_paged_decode_attention(
     const void* q, const void* k_cache, const void* v_cache,
@@ -163,10 +176,31 @@ pda_status pda_paged_decode_attention(
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The two launches of pda_paged_decode_attention, one call each, for callers
+ * that time them apart or put other work between them. Called in this
+ * order, on one stream, with the same arguments and the same workspace, they
+ * do exactly what pda_paged_decode_attention does. The decode stage writes
+ * `out` for rows it finishes alone and the workspace for the rest; the
+ * combine stage merges the workspace into `out` (it launches nothing when
+ * the call has one split). Between them the workspace layout is private to
+ * the library.
+ */
+pda_status pda_attention_decode_stage(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+    float scale, int32_t window, int32_t num_splits, void* out,
+    const float* k_scale, const float* v_scale, const pda_decode_dims* dims,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+pda_status pda_attention_combine_stage(
+    void* out, const pda_decode_dims* dims, int32_t window, int32_t num_splits,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The decode stage alone: writes the per-split partials of every row into
  * `workspace` (always, also for one split) and launches nothing else.
  * Arguments as for pda_paged_decode_attention, without `out`; `num_splits`
- * 0 resolves as there. Partials layout, with S the resolved split count:
+ * 0 resolves to pda_decode_resolve_splits's count (one count for every
+ * sequence: no balancing). Partials layout, with S the resolved split count:
  *
  *   partial_o  = (float*)workspace                       [T, Hq, S, D]
  *   partial_ml = (float*)workspace + T * Hq * S * D      [T, Hq, S, 2]
@@ -236,16 +270,19 @@ pda_status pda_write_kv_cache(const void* key, const void* value,
                               const float* v_scale, const pda_cache_dims* dims,
                               hipStream_t stream);
 
-/* Split count a call with these sizes uses: `num_splits` itself when it is
- * >= 1, otherwise the automatic choice for a device with `num_cus` compute
- * units (num_cus <= 0: the current device's count). Host-only; no launch.
- * Returns a value in 1..PDA_MAX_SPLITS, or a negative pda_status. */
+/* Split count of a call with one count for every sequence: `num_splits`
+ * itself when it is >= 1, otherwise the automatic choice for a device with
+ * `num_cus` compute units (num_cus <= 0: the current device's count), which
+ * pda_paged_decode_partials uses (pda_paged_decode_attention may balance
+ * counts per sequence instead). Host-only; no launch. Returns a value in
+ * 1..PDA_MAX_SPLITS, or a negative pda_status. */
 int32_t pda_decode_resolve_splits(const pda_decode_dims* dims, int32_t window,
                                   int32_t num_splits, int32_t num_cus);
 
-/* Workspace bytes pda_paged_decode_attention needs (0 for one split) with
- * the split count resolved as above; pda_paged_decode_partials needs
- * pda_decode_partials_bytes. Host-only. Negative on invalid sizes. */
+/* Workspace bytes pda_paged_decode_attention (and its two stages) needs
+ * for these arguments on the current device (0 for one split);
+ * pda_paged_decode_partials needs pda_decode_partials_bytes, with the split
+ * count resolved as above. Host-only. Negative on invalid sizes. */
 int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
                                    int32_t num_splits);
 int64_t pda_decode_partials_bytes(const pda_decode_dims* dims, int32_t window,

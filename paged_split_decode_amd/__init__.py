@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "paged_decode_attention", "paged_decode_partials", "split_combine",
-    "resolve_splits", "workspace_bytes", "partials_bytes", "decode_dims",
+    "resolve_splits", "workspace_bytes", "attention_stages", "partials_bytes", "decode_dims",
     "load_library", "library_path", "KV_DTYPES", "PDA_MAX_ROWS", "PDA_MAX_SPLITS",
     "PdaError", "partials_views", "KERNELS",
 ]
@@ -63,6 +63,11 @@ _SIGNATURES = {
     "pda_paged_decode_attention": (ctypes.c_int, [
         _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
         _VP, _VP, _VP, _DIMS, _VP, ctypes.c_size_t, _VP]),
+    "pda_attention_decode_stage": (ctypes.c_int, [
+        _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+        _VP, _VP, _VP, _DIMS, _VP, ctypes.c_size_t, _VP]),
+    "pda_attention_combine_stage": (ctypes.c_int, [
+        _VP, _DIMS, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]),
     "pda_paged_decode_partials": (ctypes.c_int, [
         _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
         _VP, _VP, _DIMS, _VP, ctypes.c_size_t, _VP]),
@@ -191,6 +196,35 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, s
         _ptr(q_lens), float(scale), int(window), int(num_splits), _ptr(out),
         _ptr(k_scale), _ptr(v_scale), ctypes.byref(dims), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def attention_stages(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale, window,
+                     num_splits, out, k_scale=None, v_scale=None, kv_dtype=None,
+                     max_q_len=None, workspace=None, stream=None, kernel="auto",
+                     kv_layout="NHD", stage="both"):
+    """paged_decode_attention as its two launches, run one at a time
+    (``stage`` "decode", "combine" or "both"; a combine stage must follow a
+    decode stage of the same call on the same ``workspace``). Returns the
+    workspace used."""
+    lib = load_library()
+    _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, out, k_scale, v_scale)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel,
+                       kv_layout)
+    need = workspace_bytes(dims, window, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stage in ("decode", "both"):
+        _check(lib.pda_attention_decode_stage(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+            _ptr(q_lens), float(scale), int(window), int(num_splits), _ptr(out),
+            _ptr(k_scale), _ptr(v_scale), ctypes.byref(dims), _ptr(workspace), ws_bytes,
+            _stream(stream)))
+    if stage in ("combine", "both"):
+        _check(lib.pda_attention_combine_stage(
+            _ptr(out), ctypes.byref(dims), int(window), int(num_splits), _ptr(workspace),
+            ws_bytes, _stream(stream)))
+    return workspace
 
 
 def paged_decode_partials(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,

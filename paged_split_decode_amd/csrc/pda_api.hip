@@ -80,6 +80,10 @@ struct Plan {
   int heads_per_group; // matrix kernel: KV heads per workgroup
   int head_groups;     // grid y: workgroups across the KV heads
   int longest_first;   // matrix kernel: order grid rows by sequence length
+  int balanced;        // matrix kernel: per-sequence split counts on the device
+  int chunks;          // balanced: chunk slots per KV-head group (grid x)
+  int min_chunk;       // balanced: fewest 16-key tiles per chunk
+  int combine_waves;   // balanced: waves per combine workgroup
   int splits;
   int threads;
   size_t lds;
@@ -146,6 +150,14 @@ int64_t visible_tiles(const pda_decode_dims* d, int window) {
 }
 
 // Workgroup shape and split count of the matrix kernel.
+//  * Automatic splits with length balancing (allowed for the one-call path):
+//    the grid has as many chunk slots as workgroups fit at once, and the
+//    kernel cuts every sequence into chunks of one common size, so each
+//    workgroup gets about the same number of pages however ragged the batch
+//    is (a fixed split count per sequence leaves the compute units that hold
+//    the longest sequences working alone at the end). Used while the batch
+//    is smaller than the slot count; a uniform batch gets the same chunks as
+//    a fixed count would give it.
 //  * Up to 4 KV heads share a workgroup, one wave each: the heads of a page
 //    block (contiguous in the pool) are then fetched together, which measures
 //    faster than one head per workgroup. Fewer heads leave room for several
@@ -155,7 +167,7 @@ int64_t visible_tiles(const pda_decode_dims* d, int window) {
 //  * A caller's split count: the head group shrinks until the workgroups
 //    cover every compute unit, and key_waves grows to fill the wave slots.
 void matrix_plan(const pda_decode_dims* d, int window, int num_splits, int num_cus,
-                 int waves_per_simd, int max_waves, Plan* p) {
+                 int waves_per_simd, int max_waves, bool allow_balanced, Plan* p) {
   const int64_t pages = visible_tiles(d, window);  // in 16-key tiles
   const int64_t B = std::max(1, d->batch);
   const int Hkv = d->num_kv_heads;
@@ -163,14 +175,7 @@ void matrix_plan(const pda_decode_dims* d, int window, int num_splits, int num_c
   int hpw = std::min({Hkv, 4, max_waves});
   int kw = std::max(1, std::min(4, max_waves) / hpw);
   int64_t S;
-  if (num_splits >= 1) {
-    S = num_splits;
-    while (hpw > 1 && S * B * groups(hpw) < num_cus) hpw = (hpw + 1) / 2;
-    const int64_t slots = (int64_t)num_cus * 4 * waves_per_simd;
-    const int64_t want = slots / (S * B * groups(hpw) * hpw);
-    const int64_t by_pages = std::max<int64_t>(1, pages / (2 * S));
-    kw = (int)std::max<int64_t>(1, std::min<int64_t>({want, max_waves / hpw, by_pages}));
-  } else {
+  if (num_splits < 1) {
     // Fill every SIMD's wave slots once, never a second round. (At two
     // waves per SIMD the second workgroup per CU hides the first one's
     // latency: the headline shape decodes in 27.3 us at 32 splits against
@@ -178,21 +183,47 @@ void matrix_plan(const pda_decode_dims* d, int window, int num_splits, int num_c
     S = (int64_t)num_cus * waves_per_simd / (B * groups(hpw));
     S = std::min<int64_t>(S, std::max<int64_t>(1, pages / (2 * kw)));
     S = std::max<int64_t>(1, std::min<int64_t>(S, PDA_MAX_SPLITS));
+  } else {
+    S = num_splits;
   }
+  // Workgroup shape for S splits per sequence: the head group shrinks until
+  // the workgroups cover every compute unit, and key_waves grows to fill the
+  // wave slots.
+  hpw = std::min({Hkv, 4, max_waves});
+  while (hpw > 1 && S * B * groups(hpw) < num_cus) hpw = (hpw + 1) / 2;
+  const int64_t slots = (int64_t)num_cus * 4 * waves_per_simd;
+  const int64_t want = slots / (S * B * groups(hpw) * hpw);
+  const int64_t by_pages = std::max<int64_t>(1, pages / (2 * S));
+  kw = (int)std::max<int64_t>(1, std::min<int64_t>({want, max_waves / hpw, by_pages}));
   p->heads_per_group = hpw;
   p->key_waves = kw;
   p->head_groups = (int)groups(hpw);
   p->splits = (int)S;
+  p->balanced = 0;
+  p->chunks = 0;
+  p->min_chunk = 0;
+  p->combine_waves = 0;
   // With more workgroups than fit at once, dispatch the longest sequences
   // first (ragged batches then finish together); with one round the order
   // cannot matter.
   const int64_t wgs = S * B * groups(hpw);
   const int64_t wg_fit = (int64_t)num_cus * std::max(1, 4 * waves_per_simd / (hpw * kw));
   p->longest_first = d->batch <= 64 && wgs > wg_fit;
+  // Automatic splits, balanced: the same workgroups (S per sequence on
+  // average), cut by length on the device.
+  if (num_splits < 1 && allow_balanced && S >= 2 && d->batch < 256) {
+    p->balanced = 1;
+    p->chunks = (int)(S * B);
+    p->min_chunk = 2 * kw;
+    // Waves of a combine workgroup: one per 16 splits of a uniform batch's
+    // row; the longer rows of a ragged batch take more passes.
+    p->combine_waves = (int)((S + 15) / 16);
+    p->longest_first = 0;
+  }
 }
 
 pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_splits, int num_cus,
-                     Plan* p) {
+                     Plan* p, bool allow_balanced = false) {
   pda_status st = check_dims(d);
   if (st != PDA_OK) return st;
   if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
@@ -220,6 +251,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
     p->heads_per_group = 1;
     p->head_groups = d->num_kv_heads;
     p->longest_first = 0;
+    p->balanced = 0;
     return PDA_OK;
   }
   // The matrix-core kernel is faster on every measured shape; the v_dot2
@@ -235,7 +267,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
         pda::mfma_waves_per_simd(d->head_dim, kv_kind(d->kv_dtype), p->row_tiles);
     const int lds_waves = (int)std::max<size_t>(1, 65536 / p->wave_lds);
     matrix_plan(d, window, num_splits, num_cus, waves_per_simd,
-                std::min(4 * waves_per_simd, lds_waves), p);
+                std::min(4 * waves_per_simd, lds_waves), allow_balanced, p);
     const int waves = p->heads_per_group * p->key_waves;
     p->row_groups = 1;
     p->rows_per_wave = p->rows;
@@ -256,6 +288,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
   p->heads_per_group = 1;
   p->head_groups = d->num_kv_heads;
   p->longest_first = 0;
+  p->balanced = 0;
   p->splits = num_splits >= 1
                   ? num_splits
                   : auto_splits(d, window, pda::unit_keys(d->head_dim, kv_kind(d->kv_dtype)),
@@ -295,8 +328,37 @@ int64_t partials_bytes(const pda_decode_dims* d, int splits) {
          (int64_t)sizeof(float);
 }
 
-int64_t attention_workspace_bytes(const pda_decode_dims* d, int splits) {
-  return splits == 1 ? 0 : partials_bytes(d, splits);
+// Workspace of the one-call path. Fixed split count: the partials as laid
+// out for pda_paged_decode_partials (none for one split). Balanced splits:
+// records [KV head][G * max_q_len rows][chunk slot] (o, then (m, l) padded
+// to 16 bytes), then the per-token chunk lists.
+struct WsLayout {
+  int64_t ml;    // byte offset of the (m, l) records
+  int64_t meta;  // byte offset of the chunk lists (balanced)
+  int64_t total;
+};
+
+WsLayout fixed_ws_layout(const pda_decode_dims* d, int splits) {
+  WsLayout w{0, 0, 0};
+  if (splits > 1) {
+    w.ml = (int64_t)d->num_tokens * d->num_q_heads * splits * d->head_dim * 4;
+    w.total = partials_bytes(d, splits);
+  }
+  return w;
+}
+
+WsLayout attention_ws_layout(const pda_decode_dims* d, const Plan& p) {
+  WsLayout w{0, 0, 0};
+  if (p.balanced) {
+    const int64_t records =
+        (int64_t)p.head_groups * p.chunks * p.heads_per_group * p.rows;
+    w.ml = records * d->head_dim * 4;
+    w.meta = w.ml + ((records * 8 + 15) & ~(int64_t)15);
+    w.total = w.meta + (int64_t)d->num_tokens * 16;
+  } else if (!p.prefill) {
+    w = fixed_ws_layout(d, p.splits);
+  }
+  return w;
 }
 
 pda_status check_pointers(const void* q, const void* k, const void* v, const int32_t* bt,
@@ -334,7 +396,7 @@ pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArg
     if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
     return PDA_OK;
   }
-  const dim3 grid(p.splits, p.head_groups, d->batch);
+  const dim3 grid(p.balanced ? p.chunks : p.splits, p.head_groups, p.balanced ? 1 : d->batch);
   if (p.matrix) {
     switch (kv_kind(d->kv_dtype)) {
       case pda::kKvF16:
@@ -399,6 +461,9 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.tile_shift = __builtin_ctz((unsigned)(d->page_size / pda::kPageSize));
   a.rows = p.rows;
   a.wave_lds_bytes = (int32_t)p.wave_lds;
+  a.balanced = p.balanced;
+  a.chunks = p.chunks;
+  a.min_chunk = p.min_chunk;
   return a;
 }
 
@@ -413,11 +478,47 @@ pda_status check_q_lens(const int32_t* q_lens, const pda_decode_dims* d) {
   return PDA_OK;
 }
 
+pda_status check_out(const void* out) {
+  if (!out) return fail(PDA_ERR_NULL, "out must be non-NULL");
+  if (!aligned16(out)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
+  return PDA_OK;
+}
+
+pda_status check_workspace(const void* workspace, size_t workspace_bytes, const WsLayout& w) {
+  if (w.total > 0) {
+    if (!workspace || (int64_t)workspace_bytes < w.total)
+      return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed",
+                  workspace_bytes, workspace, (long long)w.total);
+    if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  return PDA_OK;
+}
+
+// Launch plan of the one-call path: automatic splits may be balanced per
+// sequence (matrix kernel); otherwise the automatic count is resolved first
+// and planned as a caller's count.
+pda_status attention_plan(const pda_decode_dims* d, int32_t window, int32_t num_splits,
+                          Plan* p, WsLayout* w, bool check_ws = false,
+                          const void* workspace = nullptr, size_t workspace_bytes = 0) {
+  if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
+    return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
+  *w = WsLayout{0, 0, 0};
+  if (d->batch == 0 || d->num_tokens == 0) return PDA_OK;
+  // A caller's count fixes the workspace without the device: check it first.
+  if (num_splits >= 1 && !routes_to_prefill(d) && check_ws &&
+      check_workspace(workspace, workspace_bytes, fixed_ws_layout(d, num_splits)) != PDA_OK)
+    return PDA_ERR_WORKSPACE;
+  const pda_status st = make_plan(d, window, num_splits, 0, p, /*allow_balanced=*/true);
+  if (st != PDA_OK) return st;
+  *w = attention_ws_layout(d, *p);
+  return check_ws ? check_workspace(workspace, workspace_bytes, *w) : PDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+pda_status pda_attention_decode_stage(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_table, const int32_t* seq_lens,
                                       const int32_t* q_lens, float scale, int32_t window,
                                       int32_t num_splits, void* out, const float* k_scale,
@@ -428,40 +529,71 @@ pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const 
   if (st != PDA_OK) return st;
   if ((st = check_pointers(q, k_cache, v_cache, block_table, seq_lens, k_scale, v_scale, dims)))
     return st;
-  if (!out) return fail(PDA_ERR_NULL, "out must be non-NULL");
-  if (!aligned16(out)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
   if ((st = check_q_lens(q_lens, dims))) return st;
-  if (num_splits < 0 || num_splits > PDA_MAX_SPLITS)
-    return fail(PDA_ERR_SHAPE, "num_splits %d outside 0..%d", num_splits, PDA_MAX_SPLITS);
-  if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
-  int splits = 0;
-  if ((st = resolve_split_count(dims, window, num_splits, 0, &splits))) return st;
-  if (splits > 1) {
-    const int64_t need = attention_workspace_bytes(dims, splits);
-    if (!workspace || (int64_t)workspace_bytes < need)
-      return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %lld needed for %d splits",
-                  workspace_bytes, workspace, (long long)need, splits);
-    if (!aligned16(workspace)) return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
   Plan p;
-  if ((st = make_plan(dims, window, splits, 0, &p))) return st;
+  WsLayout w;
+  if ((st = check_out(out))) return st;
+  if ((st = attention_plan(dims, window, num_splits, &p, &w, true, workspace, workspace_bytes)))
+    return st;
+  if (dims->batch == 0 || dims->num_tokens == 0) return PDA_OK;
   pda::DecodeArgs a = make_args(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
                                 window, k_scale, v_scale, dims, p);
   a.out = static_cast<uint16_t*>(out);
-  if (p.splits == 1) {
-    a.direct = 1;
-    return launch_decode(p, dims, a, stream);
+  a.direct = !p.balanced && p.splits == 1;
+  if (w.total > 0) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(ws + w.ml);
+    a.meta = p.balanced ? reinterpret_cast<int32_t*>(ws + w.meta) : nullptr;
   }
-  a.direct = 0;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = a.part_o + (size_t)dims->num_tokens * dims->num_q_heads * p.splits * dims->head_dim;
-  if ((st = launch_decode(p, dims, a, stream))) return st;
+  return launch_decode(p, dims, a, stream);
+}
+
+pda_status pda_attention_combine_stage(void* out, const pda_decode_dims* dims, int32_t window,
+                                       int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  pda_status st = check_dims(dims);
+  if (st != PDA_OK) return st;
+  Plan p;
+  WsLayout w;
+  if ((st = check_out(out))) return st;
+  if ((st = attention_plan(dims, window, num_splits, &p, &w, true, workspace, workspace_bytes)))
+    return st;
+  if (dims->batch == 0 || dims->num_tokens == 0 || w.total == 0) return PDA_OK;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  pda::CombineArgs c{};
+  c.part_o = reinterpret_cast<const float*>(ws);
+  c.part_ml = reinterpret_cast<const float*>(ws + w.ml);
+  c.out = static_cast<uint16_t*>(out);
+  c.meta = p.balanced ? reinterpret_cast<const int32_t*>(ws + w.meta) : nullptr;
+  c.num_splits = p.splits;
+  c.num_q_heads = dims->num_q_heads;
+  c.group = dims->num_q_heads / dims->num_kv_heads;
+  c.rows = p.rows;
+  c.heads_per_group = p.heads_per_group;
+  c.chunks = p.chunks;
   const int rows = dims->num_tokens * dims->num_q_heads;
+  const int waves = p.balanced ? p.combine_waves : pda::combine_waves(p.splits);
   const hipError_t e = pda::launch_combine(
-      a.part_o, a.part_ml, static_cast<uint16_t*>(out), rows, dims->head_dim, p.splits,
-      pda::combine_dim_parts(rows, dims->head_dim, device_cu_count()), stream);
+      c, rows, dims->head_dim, waves, pda::combine_dim_parts(rows, dims->head_dim, device_cu_count()),
+      stream);
   if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "combine launch: %s", hipGetErrorString(e));
   return PDA_OK;
+}
+
+pda_status pda_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      const int32_t* q_lens, float scale, int32_t window,
+                                      int32_t num_splits, void* out, const float* k_scale,
+                                      const float* v_scale, const pda_decode_dims* dims,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  const pda_status st = pda_attention_decode_stage(
+      q, k_cache, v_cache, block_table, seq_lens, q_lens, scale, window, num_splits, out,
+      k_scale, v_scale, dims, workspace, workspace_bytes, stream);
+  if (st != PDA_OK) return st;
+  return pda_attention_combine_stage(out, dims, window, num_splits, workspace, workspace_bytes,
+                                     stream);
 }
 
 pda_status pda_paged_decode_partials(const void* q, const void* k_cache, const void* v_cache,
@@ -515,8 +647,13 @@ pda_status pda_split_combine(const float* partial_o, const float* partial_ml, vo
   if (num_tokens == 0) return PDA_OK;
   const int64_t rows = (int64_t)num_tokens * num_q_heads;
   if (rows > INT32_MAX) return fail(PDA_ERR_SHAPE, "num_tokens * num_q_heads too large");
+  pda::CombineArgs c{};
+  c.part_o = partial_o;
+  c.part_ml = partial_ml;
+  c.out = static_cast<uint16_t*>(out);
+  c.num_splits = num_splits;
   const hipError_t e = pda::launch_combine(
-      partial_o, partial_ml, static_cast<uint16_t*>(out), (int)rows, head_dim, num_splits,
+      c, (int)rows, head_dim, pda::combine_waves(num_splits),
       pda::combine_dim_parts((int)rows, head_dim, device_cu_count()), stream);
   if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "combine launch: %s", hipGetErrorString(e));
   return PDA_OK;
@@ -538,9 +675,18 @@ int64_t pda_decode_partials_bytes(const pda_decode_dims* dims, int32_t window,
 
 int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
                                    int32_t num_splits) {
-  int splits = 0;
-  const pda_status st = resolve_split_count(dims, window, num_splits, 0, &splits);
-  return st == PDA_OK ? attention_workspace_bytes(dims, splits) : st;
+  pda_status st = check_dims(dims);
+  if (st != PDA_OK) return st;
+  if (num_splits >= 1 && num_splits <= PDA_MAX_SPLITS) {  // no device needed
+    if (!routes_to_prefill(dims)) return fixed_ws_layout(dims, num_splits).total;
+    if (num_splits > 1)
+      return fail(PDA_ERR_UNSUPPORTED, "the prefill kernel runs one split (num_splits 0 or 1)");
+    return 0;
+  }
+  Plan p;
+  WsLayout w;
+  st = attention_plan(dims, window, num_splits, &p, &w);
+  return st == PDA_OK ? w.total : st;
 }
 
 const char* pda_last_error(void) { return pda::host_last_error(); }

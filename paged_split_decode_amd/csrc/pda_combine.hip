@@ -4,8 +4,9 @@
 // scores on every wave and 4 barriers per tile"), sections "Purpose" and
 // "Test Result" (split-K combine).
 //
-// One workgroup per row and slice of D / DP dims, with ceil(S / 16) waves;
-// wave w owns splits 16w .. 16w + 15 and issues all of their o loads at once
+// One workgroup per row and slice of D / DP dims. With a fixed split count S
+// it has ceil(S / 16) waves; wave w owns splits 16w .. 16w + 15 and issues
+// all of their o loads at once
 // (lane = D / (64 DP) contiguous dims of a split row), so the partials cost
 // about one memory round trip whatever S is. With few rows (small batches)
 // the dims are cut into DP slices so that more compute units share the
@@ -13,7 +14,10 @@
 // (split s in lane s % 64, slot s / 64) to get the global max M and the
 // denominator; a split's weight is 2^(m_s - M). Several waves add up through
 // LDS. A split with l = 0 (no visible key) has weight 0 and its o is never
-// used; a row with no live split is written as zeros.
+// used; a row with no live split is written as zeros. With balanced splits
+// (a per-sequence split count read from the decode kernel's chunk lists) the
+// waves are fewer than the longest rows need, and a wave takes batches of 16
+// splits nwaves * 16 apart.
 #include "pda_kernels.h"
 
 namespace pda {
@@ -64,8 +68,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <int D, int DP>
 __global__ void __launch_bounds__(64 * kMaxCombineWaves)
-pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                   uint16_t* __restrict__ out, int S) {
+pda_combine_kernel(const CombineArgs a) {
   constexpr int DW = D / DP;  // dims of this workgroup's slice
   constexpr int DT = DW / 64;
   static_assert(DT >= 1, "a lane holds at least one dim");
@@ -77,18 +80,39 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   const int nwaves = blockDim.x >> 6;
   const size_t row = blockIdx.x;
   const int d0 = DW * blockIdx.y;
-  const float* ml = part_ml + row * S * 2;
 
-  // Every load is issued before any is used, with no branches between them:
-  // indexes past the last split are clamped to it (in bounds) and their
-  // weight is 0. First this wave's o rows (splits s0 .. s0 + 15) ...
-  const int s0 = kSplitsPerWave * wave;
-  const int n = min(kSplitsPerWave, S - s0);  // >= 1: the waves cover S exactly
-  const float* src = part_o + (row * S + s0) * D + d0 + lane * DT;
+  // This row's first partial record (its splits' records are adjacent) and
+  // its split count.
+  size_t rec0;
+  int S = a.num_splits;
+  if (a.meta) {
+    const int Hq = a.num_q_heads;
+    const size_t t = row / Hq;
+    const int h = (int)(row - t * Hq);
+    const int4 mt = *reinterpret_cast<const int4*>(a.meta + 4 * t);
+    S = mt.y;
+    if (S <= 1) return;  // one chunk: the decode kernel wrote this row
+    const int k = h / a.group;
+    rec0 = ((size_t)k * a.rows + mt.z * a.group + (h - k * a.group)) * a.chunks + mt.x;
+  } else {
+    rec0 = row * S;
+  }
+  const float* ml = a.part_ml + 2 * rec0;
+  const float* src = a.part_o + rec0 * D + d0 + lane * DT;
+
+  // Every load of the first batch is issued before any is used, with no
+  // branches between them: indexes past the last split are clamped to it (in
+  // bounds) and their weight is 0. First this wave's o rows (splits s0 ..
+  // s0 + 15; later batches, s0 + 16 nwaves .., only with more splits than
+  // 16 per wave) ...
   fv_t x[kSplitsPerWave];
+  auto load_batch = [&](int s0) {
 #pragma unroll
-  for (int j = 0; j < kSplitsPerWave; ++j)
-    x[j] = *reinterpret_cast<const fv_t*>(src + (size_t)min(j, n - 1) * D);
+    for (int j = 0; j < kSplitsPerWave; ++j)
+      x[j] = *reinterpret_cast<const fv_t*>(src + (size_t)min(s0 + j, S - 1) * D);
+  };
+  const int s_first = kSplitsPerWave * wave;
+  if (s_first < S) load_batch(s_first);
   // ... then every split's (m, l): split lane + 64 k in slot k of the lane.
   f2_t p[kMaxSplitSlots];
 #pragma unroll
@@ -117,17 +141,20 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
   // Weights of splits s0 .. s0 + 15: slot s0 / 64, lanes s0 % 64 + j. A
   // split with weight 0 (no visible key, or past S) is never added: its o may
   // hold anything.
-  const int slot = s0 >> 6;
-  const float wsel = slot == 0 ? wv[0] : slot == 1 ? wv[1] : slot == 2 ? wv[2] : wv[3];
-  const int lane0 = s0 & 63;
   fv_t acc = {};
+  for (int s0 = s_first; s0 < S; s0 += kSplitsPerWave * nwaves) {
+    if (s0 != s_first) load_batch(s0);
+    const int slot = s0 >> 6;
+    const float wsel = slot == 0 ? wv[0] : slot == 1 ? wv[1] : slot == 2 ? wv[2] : wv[3];
+    const int lane0 = s0 & 63;
 #pragma unroll
-  for (int j = 0; j < kSplitsPerWave; ++j) {
-    const float w = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsel), lane0 + j));
-    const fv_t t = acc + w * x[j];
+    for (int j = 0; j < kSplitsPerWave; ++j) {
+      const float w = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsel), lane0 + j));
+      const fv_t t = acc + w * x[j];
 #pragma unroll
-    for (int e = 0; e < DT; ++e) acc[e] = w > 0.0f ? t[e] : acc[e];
+      for (int e = 0; e < DT; ++e) acc[e] = w > 0.0f ? t[e] : acc[e];
+    }
   }
 
   if (nwaves == 1) {
@@ -135,7 +162,7 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
     hv_t y;
 #pragma unroll
     for (int e = 0; e < DT; ++e) y[e] = den > 0.0f ? (_Float16)(acc[e] / den) : (_Float16)0.0f;
-    *reinterpret_cast<hv_t*>(out + row * D + d0 + lane * DT) = y;
+    *reinterpret_cast<hv_t*>(a.out + row * D + d0 + lane * DT) = y;
     return;
   }
   *reinterpret_cast<fv_t*>(red + wave * DW + lane * DT) = acc;
@@ -144,7 +171,7 @@ pda_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ p
     float o = 0.0f;
     for (int w = 0; w < nwaves; ++w) o += red[w * DW + d];
     const _Float16 y = den > 0.0f ? (_Float16)(o / den) : (_Float16)0.0f;
-    out[row * D + d0 + d] = __builtin_bit_cast(uint16_t, y);
+    a.out[row * D + d0 + d] = __builtin_bit_cast(uint16_t, y);
   }
 }
 
@@ -154,17 +181,16 @@ int combine_dim_parts(int rows, int head_dim, int num_cus) {
   return dp;
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_ml, uint16_t* out,
-                          int rows, int head_dim, int num_splits, int dim_parts,
-                          hipStream_t stream) {
-  if (num_splits < 1 || num_splits > 64 * kMaxSplitSlots) return hipErrorInvalidValue;
-  const int waves = (num_splits + kSplitsPerWave - 1) / kSplitsPerWave;
+hipError_t launch_combine(const CombineArgs& args, int rows, int head_dim, int waves,
+                          int dim_parts, hipStream_t stream) {
+  if (waves < 1 || waves > kMaxCombineWaves) return hipErrorInvalidValue;
+  if (!args.meta && (args.num_splits < 1 || args.num_splits > 64 * kMaxSplitSlots))
+    return hipErrorInvalidValue;
   const dim3 grid(rows, dim_parts), block(64 * waves);
   const size_t lds = waves > 1 ? (size_t)waves * (head_dim / dim_parts) * sizeof(float) : 0;
 #define PDA_CCASE(DD, PP)                                                                  \
   if (head_dim == DD && dim_parts == PP) {                                                 \
-    hipLaunchKernelGGL((pda_combine_kernel<DD, PP>), grid, block, lds, stream, part_o,     \
-                       part_ml, out, num_splits);                                          \
+    hipLaunchKernelGGL((pda_combine_kernel<DD, PP>), grid, block, lds, stream, args);      \
     return hipGetLastError();                                                              \
   }
   PDA_CCASE(128, 1)

@@ -68,6 +68,160 @@ constexpr int mfma_ring_depth() {
 #endif
 }
 
+// 16-key tiles sequence b must read: those holding a key that one of its
+// new tokens sees (from the first token's window start to the last key).
+__device__ __forceinline__ int visible_tile_count(int L, int Qb, int window) {
+  const int klo = window > 0 ? max(0, L - Qb + 1 - window) : 0;
+  return max(0, (L + kPageSize - 1) / kPageSize - klo / kPageSize);
+}
+
+// Wave-wide integer sum / max through DPP within rows of 16 lanes and
+// permlane swaps across rows (no LDS round trips); every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_i<0x141>(v);  // row_half_mirror
+  v += dpp_i<0x140>(v);  // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = (int)a[0] + (int)a[1];
+  auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (int)c[0] + (int)c[1];
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((int)c[0], (int)c[1]);
+}
+// Inclusive prefix sum over the wave's lanes: row_shr steps of 1, 2, 4, 8
+// within each row of 16 (lanes shifted in from before the row read 0), then
+// the totals of the rows before.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += dpp_i<0x111>(v);
+  v += dpp_i<0x112>(v);
+  v += dpp_i<0x114>(v);
+  v += dpp_i<0x118>(v);
+  const int t0 = __builtin_amdgcn_readlane(v, 15);
+  const int t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  const int r = lane >> 4;
+  return v + (r >= 1 ? t0 : 0) + (r >= 2 ? t1 : 0) + (r >= 3 ? t2 : 0);
+}
+
+// Length-balanced chunks (automatic split count). Sequence b, with w_b tiles
+// to read, is cut into n_b = max(1, ceil(w_b / C)) chunks, where C is the
+// smallest chunk size (at least a.min_chunk tiles, and at least
+// ceil(max_b w_b / 256) so that no row gets more than 256 partials) for which
+// the chunks of all sequences fit in the grid's a.chunks slots. Slot x then
+// holds chunk x - P_b of the sequence b with P_b <= x < P_b + n_b, P_b =
+// n_0 + ... + n_{b-1}; slots past the last chunk hold nothing. Every
+// workgroup derives the same C from seq_lens and q_lens (the host uses this
+// mode only with at least two slots per sequence, so some C fits:
+// with C = ceil(W / (slots - B)), W = sum of w_b, the counts add up to at most
+// W / C + B <= slots, and with C >= max w_b they add up to B). A lane holds
+// sequences lane + 64 k, k < NK: NK = 1 for B <= 64 (the total of at most 64
+// counts of < 2^26 tiles fits in 32 bits), NK = 4 up to B = 255 (64-bit
+// total).
+struct BalancedChunk {
+  int b, split, count, first, len, qlen, off;  // off: the sequence's first token
+  bool live;
+};
+
+template <int NK>
+__device__ __forceinline__ BalancedChunk balanced_chunk(const DecodeArgs& a, int lane, int x) {
+  const int B = a.batch;
+  int w[NK], Ls[NK], Qs[NK];
+  int wsum = 0, wmax = 0;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int bb = lane + 64 * k;
+    const bool in = bb < B;
+    Ls[k] = in ? a.seq_lens[bb] : 0;
+    Qs[k] = in ? (a.q_lens ? a.q_lens[bb] : 1) : 0;
+    w[k] = in ? visible_tile_count(Ls[k], Qs[k], a.window) : -1;  // -1: not a sequence
+    wsum += in ? w[k] : 0;
+    wmax = max(wmax, w[k]);
+  }
+  // The reductions are wave-uniform: keep them (and the search below) in
+  // scalar registers.
+  wmax = __builtin_amdgcn_readfirstlane(wave_max_i(wmax));
+  long long wtot;
+  if constexpr (NK == 1) {
+    wtot = (uint32_t)__builtin_amdgcn_readfirstlane(wave_sum_i(wsum));  // < 64 x 2^26 = 2^32
+  } else {
+    // Sum the high and low 16 bits apart (both sums fit) and join them.
+    wtot = ((long long)__builtin_amdgcn_readfirstlane(wave_sum_i(wsum >> 16)) << 16) +
+           __builtin_amdgcn_readfirstlane(wave_sum_i(wsum & 0xFFFF));
+  }
+  const int N = a.chunks;
+  auto count_for = [&](int C, int k) {
+    return w[k] < 0 ? 0 : (w[k] <= C ? 1 : (int)(((uint32_t)w[k] + C - 1) / (uint32_t)C));
+  };
+  auto total_for = [&](int C) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) n += count_for(C, k);
+    return __builtin_amdgcn_readfirstlane(wave_sum_i(n));
+  };
+  // Any C >= max w_b gives every sequence one chunk (B <= N slots), so the
+  // search stays at or below cap; below lo the chunks cannot fit.
+  const int cap = max(max(wmax, a.min_chunk), 1);
+  int lo, hi;
+  if (wtot < 0x7FFFFFFFll) {
+    const uint32_t wt = (uint32_t)wtot;
+    lo = (int)min((uint32_t)cap, (wt + N - 1) / (uint32_t)N);
+    hi = (int)min((uint32_t)cap, (wt + (N - B) - 1) / (uint32_t)(N - B));
+  } else {
+    lo = (int)min((long long)cap, (wtot + N - 1) / N);
+    hi = (int)min((long long)cap, (wtot + (N - B) - 1) / (N - B));
+  }
+  lo = min(cap, max(max(a.min_chunk, 1), max((wmax + 255) / 256, lo)));
+  hi = max(lo, hi);
+  if (lo < hi && total_for(lo) <= N) hi = lo;  // the usual case: uniform and near-uniform batches
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (total_for(mid) <= N) hi = mid; else lo = mid + 1;
+  }
+  const int C = lo;
+  BalancedChunk r{0, 0, 0, 0, 0, 1, 0, false};
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int n = count_for(C, k);
+    const int incl = wave_incl_scan(n, lane) + base;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(w[k] >= 0 && incl > x);
+    if (hit != 0) {
+      const int j = (int)__builtin_ctzll(hit);
+      r.b = 64 * k + j;
+      r.count = __builtin_amdgcn_readlane(n, j);
+      r.first = __builtin_amdgcn_readlane(incl, j) - r.count;
+      r.split = x - r.first;
+      r.len = __builtin_amdgcn_readlane(Ls[k], j);
+      r.qlen = __builtin_amdgcn_readlane(Qs[k], j);
+      r.live = true;
+      break;
+    }
+    base = __builtin_amdgcn_readlane(incl, 63);
+  }
+  // Token offset of sequence b: the q_lens of the sequences before it.
+  r.off = r.b;
+  if (r.live && a.q_lens) {
+    int q = 0;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) q += lane + 64 * k < r.b ? Qs[k] : 0;
+    r.off = __builtin_amdgcn_readfirstlane(wave_sum_i(q));
+  }
+  return r;
+}
+
 template <int D, int KV, int NRT>
 __global__ void __launch_bounds__(256 * mfma_waves_per_simd(D, KV, NRT),
                                   mfma_waves_per_simd(D, KV, NRT))
@@ -90,7 +244,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = lane >> 4;  // lane group: keys 4s..4s+3 of a page in the scores
   const int c = lane & 15;  // key of the page (loads) / query row (scores, output)
-  const int split = blockIdx.x;
+  int split = blockIdx.x;
   const int KW = a.key_waves;   // waves sharing this KV head's key range
   const int hw = wave / KW;     // head slot of this wave in the workgroup
   const int kw = wave - hw * KW;
@@ -99,7 +253,12 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   const int g = head_ok ? g_raw : 0;
   const int G = a.group;
   const int Hq = a.num_q_heads;
-  const int S = a.num_splits;
+  // Token of query row r (rows are token-major, G per token): r / G, as a
+  // float product: for r < 32 and G <= 32 the quotient sits at least 1/64
+  // from the next integer, far beyond the reciprocal's rounding error.
+  const float inv_g = 1.0f / (float)G;
+  auto token_of = [&](int r) { return (int)(((float)r + 0.5f) * inv_g); };
+  int S = a.num_splits;
   const int R = a.rows;  // G * max_q_len
   const size_t wave_lds = a.wave_lds_bytes;
   uint8_t* my_lds = lds_raw + (size_t)wave * wave_lds;
@@ -110,7 +269,24 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   // ones are dispatched first and the short ones fill in behind them.
   int b = blockIdx.z;
   int L;
-  if (a.longest_first) {
+  int Qb;
+  int off = b;
+  bool direct = a.direct;
+  int first_chunk = 0;
+  if (a.balanced) {
+    const BalancedChunk ch = a.batch <= 64 ? balanced_chunk<1>(a, lane, blockIdx.x)
+                                           : balanced_chunk<4>(a, lane, blockIdx.x);
+    if (!ch.live) return;  // a slot past the last chunk (uniform over the workgroup)
+    // All wave-uniform: keep them in scalar registers.
+    b = __builtin_amdgcn_readfirstlane(ch.b);
+    L = __builtin_amdgcn_readfirstlane(ch.len);
+    Qb = __builtin_amdgcn_readfirstlane(ch.qlen);
+    split = __builtin_amdgcn_readfirstlane(ch.split);
+    S = __builtin_amdgcn_readfirstlane(ch.count);
+    first_chunk = __builtin_amdgcn_readfirstlane(ch.first);
+    direct = S == 1;
+    off = __builtin_amdgcn_readfirstlane(ch.off);
+  } else if (a.longest_first) {
     const int B = a.batch;
     const int my_len = lane < B ? a.seq_lens[lane] : -1;
     int rank = 0;
@@ -122,16 +298,28 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
     L = __builtin_amdgcn_readlane(my_len, b);
   } else {
-    L = a.seq_lens[b];
-  }
-  const int Qb = a.q_lens ? a.q_lens[b] : 1;
-  int off = b;
-  if (a.q_lens) {
+    // The token offset (q_lens of the sequences before b) is loaded
+    // together with the length.
     int sum = 0;
-    for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
-    off = wave_sum_int(sum);
+    if (a.q_lens)
+      for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
+    L = a.seq_lens[b];
+    off = a.q_lens ? __builtin_amdgcn_readfirstlane(wave_sum_i(sum)) : b;
+  }
+  if (!a.balanced) Qb = a.q_lens ? a.q_lens[b] : 1;
+  if (a.longest_first) {
+    off = b;  // the token offset with one token per sequence
+    if (a.q_lens) {
+      int sum = 0;
+      for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
+      off = __builtin_amdgcn_readfirstlane(wave_sum_i(sum));
+    }
   }
   const int pos0 = L - Qb;
+  // Balanced splits: the sequence's first workgroup records where the combine
+  // finds each of its tokens' partials.
+  if (a.balanced && split == 0 && blockIdx.y == 0 && wave == 0 && lane < Qb)
+    *reinterpret_cast<int4*>(a.meta + 4 * (size_t)(off + lane)) = int4{first_chunk, S, lane, 0};
 
   // Pages any new token can see, split into `num_splits` chunks, then into one
   // run per wave.
@@ -141,30 +329,24 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   const int per_split = (nu + S - 1) / S;
   const int s_lo = u_lo + min(nu, split * per_split);
   const int ns = min(nu, (split + 1) * per_split) - min(nu, split * per_split);
-  const int per_wave = (ns + KW - 1) / KW;
+  const int per_wave = KW == 1 ? ns : (ns + KW - 1) / KW;
   const int w_lo = s_lo + min(ns, kw * per_wave);
   int w_hi = s_lo + min(ns, (kw + 1) * per_wave);
 
   // Visibility bounds: uniform summary over the real rows (fast-path test),
-  // and this lane's own rows (16 * rt + c) for masked pages.
-  int lo_max = 0, hi_min = 0x7fffffff;
-  bool any_active = false;
-  for (int r = 0; r < R; ++r) {
-    const int i = r / G;
-    const int pos = pos0 + i;
-    if (i < Qb && pos >= 0) {
-      lo_max = max(lo_max, a.window > 0 ? max(0, pos - a.window + 1) : 0);
-      hi_min = min(hi_min, pos);
-      any_active = true;
-    }
-  }
+  // and this lane's own rows (16 * rt + c) for masked pages. Token i sits at
+  // pos0 + i; the first token that sees a key is i_lo = max(0, -pos0), the
+  // last one (position L - 1) has the latest window start.
+  const bool any_active = L >= 1;
+  const int hi_min = max(pos0, 0);
+  const int lo_max = a.window > 0 ? max(0, L - a.window) : 0;
   if (!any_active || !head_ok) w_hi = w_lo;
   const int n = w_hi - w_lo;
   int lo_c[NRT], hi_c[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int row = 16 * rt + c;
-    const int i = row / G;
+    const int i = token_of(row);
     const int pos = pos0 + i;
     const bool active = row < R && i < Qb && pos >= 0;
     lo_c[rt] = active ? (a.window > 0 ? max(0, pos - a.window + 1) : 0) : 0;
@@ -223,7 +405,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int row = 16 * rt + c;
-    const int i = row / G;
+    const int i = token_of(row);
     const bool exists = head_ok && row < R && i < Qb;
     const uint8_t* qrow = a.q + ((size_t)(off + i) * Hq + g * G + (row - i * G)) * (D * 2);
 #pragma unroll
@@ -440,6 +622,17 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     l[rt] = add4(l[rt]);
   }
 
+  // Partial record of (head slot hs, row = i * G + j) for token i of this
+  // sequence: rec_a(hs) + row * rec_b + i * rec_c. Fixed split count: record
+  // ((off + i) * Hq + head * G + j) * S + split. Balanced splits: record
+  // (head * R + row) * chunks + slot, so a row's chunks are adjacent.
+  const size_t rec_b = a.balanced ? (size_t)a.chunks : (size_t)S;
+  const size_t rec_c = a.balanced ? 0 : (size_t)(Hq - G) * S;
+  auto rec_a = [&](int hs) -> size_t {
+    const size_t gg = (size_t)blockIdx.y * a.heads_per_group + hs;
+    return a.balanced ? gg * R * a.chunks + blockIdx.x : ((size_t)off * Hq + gg * G) * S + split;
+  };
+
   // One wave per head: write the result from registers (lane (s, c) holds
   // row 16 rt + c, dims 16 dt + 4 s .. + 3).
   if (KW == 1) {
@@ -448,11 +641,11 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       const int row = 16 * rt + c;
-      const int i = row / G;
+      const int i = token_of(row);
       if (row >= R || i >= Qb) continue;
       const size_t hrow = (size_t)(off + i) * Hq + g * G + (row - i * G);
       const float lsum = l[rt];
-      if (a.direct) {
+      if (direct) {
         uint16_t* dst = a.out + hrow * D + 4 * s;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -463,7 +656,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
           *reinterpret_cast<h4_t*>(dst + 16 * dt) = y;
         }
       } else {
-        const size_t prow = hrow * S + split;
+        const size_t prow = rec_a(hw) + (size_t)row * rec_b + (size_t)i * rec_c;
         float* dst = a.part_o + prow * D + 4 * s;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f4_t*>(dst + 16 * dt) = o[rt][dt] * vs;
@@ -500,7 +693,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     const int row = rem / D;
     const int d = rem - row * D;
     const int gg = blockIdx.y * HPW + hs;
-    const int i = row / G;
+    const int i = token_of(row);
     if (gg >= a.num_kv_heads || i >= Qb) continue;
     const int h = gg * G + (row - i * G);
     const int t = off + i;
@@ -517,11 +710,11 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
       osum += wt * rec[4 + d];
     }
     osum *= a.v_scale ? a.v_scale[gg] : 1.0f;
-    if (a.direct) {
+    if (direct) {
       const _Float16 y = lsum > 0.0f ? (_Float16)(osum / lsum) : (_Float16)0.0f;
       a.out[((size_t)t * Hq + h) * D + d] = __builtin_bit_cast(uint16_t, y);
     } else {
-      const size_t prow = ((size_t)t * Hq + h) * S + split;
+      const size_t prow = rec_a(hs) + (size_t)row * rec_b + (size_t)i * rec_c;
       a.part_o[prow * D + d] = osum;
       if (d == 0) {
         a.part_ml[prow * 2] = lsum > 0.0f ? M : -INFINITY;

@@ -58,6 +58,15 @@ struct DecodeArgs {
   int32_t tile_shift;          // matrix kernel: log2(page_size / 16)
   int32_t rows;                // G * max_q_len (matrix kernel)
   int32_t wave_lds_bytes;      // LDS bytes per wave (matrix kernel)
+  // Length-balanced splits (matrix kernel, automatic split count): grid x
+  // has `chunks` slots per KV-head group, filled by the chunks of every
+  // sequence (see balanced_chunk); partials go to per-chunk records and
+  // `meta` gets, per token, {first chunk slot, chunk count, token index in
+  // its sequence, 0}.
+  int32_t balanced;
+  int32_t chunks;
+  int32_t min_chunk;           // fewest 16-key tiles in a chunk
+  int32_t* meta;               // [T][4]
 };
 
 // Launch the decode kernel for (head_dim, kv_kind, rows_per_wave) with
@@ -140,8 +149,30 @@ const char* host_last_error();
 // units when there are few rows.
 int combine_dim_parts(int rows, int head_dim, int num_cus);
 
-hipError_t launch_combine(const float* part_o, const float* part_ml,
-                          uint16_t* out, int rows, int head_dim, int num_splits,
+// Where the combine finds a row's partials. Fixed split count (meta ==
+// nullptr): row r's split s is record r * num_splits + s. Balanced splits:
+// row (t, h) of KV head k = h / group has meta[t] = {first chunk slot P,
+// chunk count n, token index i, 0}; its split s is record
+// (k * rows + i * group + h % group) * chunks + P + s, and a row with n <= 1
+// was written by the decode kernel itself. Record e holds o at part_o + e * D
+// and (m, l) at part_ml + 2 e.
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  uint16_t* out;
+  const int32_t* meta;
+  int32_t num_splits;
+  int32_t num_q_heads;
+  int32_t group;
+  int32_t rows;
+  int32_t heads_per_group;
+  int32_t chunks;
+};
+
+// Waves per combine workgroup for a fixed split count: one per 16 splits.
+inline int combine_waves(int num_splits) { return (num_splits + 15) / 16; }
+
+hipError_t launch_combine(const CombineArgs& args, int rows, int head_dim, int waves,
                           int dim_parts, hipStream_t stream);
 
 }  // namespace pda
