@@ -98,11 +98,17 @@ def kernel_source_hash(kernel: str = "decode_mfma") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
+def workload_key(workload: str, over: dict) -> str:
+    """Name of a workload with the command line's overrides (batch, window,
+    split count), as profiles/ files are keyed."""
+    tags = {"batch": "b", "window": "w", "num_splits": "s"}
+    return workload + "".join(f"_{tags[k]}{v}" for k, v in sorted(over.items()) if k in tags)
+
+
+def traffic_for(key: str):
     """HBM bytes per decode launch from a committed rocprofv3 counter summary
-    of the current kernel sources (profiles/traffic_<workload>.json), else
-    None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    of the current kernel sources (profiles/traffic_<key>.json), else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -391,7 +397,7 @@ def main(argv=None):
     m = measure(case, args.steps, args.warmup, w.num_splits, device, args.kernel)
     gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
     dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
-    traffic = traffic_for(args.workload)
+    traffic = traffic_for(workload_key(args.workload, over))
     rec = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 5),
