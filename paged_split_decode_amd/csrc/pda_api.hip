@@ -570,8 +570,9 @@ pda_status pda_attention_combine_stage(void* out, const pda_decode_dims* dims, i
   c.num_q_heads = dims->num_q_heads;
   c.group = dims->num_q_heads / dims->num_kv_heads;
   c.rows = p.rows;
-  c.heads_per_group = p.heads_per_group;
   c.chunks = p.chunks;
+  c.per_seq = p.splits;
+  c.max_q_len = dims->max_q_len;
   const int rows = dims->num_tokens * dims->num_q_heads;
   const int waves = p.balanced ? p.combine_waves : pda::combine_waves(p.splits);
   const hipError_t e = pda::launch_combine(

@@ -16,8 +16,10 @@
 // LDS. A split with l = 0 (no visible key) has weight 0 and its o is never
 // used; a row with no live split is written as zeros. With balanced splits
 // (a per-sequence split count read from the decode kernel's chunk lists) the
-// waves are fewer than the longest rows need, and a wave takes batches of 16
-// splits nwaves * 16 apart.
+// waves are those a uniform batch needs, the longer rows of a ragged batch
+// take batches of 16 splits nwaves * 16 apart, and the partials' loads for a
+// uniform batch's layout go out together with the chunk list's load (issued
+// again only when the list differs).
 #include "pda_kernels.h"
 
 namespace pda {
@@ -81,43 +83,57 @@ pda_combine_kernel(const CombineArgs a) {
   const size_t row = blockIdx.x;
   const int d0 = DW * blockIdx.y;
 
-  // This row's first partial record (its splits' records are adjacent) and
-  // its split count.
-  size_t rec0;
-  int S = a.num_splits;
-  if (a.meta) {
-    const int Hq = a.num_q_heads;
-    const size_t t = row / Hq;
-    const int h = (int)(row - t * Hq);
-    const int4 mt = *reinterpret_cast<const int4*>(a.meta + 4 * t);
-    S = mt.y;
-    if (S <= 1) return;  // one chunk: the decode kernel wrote this row
-    const int k = h / a.group;
-    rec0 = ((size_t)k * a.rows + mt.z * a.group + (h - k * a.group)) * a.chunks + mt.x;
-  } else {
-    rec0 = row * S;
-  }
-  const float* ml = a.part_ml + 2 * rec0;
-  const float* src = a.part_o + rec0 * D + d0 + lane * DT;
-
   // Every load of the first batch is issued before any is used, with no
   // branches between them: indexes past the last split are clamped to it (in
   // bounds) and their weight is 0. First this wave's o rows (splits s0 ..
   // s0 + 15; later batches, s0 + 16 nwaves .., only with more splits than
-  // 16 per wave) ...
+  // 16 per wave), then every split's (m, l): split lane + 64 k in slot k of
+  // the lane. A row's splits are adjacent records from rec0 on.
+  size_t rec0;
+  int S = a.num_splits;
+  const float* src;
   fv_t x[kSplitsPerWave];
+  f2_t p[kMaxSplitSlots];
+  const int s_first = kSplitsPerWave * wave;
   auto load_batch = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < kSplitsPerWave; ++j)
       x[j] = *reinterpret_cast<const fv_t*>(src + (size_t)min(s0 + j, S - 1) * D);
   };
-  const int s_first = kSplitsPerWave * wave;
-  if (s_first < S) load_batch(s_first);
-  // ... then every split's (m, l): split lane + 64 k in slot k of the lane.
-  f2_t p[kMaxSplitSlots];
+  auto issue = [&]() {
+    src = a.part_o + rec0 * D + d0 + lane * DT;
+    if (s_first < S) load_batch(s_first);
+    const float* ml = a.part_ml + 2 * rec0;
 #pragma unroll
-  for (int k = 0; k < kMaxSplitSlots; ++k)
-    p[k] = *reinterpret_cast<const f2_t*>(ml + 2 * min(lane + 64 * k, S - 1));
+    for (int k = 0; k < kMaxSplitSlots; ++k)
+      p[k] = *reinterpret_cast<const f2_t*>(ml + 2 * min(lane + 64 * k, S - 1));
+  };
+  if (a.meta) {
+    // Balanced splits: the row's chunk list gives its first chunk slot and
+    // count. The loads for a uniform batch's layout (every sequence
+    // max_q_len tokens and per_seq chunks) go out with the list's load, and
+    // are issued again only if the list says otherwise.
+    const int Hq = a.num_q_heads;
+    const size_t t = row / Hq;
+    const int h = (int)(row - t * Hq);
+    const int k = h / a.group;
+    const int4 mt = *reinterpret_cast<const int4*>(a.meta + 4 * t);
+    const size_t rec_k = (size_t)k * a.rows + (h - k * a.group);
+    const int bg = (int)(t / a.max_q_len);
+    const int ig = (int)t - bg * a.max_q_len;
+    S = a.per_seq;
+    rec0 = (rec_k + (size_t)ig * a.group) * a.chunks + (size_t)bg * a.per_seq;
+    issue();
+    if (mt.x != bg * a.per_seq || mt.y != a.per_seq || mt.z != ig) {
+      S = mt.y;
+      if (S <= 1) return;  // one chunk: the decode kernel wrote this row
+      rec0 = (rec_k + (size_t)mt.z * a.group) * a.chunks + mt.x;
+      issue();
+    }
+  } else {
+    rec0 = row * S;
+    issue();
+  }
 
   float mv[kMaxSplitSlots], lv[kMaxSplitSlots];
   float M = -INFINITY;

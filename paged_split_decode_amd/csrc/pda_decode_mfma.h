@@ -116,7 +116,9 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v + (r >= 1 ? t0 : 0) + (r >= 2 ? t1 : 0) + (r >= 3 ? t2 : 0);
 }
 
-// Length-balanced chunks (automatic split count). Sequence b, with w_b tiles
+// Length-balanced chunks (automatic split count). A uniform batch (every
+// sequence with the same tile count and q_len) takes the fixed split: S =
+// slots / B chunks per sequence. Otherwise sequence b, with w_b tiles
 // to read, is cut into n_b = max(1, ceil(w_b / C)) chunks, where C is the
 // smallest chunk size (at least a.min_chunk tiles, and at least
 // ceil(max_b w_b / 256) so that no row gets more than 256 partials) for which
@@ -136,23 +138,68 @@ struct BalancedChunk {
 };
 
 template <int NK>
-__device__ __forceinline__ BalancedChunk balanced_chunk(const DecodeArgs& a, int lane, int x) {
-  const int B = a.batch;
-  int w[NK], Ls[NK], Qs[NK];
-  int wsum = 0, wmax = 0;
+struct BalancedLens {
+  int L[NK], Q[NK];  // seq_lens / q_lens of sequences lane + 64 k (0 past the batch)
+};
+
+template <int NK>
+__device__ __forceinline__ BalancedLens<NK> balanced_lens(const DecodeArgs& a, int lane) {
+  // Branch-free (every lane reads an in-bounds entry, unused values are
+  // discarded), so that later loads can be waited for apart from these.
+  BalancedLens<NK> r;
+  const int32_t* ql = a.q_lens ? a.q_lens : a.seq_lens;
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     const int bb = lane + 64 * k;
-    const bool in = bb < B;
-    Ls[k] = in ? a.seq_lens[bb] : 0;
-    Qs[k] = in ? (a.q_lens ? a.q_lens[bb] : 1) : 0;
+    const bool in = bb < a.batch;
+    const int bc = in ? bb : 0;
+    const int Lv = a.seq_lens[bc];
+    const int Qv = ql[bc];
+    r.L[k] = in ? Lv : 0;
+    r.Q[k] = in ? (a.q_lens ? Qv : 1) : 0;
+  }
+  return r;
+}
+
+template <int NK>
+__device__ __forceinline__ BalancedChunk balanced_chunk(const DecodeArgs& a, int lane, int x,
+                                                        const BalancedLens<NK>& ln) {
+  const int B = a.batch;
+  int w[NK], Ls[NK], Qs[NK];
+  int wsum = 0, wmax = 0, wmin = 0x7fffffff, qmax = 0, qmin = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const bool in = lane + 64 * k < B;
+    Ls[k] = ln.L[k];
+    Qs[k] = ln.Q[k];
     w[k] = in ? visible_tile_count(Ls[k], Qs[k], a.window) : -1;  // -1: not a sequence
     wsum += in ? w[k] : 0;
     wmax = max(wmax, w[k]);
+    wmin = in ? min(wmin, w[k]) : wmin;
+    qmax = in ? max(qmax, Qs[k]) : qmax;
+    qmin = in ? min(qmin, Qs[k]) : qmin;
   }
   // The reductions are wave-uniform: keep them (and the search below) in
   // scalar registers.
   wmax = __builtin_amdgcn_readfirstlane(wave_max_i(wmax));
+  BalancedChunk r{0, 0, 0, 0, 0, 1, 0, false};
+  // A batch whose sequences all read as many tiles, with as many new tokens:
+  // the fixed split (S = slots / B chunks each, sequence x / S), which
+  // balances it as well and needs no search.
+  if (__builtin_amdgcn_readfirstlane(-wave_max_i(-wmin)) == wmax &&
+      __builtin_amdgcn_readfirstlane(wave_max_i(qmax)) ==
+          __builtin_amdgcn_readfirstlane(-wave_max_i(-qmin))) {
+    const int S = a.num_splits;
+    r.b = x / S;
+    r.split = x - r.b * S;
+    r.count = S;
+    r.first = r.b * S;
+    r.len = __builtin_amdgcn_readfirstlane(Ls[0]);
+    r.qlen = __builtin_amdgcn_readfirstlane(Qs[0]);
+    r.off = r.b * r.qlen;
+    r.live = true;
+    return r;
+  }
   long long wtot;
   if constexpr (NK == 1) {
     wtot = (uint32_t)__builtin_amdgcn_readfirstlane(wave_sum_i(wsum));  // < 64 x 2^26 = 2^32
@@ -191,7 +238,6 @@ __device__ __forceinline__ BalancedChunk balanced_chunk(const DecodeArgs& a, int
     if (total_for(mid) <= N) hi = mid; else lo = mid + 1;
   }
   const int C = lo;
-  BalancedChunk r{0, 0, 0, 0, 0, 1, 0, false};
   int base = 0;
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
@@ -273,9 +319,72 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   int off = b;
   bool direct = a.direct;
   int first_chunk = 0;
+
+  // This wave's run of 16-key tiles for split `sp` of `ns_total` of a
+  // sequence of L_ keys and Q_ new tokens: every tile a new token can see,
+  // cut into ns_total chunks, then into one run per wave of the head.
+  auto run_of = [&](int L_, int Q_, int sp, int ns_total, int& wl, int& nn) {
+    const int klo = a.window > 0 ? max(0, L_ - Q_ + 1 - a.window) : 0;
+    const int u_lo = klo / kPageSize;
+    const int nu = max(0, (L_ + kPageSize - 1) / kPageSize - u_lo);
+    const int per_split = (nu + ns_total - 1) / ns_total;
+    const int s_lo = u_lo + min(nu, sp * per_split);
+    const int ns = min(nu, (sp + 1) * per_split) - min(nu, sp * per_split);
+    const int per_wave = KW == 1 ? ns : (ns + KW - 1) / KW;
+    wl = s_lo + min(ns, kw * per_wave);
+    const int wh = s_lo + min(ns, (kw + 1) * per_wave);
+    nn = (L_ >= 1 && head_ok) ? wh - wl : 0;  // no key visible, or no such head
+  };
+  // Byte offsets of the first 2 NB - 1 tiles of a run (the ring's preload
+  // and its first lookahead), clamped to the run's last tile. A "page" of
+  // this loop is a tile of 16 keys; a pool page of 16 * 2^tile_shift keys
+  // holds 2^tile_shift consecutive tiles. The table entries come from one
+  // vector load (lane k: tile k, clamped into the run, so every lane reads an
+  // entry the sequence uses) instead of 2 NB - 1 dependent scalar loads.
+  typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
+  const size_t page_bytes = a.page_bytes;
+  const int tshift = a.tile_shift;
+  const int tmask = (1 << tshift) - 1;
+  const uint32_t key_stride = a.key_stride;
+  size_t pre[2 * NB - 1];
+  int pre_entry = 0;  // lane k: table entry of tile k of the run
+  int pre_lo = 0, pre_n = 0;
+  bool pre_ok = false;
+  auto fetch_pre = [&](int bb, int wl, int nn) {  // nn = 0: entry 0 of the row, unused
+    pre_lo = wl;
+    pre_n = nn;
+    const int col = nn > 0 ? (wl + min(lane, nn - 1)) >> tshift : 0;
+    pre_entry = a.block_table[(size_t)bb * a.max_pages + col];
+  };
+  auto fill_pre = [&]() {
+#pragma unroll
+    for (int k = 0; k < 2 * NB - 1; ++k) {
+      const int u = pre_lo + min(k, pre_n - 1);
+      pre[k] = (size_t)__builtin_amdgcn_readlane(pre_entry, k) * page_bytes +
+               (size_t)((u & tmask) * kPageSize) * key_stride;
+    }
+  };
+
   if (a.balanced) {
-    const BalancedChunk ch = a.batch <= 64 ? balanced_chunk<1>(a, lane, blockIdx.x)
-                                           : balanced_chunk<4>(a, lane, blockIdx.x);
+    BalancedChunk ch;
+    if (a.batch <= 64) {
+      const BalancedLens<1> ln = balanced_lens<1>(a, lane);
+      // While the lengths for the search are in flight, take the chunk a
+      // uniform batch would give this slot (sequence x / S, split x % S) and
+      // fetch its first table entries; they are used if the search agrees.
+      const int Sg = a.num_splits;
+      const int bg = (int)blockIdx.x / Sg;
+      const int sg = (int)blockIdx.x - bg * Sg;
+      int wlg, ng;
+      const int32_t* ql = a.q_lens ? a.q_lens : a.seq_lens;
+      const int Lg = a.seq_lens[bg], Qg = ql[bg];
+      run_of(Lg, a.q_lens ? Qg : 1, sg, Sg, wlg, ng);
+      fetch_pre(bg, wlg, ng);
+      ch = balanced_chunk<1>(a, lane, blockIdx.x, ln);
+      pre_ok = ng > 0 && ch.b == bg && ch.split == sg && ch.count == Sg;
+    } else {
+      ch = balanced_chunk<4>(a, lane, blockIdx.x, balanced_lens<4>(a, lane));
+    }
     if (!ch.live) return;  // a slot past the last chunk (uniform over the workgroup)
     // All wave-uniform: keep them in scalar registers.
     b = __builtin_amdgcn_readfirstlane(ch.b);
@@ -321,27 +430,16 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   if (a.balanced && split == 0 && blockIdx.y == 0 && wave == 0 && lane < Qb)
     *reinterpret_cast<int4*>(a.meta + 4 * (size_t)(off + lane)) = int4{first_chunk, S, lane, 0};
 
-  // Pages any new token can see, split into `num_splits` chunks, then into one
-  // run per wave.
-  const int klo = a.window > 0 ? max(0, pos0 + 1 - a.window) : 0;
-  const int u_lo = klo / kPageSize;
-  const int nu = max(0, (L + kPageSize - 1) / kPageSize - u_lo);
-  const int per_split = (nu + S - 1) / S;
-  const int s_lo = u_lo + min(nu, split * per_split);
-  const int ns = min(nu, (split + 1) * per_split) - min(nu, split * per_split);
-  const int per_wave = KW == 1 ? ns : (ns + KW - 1) / KW;
-  const int w_lo = s_lo + min(ns, kw * per_wave);
-  int w_hi = s_lo + min(ns, (kw + 1) * per_wave);
+  // This wave's run of tiles.
+  int w_lo, n;
+  run_of(L, Qb, split, S, w_lo, n);
 
   // Visibility bounds: uniform summary over the real rows (fast-path test),
   // and this lane's own rows (16 * rt + c) for masked pages. Token i sits at
   // pos0 + i; the first token that sees a key is i_lo = max(0, -pos0), the
   // last one (position L - 1) has the latest window start.
-  const bool any_active = L >= 1;
   const int hi_min = max(pos0, 0);
   const int lo_max = a.window > 0 ? max(0, L - a.window) : 0;
-  if (!any_active || !head_ok) w_hi = w_lo;
-  const int n = w_hi - w_lo;
   int lo_c[NRT], hi_c[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
@@ -353,23 +451,18 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     hi_c[rt] = active ? pos : -1;
   }
 
-  // Addresses. A "page" of this loop is a tile of 16 keys; a pool page of
-  // 16 * 2^tile_shift keys holds 2^tile_shift consecutive tiles. Within a
-  // page, slot j of head g starts at j * key_stride + g * head_stride (NHD:
-  // key_stride = Hkv * row, head_stride = row; HND: key_stride = row,
-  // head_stride = P * row).
-  const uint32_t key_stride = a.key_stride;
+  // Addresses. Within a page, slot j of head g starts at j * key_stride + g
+  // * head_stride (NHD: key_stride = Hkv * row, head_stride = row; HND:
+  // key_stride = row, head_stride = P * row).
   const uint32_t head_off = (uint32_t)g * a.head_stride;
-  const size_t page_bytes = a.page_bytes;
-  const int tshift = a.tile_shift;
-  const int tmask = (1 << tshift) - 1;
   const uint32_t koff = (uint32_t)c * key_stride + head_off + 16u * s;
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     voff[i] = (uint32_t)(s + 4 * i) * key_stride + head_off + lane_piece_offset<D, KV>(c);
-  typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
   const bt_ptr_t bt = (bt_ptr_t)(a.block_table + (size_t)b * a.max_pages);
+  if (!pre_ok && n > 0) fetch_pre(b, w_lo, n);
+  if (n > 0) fill_pre();
   // Byte offset of the k-th tile of this wave's run (clamped to the last).
   auto pid_of = [&](int k) -> size_t {
     const int u = w_lo + min(k, n - 1);
@@ -393,7 +486,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   uint32_t kb[NB][NKL][4], vb[NB][4][VR];
   if (n > 0) {
 #pragma unroll
-    for (int st = 0; st < NB - 1; ++st) load_page(kb[st], vb[st], pid_of(st));
+    for (int st = 0; st < NB - 1; ++st) load_page(kb[st], vb[st], pre[st]);
   }
 
   // Q^T as the B operand: lane (s, c) holds row 16 rt + c, dims of step t in
@@ -593,7 +686,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
   if (n > 0) {
     size_t pid_s[NB];
 #pragma unroll
-    for (int st = 0; st < NB; ++st) pid_s[st] = pid_of(NB - 1 + st);
+    for (int st = 0; st < NB; ++st) pid_s[st] = pre[NB - 1 + st];
     const int n_main = n - n % NB;
     for (int it = 0; it < n_main; it += NB) {
 #pragma unroll

@@ -165,8 +165,9 @@ struct CombineArgs {
   int32_t num_q_heads;
   int32_t group;
   int32_t rows;
-  int32_t heads_per_group;
   int32_t chunks;
+  int32_t per_seq;    // balanced: chunk slots per sequence (chunks / B)
+  int32_t max_q_len;  // balanced: tokens per sequence of a uniform batch
 };
 
 // Waves per combine workgroup for a fixed split count: one per 16 splits.
