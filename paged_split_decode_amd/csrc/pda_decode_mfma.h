@@ -50,7 +50,11 @@ struct MGeom {
   static constexpr int kVDims = D / 16;                 // V dims per lane per key row
   static constexpr int kVRaw = kVDims * kElemBytes / 4; // raw V dwords per lane per key
   static constexpr int kDTiles = D / 16;                // PV output tiles of 16 dims
-  static constexpr int kLdsRow = D + 8;                 // LDS V row stride in halves
+  // LDS V row stride in halves: 16 halves of pad shift each row by 8 banks,
+  // so the 8 rows x 32 bytes of one pass of a transposing read fall on
+  // disjoint banks (an 8-half pad gave 2-way conflicts: a quarter of the
+  // kernel's LDS cycles at fp16).
+  static constexpr int kLdsRow = D + 16;
   static constexpr int kRowBytes = D * kElemBytes;
 };
 

@@ -103,10 +103,10 @@ constexpr int mfma_waves_per_simd(int head_dim, int kv_kind, int row_tiles) {
 }
 
 // LDS bytes one wave of the matrix kernel needs: its fp16 V tile (16 rows of
-// D + 8 halves) during the loop, then its merge records (per row: m, l, two
+// D + 16 halves) during the loop, then its merge records (per row: m, l, two
 // pad floats, o[D]); the two uses alias. Rounded up to 256 bytes.
 inline size_t mfma_wave_lds_bytes(int head_dim, int rows) {
-  const size_t tile = (size_t)16 * (head_dim + 8) * 2;
+  const size_t tile = (size_t)16 * (head_dim + 16) * 2;
   const size_t merge = (size_t)rows * (head_dim + 4) * 4;
   const size_t bytes = tile > merge ? tile : merge;
   return (bytes + 255) & ~(size_t)255;
