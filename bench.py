@@ -182,6 +182,14 @@ class Runner:
 
 
 
+SETTLE_MS = 20.0  # GPU time of untimed steps between the hold and a timed loop
+
+
+def settle_steps(ms_per_step: float) -> int:
+    """Untimed steps worth about SETTLE_MS of GPU time (5 to 400)."""
+    return int(min(400, max(5, math.ceil(SETTLE_MS / max(ms_per_step, 1e-3)))))
+
+
 def _hold_gpu():
     """Keep the GPU busy for a few ms so that the timed launches that follow
     are all queued before the first one runs (they then run back to back,
@@ -203,22 +211,37 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     pool = case.k_cache.numel() * case.k_cache.element_size() * 2
     replicas = max(1, min(16, math.ceil((1 << 30) / max(pool, 1))))
     r = Runner(case, device, replicas, num_splits, kernel)
-    # Every replica is read at least once before timing (first touches of
-    # freshly allocated memory are not part of a step).
-    for i in range(max(warmup, replicas)):
-        r.step(i)
-    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-
-    # Whole steps, queued ahead of the device.
-    _hold_gpu()
+    # Every replica is read at least once before timing (first touches of
+    # freshly allocated memory are not part of a step); the warmup also
+    # gives an estimate of the step time.
+    n_warm = max(warmup, replicas)
     t0.record()
-    for i in range(steps):
+    for i in range(n_warm):
         r.step(i)
     t1.record()
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    settle = settle_steps(t0.elapsed_time(t1) / n_warm)
+
+    def queued(fn):
+        """`steps` calls queued back to back behind the hold, after `settle`
+        untimed ones: the clocks drop while the GPU runs the hold's single
+        wave and take tens of milliseconds of load to come back (the
+        compute-bound prefill measured 10-15% slow without this; the decode
+        did not change)."""
+        _hold_gpu()
+        for i in range(settle):
+            fn(i)
+        t0.record()
+        for i in range(steps):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    # Whole steps, queued ahead of the device.
+    ms_step = queued(r.step)
 
     # The same, paced by the host (no queue-ahead).
     t0.record()
@@ -230,15 +253,9 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
 
     # The decode kernel alone: `steps` launches queued back to back on the
     # launch stream, bracketed by two events.
-    _hold_gpu()
-    t0.record()
-    for i in range(steps):
-        r.decode(i)
-    t1.record()
-    torch.cuda.synchronize()
-    decode_ms = t0.elapsed_time(t1) / steps
+    decode_ms = queued(r.decode)
     return dict(ms_per_step=ms_step, ms_eager=ms_eager, decode_ms=decode_ms, bytes=nbytes,
-                splits=r.S if r.S >= 1 else "auto", replicas=replicas)
+                splits=r.S if r.S >= 1 else "auto", replicas=replicas, settle=settle)
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -326,12 +343,18 @@ def measure_writer(T, Hkv, D, kv, steps, device):
         k, v, kc, vc = sets[i % reps]
         pda.write_kv_cache(k, v, c.slot_mapping, kc, vc, c.k_scale, c.v_scale, kv_dtype=kv)
 
-    for i in range(3):
-        run(i)
-    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    n_warm = max(3, reps)
+    t0.record()
+    for i in range(n_warm):
+        run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    settle = settle_steps(t0.elapsed_time(t1) / n_warm)
     _hold_gpu()
+    for i in range(settle):
+        run(i)
     t0.record()
     for i in range(steps):
         run(i)
@@ -443,6 +466,7 @@ def main(argv=None):
                    "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "algorithmic_bytes": m["bytes"], "input_replicas": m["replicas"],
+                   "settle_steps": m["settle"],
                    "kernel": args.kernel,
                    "accumulate": "fp32"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
