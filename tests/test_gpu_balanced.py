@@ -198,3 +198,17 @@ def test_balanced_ragged_near_page_edges(seed):
     c = make_case(ragged(97 + seed, lens, q_len=int(r.choice([1, 2])), num_q_heads=4,
                          num_kv_heads=1), device=DEV)
     check(run(c), oracle.paged_decode_attention(**c.host()), "f16", repr(lens))
+
+
+@pytest.mark.parametrize("kernel,splits,Q", [("matrix", 5, 2), ("matrix", 1, 1), ("vector", 0, 1),
+                                             ("vector", 3, 2), ("auto", 0, 40)])
+def test_stages_equal_one_call_every_path(kernel, splits, Q):
+    """The two stage calls reproduce the one-call path bit for bit on the
+    fixed-count path, one split (no combine), the vector kernel and the
+    prefill kernel (40 new tokens: one split, nothing to combine)."""
+    c = make_case(ragged(101, (300, 0, 77, 1000), q_len=Q, num_q_heads=8, num_kv_heads=2),
+                  device=DEV)
+    a = run(c, num_splits=splits, kernel=kernel)
+    b = run(c, num_splits=splits, kernel=kernel, stage="stages")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check(a, oracle.paged_decode_attention(**c.host()), "f16", f"{kernel} S={splits} Q={Q}")
