@@ -119,7 +119,7 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
 
 // Long-query (prefill) kernel: 32 (token, head) rows per wave; K/V staged
 // through LDS prefill_tiles(D) 16-key tiles at a time, in two buffers of fp16
-// rows (K: D + 8 halves, V: D + 16). A workgroup has 4 waves, or 8 at D=128
+// rows (K: D + 8 halves, V: D + 32). A workgroup has 4 waves, or 8 at D=128
 // when the keys before the new tokens are long (at least 3 times as many as
 // the new tokens, from the table's capacity): there each thread stages half
 // as much of a step, so two steps of loads fit in flight, and a staged key
@@ -130,7 +130,7 @@ inline int prefill_waves(int head_dim, int max_q_len, int64_t key_capacity) {
 }
 constexpr int prefill_tiles(int) { return 4; }  // 64 keys per LDS step (two halves of 32)
 inline size_t prefill_lds_bytes(int head_dim) {
-  return (size_t)2 * prefill_tiles(head_dim) * 16 * ((head_dim + 8) + (head_dim + 16)) * 2;
+  return (size_t)2 * prefill_tiles(head_dim) * 16 * ((head_dim + 8) + (head_dim + 32)) * 2;
 }
 hipError_t launch_prefill_f16(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);

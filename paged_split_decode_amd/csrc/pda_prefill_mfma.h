@@ -44,10 +44,11 @@ template <int D, int KV, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, D == 128 ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
   // LDS row strides (halves): K rows D + 8 (4 dwords mod 64: the 16 rows of a
-  // 128-bit fragment read pass hit disjoint banks), V rows D + 16 (8 dwords
-  // mod 64: the 4 rows of a transposing read hit disjoint banks).
+  // 128-bit fragment read pass hit disjoint banks), V rows D + 32 (16 dwords
+  // mod 64: a 32-lane pass of the transposing reads covers 4 rows of 64
+  // bytes, on disjoint banks; with D + 16 they overlapped 2-way).
   constexpr int LRK = D + 8;
-  constexpr int LRV = D + 16;
+  constexpr int LRV = D + 32;
   constexpr int TILEK = 16 * LRK;  // halves of one 16-key K tile
   constexpr int TILEV = 16 * LRV;
   constexpr int KT = prefill_tiles(D);
@@ -386,15 +387,20 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       // still gets scores, from finite LDS data, when the other half is
       // needed; its softmax and P.V are skipped.)
       const bool a0 = active(key0), a1 = active(key0 + 32);
-      f16v_t st0 = {}, st1 = {};
+      // (The score registers live only inside the branches that use them: a
+      // value merged from a path that skips them would be zero-filled every
+      // step.)
       if constexpr (D == 128) {
-        if (a0 || a1) scores2(kb, kb + 2 * TILEK, st0, st1);
+        if (a0 || a1) {
+          f16v_t st0, st1;
+          scores2(kb, kb + 2 * TILEK, st0, st1);
+          if (a0) softmax_pv(st0, vb, key0);
+          if (a1) softmax_pv(st1, vb + 2 * TILEV, key0 + 32);
+        }
       } else {
-        if (a0) st0 = scores(kb);
-        if (a1) st1 = scores(kb + 2 * TILEK);
+        if (a0) softmax_pv(scores(kb), vb, key0);
+        if (a1) softmax_pv(scores(kb + 2 * TILEK), vb + 2 * TILEV, key0 + 32);
       }
-      if (a0) softmax_pv(st0, vb, key0);
-      if (a1) softmax_pv(st1, vb + 2 * TILEV, key0 + 32);
       if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1, set_c);
       if (step + 1 + NREG < n_steps) stage_load(step + 1 + NREG, set_c);
       __syncthreads();
