@@ -550,6 +550,13 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
           for (int e = 0; e < VR; ++e) vr[i][e] = 0u;
         }
     }
+    // With 1-byte codes at D=256 a lane's 16 B of codes are the 16 dims of
+    // output tile c, widened to 32 B and written in two 16-byte halves. A
+    // 16-byte write is served 8 lanes (128 bytes) at a time, and in row order
+    // lanes c and c + 4 of those 8 would share banks; tiles with c & 4 keep
+    // their two 8-dim halves swapped, so each write's 8 lanes fall on distinct
+    // banks. The transposing reads of those tiles undo the swap.
+    constexpr bool kSwap = KV != kKvF16 && D == 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       h2_t vh[D / 32];
@@ -560,7 +567,7 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(uint32_t, vh[4 * e8 + e]);
-        const int d0 = dim_of<D, KV>(c, 8 * e8);
+        const int d0 = kSwap ? 16 * c + 8 * (e8 ^ ((c >> 2) & 1)) : dim_of<D, KV>(c, 8 * e8);
         *reinterpret_cast<u32x4*>(row + d0) = w;
       }
     }
@@ -569,14 +576,16 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     // from the row-major tile with one transposing read per 16 dims: within
     // each 16-lane group, ds_read_b64_tr_b16 hands lane i element i % 4 of the
     // 8-byte rows addressed by lanes i/4 + 4k, so lane (s, c) points at row
-    // 4s + c/4, dims 16 dt + 4 (c % 4) .. + 3. Where registers allow, all
+    // 4s + c/4, dims 16 dt + 4 (c % 4) .. + 3 (in a swapped tile, 8 halves
+    // further or back). Where registers allow, all
     // reads are issued here, so their latency hides behind the scores and the
     // softmax; the scheduling barrier keeps the compiler from sinking them
     // next to their uses (which serializes one LDS round trip per read).
     typedef short s4_t __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s4_t lds_s4_t;
     auto read_va = [&](int dt) -> h4_t {
-      _Float16* src = vt + (4 * s + (c >> 2)) * LR + 16 * dt + 4 * (c & 3);
+      const int col = (4 * (c & 3)) ^ (kSwap && (dt & 4) ? 8 : 0);
+      _Float16* src = vt + (4 * s + (c >> 2)) * LR + 16 * dt + col;
       return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                           (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src));
     };
