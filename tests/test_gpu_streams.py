@@ -1,6 +1,7 @@
-"""Stream semantics of the C ABI: every launch goes on the caller's stream,
-and the library keeps no device state between calls (two calls in flight at
-once on two streams, each with its own workspace, do not interfere).
+"""Stream semantics of the C ABI: every launch (attention and cache writer)
+goes on the caller's stream, and the library keeps no device state between
+calls (two calls in flight at once on two streams, each with its own
+workspace, do not interfere).
 
 A call is queued behind a bounded GPU sleep and an asynchronous copy of its
 queries on the same side stream: it gives the oracle's answer only if its
@@ -88,3 +89,28 @@ def test_two_streams_in_flight():
     torch.cuda.synchronize()
     check(out_a, a, "stream 1")
     check(out_b, b, "stream 2")
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+def test_writer_runs_on_the_callers_stream(kv):
+    """The cache writer behind a sleep and a copy of its key rows on a side
+    stream: the cache bytes equal the writer oracle's."""
+    from synth import make_write_case
+    c = make_write_case(300, 4, 128, 16, num_pages=40, kv_dtype=kv, seed=11, device=DEV)
+    h = c.host()
+    key_src = c.key.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        key = torch.zeros_like(key_src)
+        torch.cuda._sleep(SLEEP_CYCLES)
+        key.copy_(key_src, non_blocking=True)
+        pda.write_kv_cache(key, c.value, c.slot_mapping, c.k_cache, c.v_cache,
+                           k_scale=c.k_scale, v_scale=c.v_scale, kv_dtype=c.kv_dtype,
+                           kv_layout=c.kv_layout)
+    s.synchronize()
+    want_k, want_v = oracle.write_kv_cache(h["key"], h["value"], h["slot_mapping"], h["k_cache"],
+                                           h["v_cache"], h["kv_dtype"], h["k_scale"],
+                                           h["v_scale"], h["kv_layout"])
+    assert c.k_cache.cpu().numpy().tobytes() == want_k.tobytes(), "K cache bytes differ"
+    assert c.v_cache.cpu().numpy().tobytes() == want_v.tobytes(), "V cache bytes differ"
