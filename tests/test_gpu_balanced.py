@@ -212,3 +212,15 @@ def test_stages_equal_one_call_every_path(kernel, splits, Q):
     b = run(c, num_splits=splits, kernel=kernel, stage="stages")
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     check(a, oracle.paged_decode_attention(**c.host()), "f16", f"{kernel} S={splits} Q={Q}")
+
+
+@pytest.mark.parametrize("L,W,S,Q", [(1 << 18, 0, 0, 1), (1 << 18, 0, 256, 1), (1 << 18, 0, 0, 3),
+                                     (1 << 20, 70000, 0, 3)])
+def test_very_long_sequence(L, W, S, Q):
+    """One sequence of 2^18 keys (8 times the longest benchmark) with
+    automatic splits and with the most splits a call takes, and one of 2^20
+    keys (65536 pages) with a window far inside it, against the oracle."""
+    w = ragged(103, (L,), q_len=Q, window=W, num_q_heads=4, num_kv_heads=1)
+    c = make_case(w, device=DEV)
+    check(run(c, num_splits=S), oracle.paged_decode_attention(**c.host()), "f16",
+          f"L={L} W={W} S={S} Q={Q}")
