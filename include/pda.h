@@ -26,7 +26,9 @@
  * Conventions for every entry point
  *  - All tensors are contiguous, row-major, and live in device memory of the
  *    current HIP device; the caller owns them. The library never allocates,
- *    frees or synchronizes, and keeps no device state.
+ *    frees or synchronizes, issues no memsets, and keeps no device state, so
+ *    a call can be captured in a HIP graph; with automatic splits a captured
+ *    call balances whatever seq_lens / q_lens hold when it is replayed.
  *  - Every launch goes on the caller's `stream` (the pull request passes the
  *    current stream to every launch); calls return after enqueueing.
  *  - Arguments are validated on the host before any HIP call; a failure
@@ -89,7 +91,7 @@ typedef enum pda_kv_layout {
  *  PDA_KERNEL_MATRIX: Q.K^T and P.V on the MFMA units (fp16 operands, fp32
  *    accumulation; P rounded to fp16 for the P.V product).
  *  PDA_KERNEL_PREFILL: the long-query kernel: one workgroup per block of
- *    new tokens of a sequence and KV head (128 query rows), K/V staged once
+ *    new tokens of a sequence and KV head (128 or 256 query rows), K/V staged once
  *    per workgroup through LDS for all its rows, MFMA for both products.
  *    For prefill, chunked prefill and long verification runs; always one
  *    split (num_splits 0 or 1).
