@@ -289,7 +289,7 @@ def cpu_baseline(case, budget_s: float = 12.0):
 
 
 # Long-query (prefill kernel) cells: a fresh prefill and a chunked prefill.
-PREFILL_CELLS = ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512"]
+PREFILL_CELLS = ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512", "prefill_d256_b4_q2048"]
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, AMD published
 
 

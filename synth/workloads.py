@@ -84,13 +84,17 @@ WORKLOADS = {
                                    forced_zero=2, num_splits=8, seed=4),
     # Long query runs on the same paged cache (the prefill kernel): a fresh
     # prefill of 4 x 2048 tokens, and chunked prefill of 512 new tokens on
-    # 8 sequences of 8192 keys, fp16 KV, D=128, 32/8 heads.
+    # 8 sequences of 8192 keys, fp16 KV, D=128, 32/8 heads; and the fresh
+    # prefill at D=256 with 24/4 heads.
     "prefill_d128_b4_q2048": Workload("prefill_d128_b4_q2048", batch=4, num_q_heads=32,
                                       num_kv_heads=8, head_dim=128, q_len=2048, seq_len=2048,
                                       num_splits=1, seed=7),
     "chunked_d128_b8_l8192_q512": Workload("chunked_d128_b8_l8192_q512", batch=8,
                                            num_q_heads=32, num_kv_heads=8, head_dim=128,
                                            q_len=512, seq_len=8192, num_splits=1, seed=8),
+    "prefill_d256_b4_q2048": Workload("prefill_d256_b4_q2048", batch=4, num_q_heads=24,
+                                      num_kv_heads=4, head_dim=256, q_len=2048, seq_len=2048,
+                                      num_splits=1, seed=9),
     # Quantized long context: D=256, 16/4 heads, 64 sequences of 32768 keys,
     # K/V as fp8-e4m3 or int8 codes with per-KV-head fp32 scales, 8 splits.
     "quant_fp8_d256_b64_l32768": Workload("quant_fp8_d256_b64_l32768",

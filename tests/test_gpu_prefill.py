@@ -119,7 +119,8 @@ def sampled_tokens(c, n_per_seq, seed):
     return worst
 
 
-@pytest.mark.parametrize("name", ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512"])
+@pytest.mark.parametrize("name", ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512",
+                                  "prefill_d256_b4_q2048"])
 def test_prefill_workloads_sampled(name):
     c = make_case(WORKLOADS[name], device=DEV)
     sampled_tokens(c, 12, seed=len(name))
