@@ -243,6 +243,24 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     # Whole steps, queued ahead of the device.
     ms_step = queued(r.step)
 
+    # The distribution over calls: the same queued steps with an event pair
+    # around each call (the events add a little between calls, so the mean
+    # above stays the figure of record).
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    _hold_gpu()
+    for i in range(settle):
+        r.step(i)
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        r.step(i)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    pick = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]  # noqa: E731
+    per_call = {"p10": round(pick(0.1), 2), "median": round(pick(0.5), 2),
+                "p90": round(pick(0.9), 2), "calls": len(per)}
+
     # The same, paced by the host (no queue-ahead).
     t0.record()
     for i in range(steps):
@@ -255,7 +273,8 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
     # launch stream, bracketed by two events.
     decode_ms = queued(r.decode)
     return dict(ms_per_step=ms_step, ms_eager=ms_eager, decode_ms=decode_ms, bytes=nbytes,
-                splits=r.S if r.S >= 1 else "auto", replicas=replicas, settle=settle)
+                splits=r.S if r.S >= 1 else "auto", replicas=replicas, settle=settle,
+                per_call_us=per_call)
 
 
 def cpu_baseline(case, budget_s: float = 12.0):
@@ -301,7 +320,7 @@ def prefill_record(name, case, m):
     tf = flops / (us * 1e-6) / 1e12
     return {"workload": name, "op": "prefill", "batch": case.workload.batch,
             "q_len": case.workload.q_len, "seq_len": case.workload.seq_len,
-            "us_per_call": round(us, 2), "TFLOP_s": round(tf, 1),
+            "us_per_call": round(us, 2), "per_call_us": m["per_call_us"], "TFLOP_s": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)},
@@ -376,7 +395,7 @@ def cell_record(name, w, m):
             "identity_table": w.identity_table, "splits": m["splits"],
             "us_per_call": round(us, 2),
             "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
+            "eager_us_per_call": round(m["ms_eager"] * 1e3, 2), "per_call_us": m["per_call_us"],
             "decode_us": round(m["decode_ms"] * 1e3, 2), "decode_GB_s": round(dec_gbs, 1),
             "algorithmic_bytes": m["bytes"]}
 
@@ -388,7 +407,7 @@ def measure_cell(spec: str, steps: int, kernel: str, device):
 
     kind, i = spec.split(":")
     i = int(i)
-    n = max(10, steps // 4)
+    n = max(50, steps // 2)  # at least 50 calls per cell (percentiles)
     if kind == "decode":
         name, over = CELLS[i]
         wc = WORKLOADS[name].with_(**over)
@@ -464,6 +483,7 @@ def main(argv=None):
                    "page_size": w.page_size, "kv_dtype": w.kv_dtype, "num_splits": m["splits"],
                    "us_per_call": round(m["ms_per_step"] * 1e3, 2),
                    "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
+                   "per_call_us": m["per_call_us"],
                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "algorithmic_bytes": m["bytes"], "input_replicas": m["replicas"],
                    "settle_steps": m["settle"],
