@@ -54,18 +54,30 @@ def check_units(c, out, what):
             assert np.isfinite(got).all() and err <= TOL, f"{what} unit ({b},{g}): {err:.3g}"
 
 
-@pytest.mark.parametrize("kernel,splits,Q", [("matrix", 0, 3), ("matrix", 5, 1), ("vector", 2, 1),
-                                             ("auto", 1, 40)])
-def test_pages_past_4gib(big, kernel, splits, Q):
-    if kernel == "vector" and big.kv_layout == "HND":
-        pytest.skip("the vector kernel reads NHD pages")
-    c = with_q_len(big, Q, seed=Q + splits)
+def call(c, splits, kernel):
     out = torch.full(c.q.shape, float("nan"), dtype=torch.float16, device=DEV)
     pda.paged_decode_attention(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.q_lens,
                                c.scale, c.window, splits, out, max_q_len=c.max_q_len,
                                kernel=kernel, kv_layout=c.kv_layout)
     torch.cuda.synchronize()
-    check_units(c, out, f"{kernel} S={splits} Q={Q} {c.kv_layout}")
+    return out
+
+
+@pytest.mark.parametrize("kernel,splits,Q", [("matrix", 0, 3), ("matrix", 5, 1), ("auto", 1, 40)])
+def test_pages_past_4gib(big, kernel, splits, Q):
+    c = with_q_len(big, Q, seed=Q + splits)
+    check_units(c, call(c, splits, kernel), f"{kernel} S={splits} Q={Q} {c.kv_layout}")
+
+
+def test_vector_kernel_pages_past_4gib(big):
+    """The vector kernel reads NHD pages of 16 keys; an HND cache is refused
+    with an error before any launch."""
+    c = with_q_len(big, 1, seed=2)
+    if c.kv_layout == "HND":
+        with pytest.raises(pda.PdaError):
+            call(c, 2, "vector")
+        return
+    check_units(c, call(c, 2, "vector"), "vector S=2 NHD")
 
 
 def test_writer_past_4gib(big):
