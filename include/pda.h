@@ -91,8 +91,9 @@ typedef enum pda_kv_layout {
  *  PDA_KERNEL_MATRIX: Q.K^T and P.V on the MFMA units (fp16 operands, fp32
  *    accumulation; P rounded to fp16 for the P.V product).
  *  PDA_KERNEL_PREFILL: the long-query kernel: one workgroup per block of
- *    new tokens of a sequence and KV head (128 or 256 query rows), K/V staged once
- *    per workgroup through LDS for all its rows, MFMA for both products.
+ *    new tokens of a sequence and KV head (128 or 256 query rows at D=128,
+ *    128 at D=256), K/V staged once per workgroup through LDS for all its
+ *    rows, MFMA for both products.
  *    For prefill, chunked prefill and long verification runs; always one
  *    split (num_splits 0 or 1).
  *  PDA_KERNEL_AUTO: the matrix kernel while (Hq / Hkv) * max_q_len <=

@@ -125,8 +125,11 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
 // the new tokens, from the table's capacity): there each thread stages half
 // as much of a step, so two steps of loads fit in flight, and a staged key
 // serves twice the rows; with short prefixes (fresh prefill) two independent
-// 4-wave workgroups per CU measured faster.
+// 4-wave workgroups per CU measured faster. At D=256 a workgroup has 8 waves
+// in pairs that share 32 rows and split the output dims (128 rows per
+// workgroup).
 inline int prefill_waves(int head_dim, int max_q_len, int64_t key_capacity) {
+  if (head_dim == 256) return 8;
   return head_dim == 128 && 4 * (int64_t)max_q_len <= key_capacity ? 8 : 4;
 }
 constexpr int prefill_tiles(int) { return 4; }  // 64 keys per LDS step (two halves of 32)

@@ -4,7 +4,8 @@
 //
 // A workgroup takes a block of new tokens of one sequence and all G query
 // heads of one KV head: 32 (token, head) rows per wave, 4 or 8 waves (8 at
-// D=128 when the keys before the new tokens are long: chunked prefill). K and
+// D=128 when the keys before the new tokens are long: chunked prefill); at
+// D=256, 8 waves in pairs that share 32 rows and split the output dims. K and
 // V go through LDS once per workgroup and serve all its waves: each step the
 // threads gather 64 keys (four 16-key tiles) of K and V from the paged cache
 // with 16-byte loads, convert 1-byte codes to fp16 (exactly), and write them
@@ -41,7 +42,7 @@ struct IntC {
 };
 
 template <int D, int KV, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, D == 128 ? 2 : 1)
+__global__ void __launch_bounds__(64 * WAVES, (D == 128 || WAVES == 8) ? 2 : 1)
 pda_prefill_mfma_kernel(const DecodeArgs a) {
   // LDS row strides (halves): K rows D + 8 (4 dwords mod 64: the 16 rows of a
   // 128-bit fragment read pass hit disjoint banks), V rows D + 32 (16 dwords
@@ -63,7 +64,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 #ifdef PDA_PREFILL_NREG8
   constexpr int NREG = WAVES == 8 ? PDA_PREFILL_NREG8 : 1;  // tuning override
 #else
-  constexpr int NREG = WAVES == 8 ? 2 : 1;
+  constexpr int NREG = (WAVES == 8 && D == 128) ? 2 : 1;
 #endif
   static_assert(NREG >= 1 && NREG <= 3, "one to three register sets");
 
@@ -75,6 +76,15 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // At D=256 waves w and w + 4 share the rows 32 (w % 4) .. + 31 and each
+  // accumulates half of the output dims: both compute the rows' scores and
+  // softmax, but o takes 64 registers instead of 128, so two waves fit per
+  // SIMD and hide each other's LDS latency (a single wave waited for every K
+  // fragment read right before its MFMA). Measured 6% faster than one wave
+  // per row block.
+  constexpr bool PAIR = D == 256 && WAVES == 8;
+  const int rg = PAIR ? (wave & 3) : wave;  // row block
+  const int dh = PAIR ? (wave >> 2) : 0;    // output dim half
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int blk = gridDim.x - 1 - blockIdx.x;  // the most keys first
@@ -107,7 +117,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // This wave's rows (16 rt + c of its 32): bounds per lane, and wave-uniform
   // summaries for the skip / unmasked tests.
   int lo_min = 0x7fffffff, lo_max = 0, hi_min = 0x7fffffff, hi_max = -1;
-  for (int r = 32 * wave; r < 32 * wave + 32 && r < a.rows; ++r) {
+  for (int r = 32 * rg; r < 32 * rg + 32 && r < a.rows; ++r) {
     const int i = i0 + r / G;
     const int pos = pos0 + i;
     if (i < Qb && pos >= 0) {
@@ -215,7 +225,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // of this wave's 32 rows; lanes l and l + 32 share the row.
   const int rr = lane & 31;
   const int hh = lane >> 5;
-  const int myr = 32 * wave + rr;  // the workgroup row of this lane
+  const int myr = 32 * rg + rr;  // the workgroup row of this lane
   const int my_i = i0 + myr / G;
   const bool my_row = myr < a.rows && my_i < Qb;
   const int my_pos = pos0 + my_i;
@@ -228,7 +238,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
   qk = fabsf(qk);
   constexpr int NK = D / 16;   // QK k-steps
-  constexpr int NDT = D / 32;  // 32-dim output tiles
+  constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
+  const int dcol = dh * (D / 2);
   h8_t qb[NK];
   {
     const uint8_t* qrow =
@@ -349,7 +360,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const int col = 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3);
+        const int col = dcol + 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3);
         const h4_t lo = tr_read(vb + (16 * ks + 4 * hh + (i16 >> 2)) * LRV + col);
         const h4_t hi = tr_read(vb + (16 * ks + 8 + 4 * hh + (i16 >> 2)) * LRV + col);
         const h8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -416,7 +427,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   if (my_row) {
     const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
     const size_t hrow = (size_t)(off + my_i) * Hq + g * G + (myr - (myr / G) * G);
-    uint16_t* dst = a.out + hrow * D + 4 * hh;
+    uint16_t* dst = a.out + hrow * D + dcol + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -443,6 +454,7 @@ hipError_t launch_prefill_kv(int head_dim, int waves, dim3 grid, size_t lds, hip
   PDA_PCASE(128, 4)
   PDA_PCASE(128, 8)
   PDA_PCASE(256, 4)
+  PDA_PCASE(256, 8)
 #undef PDA_PCASE
   return hipErrorInvalidValue;
 }
