@@ -55,14 +55,16 @@ def test_prefill_both_workgroup_shapes(kv, table_pad):
     assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv, f"prefill pad={table_pad} {kv}")
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("G", [16, 48, 128])
 @pytest.mark.parametrize("table_pad", [1, 300])
-def test_prefill_large_groups(G, table_pad):
+def test_prefill_large_groups(D, G, table_pad):
     # Workgroups whose last waves have some or no rows (G = 48: 240 of 256
-    # rows with 8 waves, 96 of 128 with 4; G = 128: two tokens per workgroup).
-    c = _ragged(G + table_pad, q_lens=[70, 9], ctx=[30, 200], table_pad=table_pad,
-                num_q_heads=2 * G, num_kv_heads=2)
-    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill G={G}")
+    # rows with 8 waves, 96 of 128 with 4 waves or with D=256's wave pairs;
+    # G = 128: two tokens per workgroup, one with the pairs).
+    c = _ragged(G + table_pad + D, q_lens=[70, 9], ctx=[30, 200], table_pad=table_pad,
+                num_q_heads=2 * G, num_kv_heads=2, head_dim=D)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill D={D} G={G}")
 
 
 @pytest.mark.parametrize("window", [1, 64, 300])
