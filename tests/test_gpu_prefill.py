@@ -67,12 +67,14 @@ def test_prefill_large_groups(D, G, table_pad):
     assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill D={D} G={G}")
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("window", [1, 64, 300])
 @pytest.mark.parametrize("layout,P", [("NHD", 16), ("HND", 64)])
-def test_prefill_window_layouts(window, layout, P):
-    c = _ragged(window + P, q_lens=[200, 50], ctx=[500, 7], window=window, layout=layout,
-                page_size=P, num_q_heads=12, num_kv_heads=3)
-    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill W={window} {layout}")
+def test_prefill_window_layouts(D, window, layout, P):
+    c = _ragged(window + P + D, q_lens=[200, 50], ctx=[500, 7], window=window, layout=layout,
+                page_size=P, num_q_heads=12, num_kv_heads=3, head_dim=D)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16",
+                  f"prefill D={D} W={window} {layout}")
 
 
 @pytest.mark.parametrize("kv", ["f16", "int8"])
