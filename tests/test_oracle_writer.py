@@ -115,6 +115,43 @@ def test_writes_land_at_their_flat_slot(kv):
     assert kc0.reshape(num_pages * P, Hkv, D)[untouched].tobytes() == flat_k[untouched].tobytes()
 
 
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
+def test_slots_past_the_pool_leave_both_caches_untouched(kv, layout):
+    """A token whose slot is at or past num_pages * P (the first slot that
+    does not exist, and ones far beyond it) writes nothing: both caches keep
+    their bytes. The tokens of the same call with in-pool slots are written,
+    so the call is not a no-op."""
+    r = np.random.default_rng(5)
+    num_pages, P, Hkv, D, T = 5, 4, 2, 8, 9
+    n_slots = num_pages * P
+    key = r.standard_normal((T, Hkv, D)).astype(np.float16)
+    val = r.standard_normal((T, Hkv, D)).astype(np.float16)
+    slots = np.array([n_slots, n_slots + 1, 3, n_slots + P, 2 * n_slots, 17, 1 << 30,
+                      n_slots + 7, 0], np.int64)
+    ks = vs = None
+    if kv != "f16":
+        ks, vs = np.full(Hkv, 0.02, np.float32), np.full(Hkv, 0.03, np.float32)
+    kc0, vc0 = _pool(num_pages, P, Hkv, D, kv), _pool(num_pages, P, Hkv, D, kv)
+    if layout == "HND":
+        kc0, vc0 = np.ascontiguousarray(kc0.swapaxes(1, 2)), np.ascontiguousarray(vc0.swapaxes(1, 2))
+    # only the out-of-pool tokens: nothing may change
+    out = slots >= n_slots
+    kc, vc = oracle.write_kv_cache(key[out], val[out], slots[out], kc0, vc0, kv, ks, vs,
+                                   kv_layout=layout)
+    assert kc.tobytes() == kc0.tobytes() and vc.tobytes() == vc0.tobytes()
+    # the whole call: exactly the in-pool slots change (each row of D elements)
+    kc, vc = oracle.write_kv_cache(key, val, slots, kc0, vc0, kv, ks, vs, kv_layout=layout)
+    to_flat = (lambda c: c.swapaxes(1, 2).reshape(n_slots, Hkv, D)) if layout == "HND" else (
+        lambda c: c.reshape(n_slots, Hkv, D))
+    changed = {i for i in range(n_slots)
+               if to_flat(kc)[i].tobytes() != to_flat(kc0)[i].tobytes()}
+    assert changed == {int(x) for x in slots if x < n_slots}
+    changed_v = {i for i in range(n_slots)
+                 if to_flat(vc)[i].tobytes() != to_flat(vc0)[i].tobytes()}
+    assert changed_v == changed
+
+
 def _written_case(kv, seed=4):
     """A batch written token by token through the writer into a poisoned
     pool, following a random page table; returns the decode inputs."""
@@ -197,6 +234,19 @@ def _no_saturation(x):
                     _ORIG_E4M3(np.clip(v, -448, 448)))
 
 
+def _slots_wrap_around(key, value, slot_mapping, k_cache, v_cache, kv_dtype="f16",
+                       k_scale=None, v_scale=None, kv_layout="NHD"):
+    n = as_nhd_shape(k_cache, kv_layout)
+    wrapped = np.array([s % n if s >= 0 else s for s in np.asarray(slot_mapping).tolist()])
+    return _ORIG_WRITE(key, value, wrapped, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                       kv_layout=kv_layout)
+
+
+def as_nhd_shape(cache, kv_layout):
+    """Slots of a cache: num_pages * P."""
+    return cache.shape[0] * (cache.shape[2] if kv_layout == "HND" else cache.shape[1])
+
+
 def _int8_truncates(x):
     return np.clip(np.trunc(np.asarray(x, np.float64)), -127, 127).astype(np.int8).view(np.uint8)
 
@@ -208,6 +258,8 @@ _ORIG_E4M3 = kw.encode_e4m3fn
 @pytest.mark.parametrize("name,target,mutant,pin", [
     ("page and slot swapped", "write_kv_cache", _swapped_page_slot,
      lambda: test_writes_land_at_their_flat_slot("f16")),
+    ("slots past the pool wrap around", "write_kv_cache", _slots_wrap_around,
+     lambda: test_slots_past_the_pool_leave_both_caches_untouched("int8", "HND")),
     ("ties away from zero", "encode_e4m3fn", _ties_away, test_e4m3_ties_to_even_at_every_midpoint),
     ("no saturation", "encode_e4m3fn", _no_saturation, test_e4m3_saturates_and_never_emits_nan),
     ("int8 truncation", "encode_int8", _int8_truncates, test_int8_rounding_matches_python_round),
