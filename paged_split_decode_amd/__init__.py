@@ -118,6 +118,22 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A call's own workspace, allocated on the stream its kernels run on.
+    torch's caching allocator ties a freed block to the stream it was
+    allocated on, so after this function's caller drops the tensor the block
+    goes only to later work on that same stream, which runs after these
+    kernels. (Allocated on another stream, it could be handed to new work
+    there while the kernels still use it.)"""
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)),
+                                           device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def _kv_code(k_cache: torch.Tensor, kv_dtype: Optional[str]) -> int:
     if kv_dtype is None:
         kv_dtype = {torch.float16: "f16", torch.float8_e4m3fn: "fp8_e4m3",
@@ -189,7 +205,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, s
                        kv_layout)
     need = workspace_bytes(dims, window, num_splits)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.pda_paged_decode_attention(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
@@ -212,7 +228,7 @@ def attention_stages(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale, 
                        kv_layout)
     need = workspace_bytes(dims, window, num_splits)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stage in ("decode", "both"):
         _check(lib.pda_attention_decode_stage(

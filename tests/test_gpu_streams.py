@@ -114,3 +114,31 @@ def test_writer_runs_on_the_callers_stream(kv):
                                            h["v_scale"], h["kv_layout"])
     assert c.k_cache.cpu().numpy().tobytes() == want_k.tobytes(), "K cache bytes differ"
     assert c.v_cache.cpu().numpy().tobytes() == want_v.tobytes(), "V cache bytes differ"
+
+
+def test_own_workspace_on_a_non_current_stream():
+    """A call that names a stream other than the current one and brings no
+    workspace: the binding's temporary workspace must not go to new work on
+    the current stream while the call's kernels (queued behind a sleep on
+    their own stream) still use it. Allocations right after the call, on the
+    current stream and of the workspace's size, are filled with NaN bytes."""
+    c = case(9, (5000, 3, 900, 64), q_len=2)
+    dims = pda.decode_dims(c.q, c.k_cache, c.block_table, c.seq_lens, c.q_lens, c.max_q_len,
+                           "f16")
+    need = pda.workspace_bytes(dims, c.window, 0)
+    assert need > 0
+    s = torch.cuda.Stream()
+    q_src = c.q.clone()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        q = torch.zeros_like(q_src)
+        out = torch.full(q.shape, float("nan"), dtype=torch.float16, device=DEV)
+        torch.cuda._sleep(SLEEP_CYCLES)
+        q.copy_(q_src, non_blocking=True)
+    assert torch.cuda.current_stream() != s
+    pda.paged_decode_attention(q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, c.q_lens,
+                               c.scale, c.window, 0, out, max_q_len=c.max_q_len, stream=s)
+    junk = [torch.empty(need, dtype=torch.uint8, device=DEV).fill_(0xFF) for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    check(out, c, "own workspace, named stream")
