@@ -129,6 +129,9 @@ pda_status check_dims(const pda_decode_dims* d) {
   return PDA_OK;
 }
 
+// Waves of a vector-kernel workgroup (its launch bound: 512 threads).
+constexpr int kVectorMaxWaves = 8;
+
 // Splits for the v_dot2 kernel: about one workgroup per compute unit.
 int auto_splits(const pda_decode_dims* d, int window, int uk, int key_waves, int num_cus) {
   int64_t keys = (int64_t)d->max_pages_per_seq * d->page_size;
@@ -275,9 +278,18 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
     p->lds = (size_t)waves * p->wave_lds;  // V tiles, then merge records
     return PDA_OK;
   }
-  const int cap = d->head_dim == 256 ? 4 : pda::kMaxRowsPerWave;
+  // Rows per wave: at most the largest compiled count, rounded up to a
+  // compiled one (the extra rows are padding: their tokens do not exist).
+  const int kk = kv_kind(d->kv_dtype);
+  const int cap = pda::vector_max_rw(d->head_dim, kk);
   p->row_groups = (p->rows + cap - 1) / cap;
-  p->rows_per_wave = (p->rows + p->row_groups - 1) / p->row_groups;
+  p->rows_per_wave =
+      pda::vector_rw_for(d->head_dim, kk, (p->rows + p->row_groups - 1) / p->row_groups);
+  if (p->row_groups > kVectorMaxWaves)
+    return fail(PDA_ERR_UNSUPPORTED,
+                "the vector kernel takes at most %d query rows per KV head with this head_dim "
+                "and kv_dtype ((num_q_heads/num_kv_heads)*max_q_len = %d); use the matrix kernel",
+                kVectorMaxWaves * cap, p->rows);
   p->key_waves = std::max(1, (4 + p->row_groups - 1) / p->row_groups);
   if (p->row_groups >= 4) p->key_waves = 1;
   const int waves = p->row_groups * p->key_waves;

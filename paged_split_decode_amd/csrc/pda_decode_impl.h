@@ -530,12 +530,16 @@ __global__ void __launch_bounds__(512) pda_decode_kernel(const DecodeArgs a) {
 template <int D, int KV>
 hipError_t launch_rw(int rw, dim3 grid, int threads, size_t lds, hipStream_t stream,
                      const DecodeArgs& args) {
+  // Only the row counts of vector_rw_compiled are instantiated.
   switch (rw) {
-#define PDA_CASE(R)                                                         \
-  case R:                                                                   \
-    hipLaunchKernelGGL((pda_decode_kernel<D, KV, R>), grid, dim3(threads), \
-                       lds, stream, args);                                  \
-    return hipGetLastError();
+#define PDA_CASE(R)                                                           \
+  case R:                                                                     \
+    if constexpr (vector_rw_compiled(D, KV, R)) {                             \
+      hipLaunchKernelGGL((pda_decode_kernel<D, KV, R>), grid, dim3(threads), \
+                         lds, stream, args);                                  \
+      return hipGetLastError();                                               \
+    }                                                                         \
+    return hipErrorInvalidValue;
     PDA_CASE(1)
     PDA_CASE(2)
     PDA_CASE(3)

@@ -198,8 +198,13 @@ __device__ __forceinline__ BalancedChunk balanced_chunk(const DecodeArgs& a, int
     r.split = x - r.b * S;
     r.count = S;
     r.first = r.b * S;
-    r.len = __builtin_amdgcn_readfirstlane(Ls[0]);
-    r.qlen = __builtin_amdgcn_readfirstlane(Qs[0]);
+    // Equal tile counts do not mean equal lengths: sequence r.b's own length
+    // sits in lane r.b % 64 of Ls[r.b / 64] (r.b < B, since x < S * B).
+    int Lb = Ls[0];
+#pragma unroll
+    for (int k = 1; k < NK; ++k) Lb = (r.b >> 6) == k ? Ls[k] : Lb;
+    r.len = __builtin_amdgcn_readlane(Lb, r.b & 63);
+    r.qlen = __builtin_amdgcn_readfirstlane(Qs[0]);  // one q_len for every sequence
     r.off = r.b * r.qlen;
     r.live = true;
     return r;
@@ -665,8 +670,15 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = visible(rt, i) ? p[i] : 0.0f;
       }
-      l[rt] += (p[0] + p[1]) + (p[2] + p[3]);
       pb[rt] = h4_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      // The denominator adds the same fp16 weights that P.V multiplies V by
+      // (v_dot2 with ones: each fp16 value enters the fp32 sum exactly), so
+      // numerator and denominator weigh every key alike.
+      const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      l[rt] = __builtin_amdgcn_fdot2(h2_t{pb[rt][0], pb[rt][1]}, one2,
+                                     __builtin_amdgcn_fdot2(h2_t{pb[rt][2], pb[rt][3]}, one2,
+                                                            l[rt], false),
+                                     false);
     }
 
     // O^T[dims][rows] += V^T . P^T. Without room to hold every V fragment,

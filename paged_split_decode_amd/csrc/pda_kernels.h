@@ -13,7 +13,30 @@ constexpr int kPageSize = 16;     // keys per tile: the page size of the vector
                                   // kernel; the matrix kernel takes pages of
                                   // 16 * 2^k keys as runs of such tiles
 constexpr int kLanesPerKey = 16;  // lanes sharing one key row in a wave
-constexpr int kMaxRowsPerWave = 8;
+
+// Query rows per wave (RW) of the vector kernel that are compiled: those whose
+// working set stays in registers (no scratch in the compiler's resource
+// report). fp16 at D=128 skips RW = 2, for which the compiler keeps part of
+// the load ring in scratch memory; a call with 2 rows per wave runs RW = 3
+// with one padding row. More rows than the largest RW take several row
+// groups (waves that share keys).
+constexpr bool vector_rw_compiled(int head_dim, int kv_kind, int rw) {
+  if (rw < 1) return false;
+  if (head_dim == 128) return kv_kind == kKvF16 ? (rw <= 5 && rw != 2) : rw <= 6;
+  return kv_kind == kKvI8 ? rw <= 3 : rw <= 4;
+}
+constexpr int vector_max_rw(int head_dim, int kv_kind) {
+  int r = 1;
+  for (int k = 1; k <= 8; ++k)
+    if (vector_rw_compiled(head_dim, kv_kind, k)) r = k;
+  return r;
+}
+// Smallest compiled RW >= rw (rw <= vector_max_rw).
+constexpr int vector_rw_for(int head_dim, int kv_kind, int rw) {
+  for (int k = rw; k <= 8; ++k)
+    if (vector_rw_compiled(head_dim, kv_kind, k)) return k;
+  return -1;
+}
 
 // Keys one pipeline unit of a wave covers: 4 keys per wave instruction
 // (64 lanes / 16 lanes per key) times the key iterations per unit. A unit

@@ -344,12 +344,13 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
         p[v] = (vis >> v) & 1u ? e : 0.0f;
       }
     }
-#pragma unroll
-    for (int v = 0; v < 16; v += 4) lsum += (p[v] + p[v + 1]) + (p[v + 2] + p[v + 3]);
     // O^T[dim][row] += V^T . P^T over two 16-key k-steps. k-step ks takes the
     // lane's keys of j = 2 ks, 2 ks + 1 (slots 8 hh + e: key 16 ks + 4 hh + e,
     // then 16 ks + 8 + 4 hh + e); V^T's A operand uses the same key order:
     // two transposing reads of 4 consecutive key rows at this lane's dim.
+    // The denominator adds the same fp16 weights that P.V multiplies V by
+    // (v_dot2 with ones: each fp16 value enters the fp32 sum exactly).
+    const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       h8_t pb;
@@ -358,6 +359,9 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
         pb[e] = (_Float16)p[8 * ks + e];
         pb[4 + e] = (_Float16)p[8 * ks + 4 + e];
       }
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        lsum = __builtin_amdgcn_fdot2(h2_t{pb[e], pb[e + 1]}, one2, lsum, false);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int col = dcol + 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3);

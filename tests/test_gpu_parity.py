@@ -9,6 +9,8 @@ bit-exactness, and the benchmark workloads at full size on sampled
 (sequence, KV head) units.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -64,6 +66,15 @@ def case_on_gpu(w):
     return make_case(w, device=DEV)
 
 
+def vector_takes(D, kv, rows):
+    """Whether the vector kernel covers G * max_q_len query rows per KV head:
+    up to 8 waves of its largest compiled row count (5 rows per wave for fp16
+    at D=128, 6 for 1-byte KV at D=128, 4 at D=256, 3 for int8 at D=256)."""
+    per_wave = {(128, "f16"): 5, (128, "fp8_e4m3"): 6, (128, "int8"): 6,
+                (256, "f16"): 4, (256, "fp8_e4m3"): 4, (256, "int8"): 3}[(D, kv)]
+    return rows <= 8 * per_wave
+
+
 def small(seed, **kw):
     base = dict(name="small", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
                 seq_lens=(1, 77, 300), seed=seed, pool_pages=48)
@@ -106,6 +117,11 @@ def _random_case(seed):
 def test_random_small_cases(seed, kernel):
     w = _random_case(seed)
     c = case_on_gpu(w)
+    G = w.num_q_heads // w.num_kv_heads
+    if kernel == "vector" and not vector_takes(w.head_dim, w.kv_dtype, G * w.q_len):
+        with pytest.raises(pda.PdaError, match="PDA_ERR_UNSUPPORTED"):
+            run_gpu(c, kernel=kernel)
+        return
     assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), w.kv_dtype, repr(w))
 
 
@@ -125,7 +141,7 @@ def test_kv_head_groups(Hkv, D, kv, G, Q, splits):
 
 
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
-@pytest.mark.parametrize("P", [16, 32, 64, 256])
+@pytest.mark.parametrize("P", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("D,kv,G,Q,W", [(128, "f16", 4, 1, 0), (256, "fp8_e4m3", 6, 2, 100),
                                         (128, "int8", 7, 3, 0), (256, "f16", 1, 1, 37)])
 @pytest.mark.parametrize("splits", [1, 5])
@@ -169,6 +185,11 @@ def test_head_dims_dtypes_groups(kv, D, G, Q, kernel):
     w = small(11, head_dim=D, kv_dtype=kv, num_q_heads=2 * G, num_kv_heads=2, q_len=Q,
               num_splits=3)
     c = case_on_gpu(w)
+    if kernel == "vector" and not vector_takes(D, kv, G * Q):
+        # more rows than the vector kernel's spill-free shapes cover: refused
+        with pytest.raises(pda.PdaError, match="PDA_ERR_UNSUPPORTED"):
+            run_gpu(c, kernel=kernel)
+        return
     assert_parity(run_gpu(c, kernel=kernel), oracle_full(c), kv, repr(w))
 
 
@@ -399,19 +420,43 @@ def test_split_combine_vs_oracle(D, S, T):
 # ---------------------------------------------------------------------------
 
 
-def sampled_parity(c, units, kernel):
-    got = run_gpu(c, kernel=kernel)
+def units_parity(c, got, units, workers=16):
+    """Compare the (sequence, KV head) units of a full-size output with the
+    oracle run on each unit alone (its pages gathered from the pool). The
+    oracle runs in a pool of host threads (its numpy work releases the
+    interpreter lock), up to `workers` units at a time, each with a
+    single-threaded BLAS."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
     assert torch.isfinite(got.float()).all()
     G = c.q.shape[1] // c.workload.num_kv_heads
+    host = got.cpu()
     worst = 0.0
-    for b, g in units:
-        sub = unit_subcase(c, b, g)
-        want = oracle.paged_decode_attention(**sub)  # [Q, G, D]
-        off = int(c.q_lens_host[:b].sum())
-        Q = int(c.q_lens_host[b])
-        part = got[off:off + Q, g * G:(g + 1) * G]
-        worst = max(worst, assert_parity(part, want, c.kv_dtype, f"unit ({b},{g})"))
-    return got, worst
+    # one BLAS thread per worker: nested BLAS threads oversubscribe the cores
+    with threadpool_limits(limits=1), ThreadPoolExecutor(
+            max_workers=max(1, min(workers, os.cpu_count() or 1))) as ex:
+        futs = []
+        for b, g in units:
+            sub = unit_subcase(c, b, g)  # device gathers stay on this thread
+            futs.append(((b, g), ex.submit(oracle.paged_decode_attention, **sub)))
+        for (b, g), f in futs:
+            want = f.result()  # [Q, G, D]
+            off = int(c.q_lens_host[:b].sum())
+            Q = int(c.q_lens_host[b])
+            part = host[off:off + Q, g * G:(g + 1) * G]
+            worst = max(worst, assert_parity(part, want, c.kv_dtype, f"unit ({b},{g})"))
+    return worst
+
+
+def all_units(c):
+    return [(b, g) for b in range(c.workload.batch) for g in range(c.workload.num_kv_heads)]
+
+
+def sampled_parity(c, units, kernel):
+    got = run_gpu(c, kernel=kernel)
+    return got, units_parity(c, got, units)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -434,25 +479,31 @@ def test_full_gqa4_d128_b8_l4096_variants(over):
 @pytest.mark.parametrize("B", [1, 2, 3, 8, 32])
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_full_gqa6_d256_l16384(B, window, kernel):
+    """Every (sequence, KV head) unit of every batch of the sweep."""
     w = WORKLOADS["gqa6_d256_l16384"].with_(batch=B, window=window)
     c = case_on_gpu(w)
-    units = sorted({(0, 0), (B - 1, 3), (B // 2, 1)})
-    sampled_parity(c, units, kernel)
+    sampled_parity(c, all_units(c), kernel)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_full_verify_q3_d128_b32(kernel):
+    """Every unit of the ragged verify batch (two empty sequences among
+    them), at its stated 8 splits."""
     c = case_on_gpu(WORKLOADS["verify_q3_d128_b32"])
-    lens = c.seq_lens_host
-    zero = int(np.flatnonzero(lens == 0)[0])
-    units = [(int(np.argmax(lens)), 0), (zero, 1), (int(np.argmin(np.where(lens > 0, lens,
-                                                                             1 << 30))), 3),
-             (7, 2)]
-    sampled_parity(c, units, kernel)
+    sampled_parity(c, all_units(c), kernel)
 
 
 @pytest.mark.parametrize("name", ["quant_fp8_d256_b64_l32768", "quant_int8_d256_b64_l32768"])
-@pytest.mark.parametrize("kernel", KERNELS)
-def test_full_quantized_d256_b64_l32768(name, kernel):
+def test_full_quantized_d256_b64_l32768(name):
+    """Every unit of the quantized long-context batch on the default path,
+    at its stated 8 splits."""
     c = case_on_gpu(WORKLOADS[name])
-    sampled_parity(c, [(0, 0), (63, 3), (31, 2)], kernel)
+    sampled_parity(c, all_units(c), "auto")
+
+
+@pytest.mark.parametrize("name", ["quant_fp8_d256_b64_l32768", "quant_int8_d256_b64_l32768"])
+def test_full_quantized_d256_b64_l32768_vector(name):
+    """The vector kernel on the same batch: 32 units, every KV head of 8
+    sequences spread over the batch."""
+    c = case_on_gpu(WORKLOADS[name])
+    sampled_parity(c, [(b, g) for b in range(0, 64, 9) for g in range(4)][:32], "vector")
