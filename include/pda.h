@@ -26,9 +26,11 @@
  * Conventions for every entry point
  *  - All tensors are contiguous, row-major, and live in device memory of the
  *    current HIP device; the caller owns them. The library never allocates,
- *    frees or synchronizes, issues no memsets, and keeps no device state, so
- *    a call can be captured in a HIP graph; with automatic splits a captured
- *    call balances whatever seq_lens / q_lens hold when it is replayed.
+ *    frees or synchronizes and issues no memsets, so a call can be captured
+ *    in a HIP graph; with automatic splits a captured call balances whatever
+ *    seq_lens / q_lens hold when it is replayed. Its only device state is the
+ *    scratch array of pda_paged_decode_attention_noalloc (a module global,
+ *    one per device, never allocated at run time).
  *  - Every launch goes on the caller's `stream` (the pull request passes the
  *    current stream to every launch); calls return after enqueueing.
  *  - Arguments are validated on the host before any HIP call; a failure
@@ -231,6 +233,30 @@ pda_status pda_split_combine(const float* partial_o, const float* partial_ml,
                              void* out, int32_t num_tokens, int32_t num_q_heads,
                              int32_t head_dim, int32_t num_splits,
                              hipStream_t stream);
+
+/*
+ * The one-call path without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Arguments and results as for
+ * pda_paged_decode_attention, which it runs; the split partials and chunk
+ * lists go to a scratch array of PDA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on, from load until the process ends. It
+ * calls no allocator. A call needing more workspace than that
+ * (pda_decode_workspace_bytes) returns PDA_ERR_WORKSPACE before any launch.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (two streams, or two host threads) race, and must be ordered by
+ * the caller. Nothing in the array needs clearing between calls (each call
+ * writes what it reads).
+ */
+#define PDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pda_status pda_paged_decode_attention_noalloc(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+    float scale, int32_t window, int32_t num_splits, void* out,
+    const float* k_scale, const float* v_scale, const pda_decode_dims* dims,
+    hipStream_t stream);
+/* Bytes of the scratch array of pda_paged_decode_attention_noalloc. */
+size_t pda_noalloc_scratch_bytes(void);
 
 /* Sizes of a cache write. */
 typedef struct pda_cache_dims {

@@ -21,7 +21,8 @@ __all__ = [
     "paged_decode_attention", "paged_decode_partials", "split_combine",
     "resolve_splits", "workspace_bytes", "attention_stages", "partials_bytes", "decode_dims",
     "load_library", "library_path", "KV_DTYPES", "PDA_MAX_ROWS", "PDA_MAX_SPLITS",
-    "PdaError", "partials_views", "KERNELS",
+    "PdaError", "partials_views", "KERNELS", "paged_decode_attention_noalloc",
+    "noalloc_scratch_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,10 @@ _SIGNATURES = {
     "pda_decode_partials_bytes": (ctypes.c_int64, [_DIMS, ctypes.c_int32, ctypes.c_int32]),
     "pda_write_kv_cache": (ctypes.c_int, [
         _VP, _VP, _I32P, _VP, _VP, _VP, _VP, ctypes.POINTER(CacheDims), _VP]),
+    "pda_paged_decode_attention_noalloc": (ctypes.c_int, [
+        _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+        _VP, _VP, _VP, _DIMS, _VP]),
+    "pda_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -212,6 +217,27 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, q_lens, s
         _ptr(q_lens), float(scale), int(window), int(num_splits), _ptr(out),
         _ptr(k_scale), _ptr(v_scale), ctypes.byref(dims), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale,
+                                   window, num_splits, out, k_scale=None, v_scale=None,
+                                   kv_dtype=None, max_q_len=None, stream=None, kernel="auto",
+                                   kv_layout="NHD"):
+    """paged_decode_attention without a workspace: the library's per-device
+    scratch array holds the split partials, so the call allocates nothing
+    (see include/pda.h; calls that overlap on one device race)."""
+    lib = load_library()
+    _contig(q, k_cache, v_cache, block_table, seq_lens, q_lens, out, k_scale, v_scale)
+    dims = decode_dims(q, k_cache, block_table, seq_lens, q_lens, max_q_len, kv_dtype, kernel,
+                       kv_layout)
+    _check(lib.pda_paged_decode_attention_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(q_lens), float(scale), int(window), int(num_splits), _ptr(out),
+        _ptr(k_scale), _ptr(v_scale), ctypes.byref(dims), _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().pda_noalloc_scratch_bytes())
 
 
 def attention_stages(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale, window,
