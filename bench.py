@@ -3,28 +3,39 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one call of the whole hot path (pda_paged_decode_attention: decode
-and split combine) over one batch of synthetic input already resident in HBM. The headline workload
-is the fp16-KV D=128 case: 8 sequences of 4096 keys, 32 query heads over 8
-KV heads, page size 16, seeded random page permutation, automatic splits.
-Its KV pool (134 MB) fits in the 256 MiB Infinity Cache, so the timed loop
-rotates over enough replicas of the inputs (>= 1 GiB in total) that every step
-reads its KV from HBM.
+and split combine) over one batch of synthetic input already resident in HBM.
+The headline workload is the largest one: fp8-e4m3 KV with per-KV-head
+scales, D=256, 16 query heads over 4 KV heads, 64 sequences of 32768 keys,
+8 splits (4.3 GB of K+V per call). Beside it, with the same fields, go a
+D=128 line (fp16 KV, 32/8 heads, 8 x 4096 keys, automatic splits) and a D=256
+fp16 line (24/4 heads, 32 x 16384 keys), since the metric names both head
+dimensions. Pools smaller than 1 GiB are replicated so that every timed step
+reads its KV from HBM, not from the 256 MiB Infinity Cache.
 
 Reported (one JSON line):
   value        algorithmic bytes (every visible K/V element once, q, out) per
                step / measured step time, GB/s
   roofline     the decode kernel alone: same bytes / its average launch
                duration (launches queued back to back on the launch stream,
-               HIP events around them), against the 8 TB/s HBM peak;
-               traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE +
-               WRITE_SIZE counters (each scaled by what the counter reads for
-               a plain 1 GiB copy) when a counter summary for the current
-               kernel sources exists, else null
-  cpu_baseline the fp64 oracle on this host's cores, on a bounded sample of
-               the same workload
-  cells        the same measurement for the D=256 and other workloads, each
-               in a process of its own (its KV pool the first large
-               allocation there, as in a serving process)
+               HIP events around them), against the 8 TB/s HBM peak and
+               against the streaming-read rate measured on this device by the
+               library's read probe; traffic = HBM bytes per launch from
+               rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each scaled by what
+               the counter reads for a plain 1 GiB copy) when a counter
+               summary for the current kernel sources exists, else null
+  lines        the D=128 and D=256 fp16 workloads with the same fields
+  cpu_baseline the fp64 oracle on this host's cores (one BLAS thread per
+               worker thread, a pool over (sequence, KV head) units), per
+               workload: the headline's sample is its `value`
+  cells        the other workloads and variants (the tiny workload, the D=256
+               batch sweep with and without a window, the ragged verify batch,
+               int8 KV, layouts, the vector kernel), each measured in a
+               process of its own (its KV pool the first large allocation
+               there, as in a serving process)
+
+`python bench.py --summarize DIR ...` turns rocprofv3 output (kernel trace
+statistics and FETCH_SIZE / WRITE_SIZE counter runs) into the summaries kept
+under profiles/.
 """
 
 from __future__ import annotations
@@ -45,24 +56,37 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "decode-attn achieved HBM GB/s (fraction of peak) + us/call, D=128 & D=256"
-HEADLINE = "gqa4_d128_b8_l4096"
+HEADLINE = "quant_fp8_d256_b64_l32768"
+# Lines reported with the headline's fields (roofline, traffic): the D=128
+# and D=256 fp16 workloads.
+LINES = [("gqa4_d128_b8_l4096", {}), ("gqa6_d256_l16384", dict(batch=32))]
 CELLS = [
-    # the headline shape with a caller split count inside the 1..8 range its
+    # the tiny workload at its two split counts (latency-bound: us only)
+    ("tiny_d128", dict(num_splits=1)),
+    ("tiny_d128", dict(num_splits=3)),
+    # the D=128 shape with a caller split count inside the 1..8 range its
     # configuration names for automatic splitting
     ("gqa4_d128_b8_l4096", dict(num_splits=8)),
-    # the headline shape in the other cache layouts: HND ([page, head, slot,
+    # the D=128 shape in the other cache layouts: HND ([page, head, slot,
     # dim]), 64-key pages, and an identity block table (pages in pool order)
     ("gqa4_d128_b8_l4096", dict(layout="HND")),
     ("gqa4_d128_b8_l4096", dict(page_size=64)),
     ("gqa4_d128_b8_l4096", dict(identity_table=True)),
-    # D=256 batch sweep, without and with a 4096-key sliding window
+    # D=256 batch sweep, without and with a 4096-key sliding window (B=32
+    # without a window is a line)
     *[("gqa6_d256_l16384", dict(batch=b, window=win))
-      for win in (0, 4096) for b in (1, 2, 3, 8, 32)],
+      for win in (0, 4096) for b in (1, 2, 3, 8, 32) if (b, win) != (32, 0)],
     ("verify_q3_d128_b32", {}),
     # the same ragged batch with automatic splits (balanced per sequence)
     ("verify_q3_d128_b32", dict(num_splits=0)),
-    ("quant_fp8_d256_b64_l32768", {}),
     ("quant_int8_d256_b64_l32768", {}),
+]
+# The vector (v_dot2) kernel family on the four larger workloads.
+VECTOR_CELLS = [
+    ("gqa4_d128_b8_l4096", {}),
+    ("gqa6_d256_l16384", dict(batch=32)),
+    ("verify_q3_d128_b32", {}),
+    ("quant_fp8_d256_b64_l32768", {}),
 ]
 
 
@@ -101,11 +125,13 @@ def kernel_source_hash(kernel: str = "decode_mfma") -> str:
     return h.hexdigest()[:16]
 
 
-def workload_key(workload: str, over: dict) -> str:
+def workload_key(workload: str, over: dict, kernel: str = "auto") -> str:
     """Name of a workload with the command line's overrides (batch, window,
-    split count), as profiles/ files are keyed."""
+    split count) and, for the vector kernel family, that family, as profiles/
+    files are keyed."""
     tags = {"batch": "b", "window": "w", "num_splits": "s"}
-    return workload + "".join(f"_{tags[k]}{v}" for k, v in sorted(over.items()) if k in tags)
+    key = workload + "".join(f"_{tags[k]}{v}" for k, v in sorted(over.items()) if k in tags)
+    return key + ("_vector" if kernel == "vector" else "")
 
 
 def traffic_for(key: str):
@@ -277,36 +303,6 @@ def measure(case, steps: int, warmup: int, num_splits: int, device, kernel: str 
                 per_call_us=per_call)
 
 
-def cpu_baseline(case, budget_s: float = 12.0):
-    """The fp64 oracle on this host, on whole (sequence, KV head) units of the
-    same workload, repeated until about `budget_s` seconds of work."""
-    import numpy as np
-
-    import oracle
-    from synth import algorithmic_bytes
-
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    h = case.host()
-    nbytes = algorithmic_bytes(case)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.paged_decode_attention(**h)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
-            break
-    np.asarray(0)
-    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"the whole {case.workload.name} workload (all {len(h['seq_lens'])} "
-                      f"sequences x {h['k_cache'].shape[2]} KV heads), {reps} pass(es) in "
-                      f"{el:.1f} s"}
-
-
 # Long-query (prefill kernel) cells: a fresh prefill and a chunked prefill.
 PREFILL_CELLS = ["prefill_d128_b4_q2048", "chunked_d128_b8_l8192_q512", "prefill_d256_b4_q2048"]
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, AMD published
@@ -386,38 +382,384 @@ def measure_writer(T, Hkv, D, kv, steps, device):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
 
 
-def cell_record(name, w, m):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Worker threads for the oracle: the host's cores, at most 16 (the CPU
+    share of one GPU on the boxes this runs on)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def time_oracle_units(case, units, threads: int, repeats: int = 1) -> float:
+    """Wall seconds for the fp64 oracle over the given (sequence, KV head)
+    units of `case` (each gathered from the pool beforehand, outside the
+    timed region), `threads` units at a time on a pool of host threads with
+    one BLAS thread each; the median of `repeats` runs."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from synth import unit_subcase
+
+    subs = [unit_subcase(case, b, g) for b, g in units]
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            if threads == 1:
+                for sub in subs:
+                    oracle.paged_decode_attention(**sub)
+            else:
+                with ThreadPoolExecutor(max_workers=threads) as ex:
+                    list(ex.map(lambda sub: oracle.paged_decode_attention(**sub), subs))
+            times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2]
+
+
+# Oracle timings per workload: (workload, overrides, units timed (None: all),
+# repeats, also with one thread). The two large quantized workloads are timed
+# on 64 of their 256 units spread over the batch (whole-call time scaled by
+# units: every unit of those has the same length).
+CPU_CONFIGS = [
+    ("tiny_d128", {}, None, 5, True),
+    ("gqa4_d128_b8_l4096", {}, None, 3, True),
+    ("gqa6_d256_l16384", dict(batch=32), None, 1, False),
+    ("gqa6_d256_l16384", dict(batch=32, window=4096), None, 1, False),
+    ("verify_q3_d128_b32", {}, None, 1, False),
+    ("quant_fp8_d256_b64_l32768", {}, 64, 1, False),
+    ("quant_int8_d256_b64_l32768", {}, 64, 1, False),
+]
+
+
+def cpu_baseline(device, gpu_us: dict, headline_case=None):
+    """The fp64 oracle timed on this host, per workload. Returns the record
+    whose `value` is the headline workload's rate (algorithmic bytes of one
+    call / the oracle's time for that call)."""
+    import torch
+
+    from synth import WORKLOADS, algorithmic_bytes, make_case
+
+    threads = oracle_threads()
+    per = []
+    head = None
+    for name, over, n_units, repeats, single in CPU_CONFIGS:
+        w = WORKLOADS[name].with_(**over)
+        if headline_case is not None and name == HEADLINE and not over:
+            case = headline_case
+        else:
+            case = make_case(w, device=device)
+        units = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+        total = len(units)
+        if n_units is not None and n_units < total:
+            step = total / n_units
+            units = [units[int(i * step)] for i in range(n_units)]
+        wall = time_oracle_units(case, units, threads, repeats)
+        us = wall * 1e6 * total / len(units)
+        nbytes = algorithmic_bytes(case)
+        key = workload_key(name, over)
+        rec = {"workload": key, "units": total, "units_timed": len(units), "threads": threads,
+               "wall_s": round(wall, 4), "us_per_call": round(us, 1),
+               "GB_s": round(nbytes / (us * 1e-6) / 1e9, 4)}
+        if key in gpu_us:
+            rec["gpu_us_per_call"] = gpu_us[key]
+            rec["gpu_speedup"] = round(us / gpu_us[key], 1)
+        if single:
+            w1 = time_oracle_units(case, units, 1, repeats)
+            rec["single_thread_wall_s"] = round(w1, 4)
+            rec["single_thread_us_per_call"] = round(w1 * 1e6 * total / len(units), 1)
+        per.append(rec)
+        print(json.dumps({"cpu_oracle": rec}), file=sys.stderr, flush=True)
+        if name == HEADLINE and not over:
+            head = rec
+        if case is not headline_case:
+            del case
+            torch.cuda.empty_cache()
+    return {"value": head["GB_s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{head['units_timed']} of the {head['units']} (sequence, KV head) units of "
+                      f"{HEADLINE}, spread over the batch, on {threads} host threads (one BLAS "
+                      f"thread each); whole-call time scaled by units "
+                      f"({head['wall_s']} s measured)",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(), "per_workload": per}
+
+
+def measure_probe(device, steps: int = 20):
+    """The streaming-read rate of one launch of the library's read probe over
+    a 4 GiB buffer (well past the on-package caches), for a few grid sizes;
+    the best one is this device's measured read roof."""
+    import torch
+
+    import paged_split_decode_amd as pda
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    best, rows = None, []
+    for per_cu in (4, 8, 16, 32):
+        wg = n_cu * per_cu
+        sink = torch.zeros(wg, dtype=torch.int32, device=device)
+        for _ in range(3):
+            pda.hbm_read_probe(buf, sink, wg)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        _hold_gpu()
+        t0.record()
+        for _ in range(steps):
+            pda.hbm_read_probe(buf, sink, wg)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / steps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append({"workgroups": wg, "us": round(us, 1), "GB_s": round(gbs, 1)})
+        if best is None or gbs > best["GB_s"]:
+            best = rows[-1]
+    return {"probe": "pda_hbm_read_probe (16-byte non-temporal loads, grid-stride)",
+            "bytes": nbytes, "GB_s": best["GB_s"], "workgroups": best["workgroups"],
+            "frac_of_peak": round(best["GB_s"] / HBM_PEAK_GBS, 4), "sweep": rows}
+
+
+def decode_record(name, over, w, m, kernel="auto", roof_gbs=None):
+    """Fields of a measured decode workload: whole-call rate, and the decode
+    kernel's own rate against the peak and the measured read roof."""
     us = m["ms_per_step"] * 1e3
     gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
     dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
-    return {"workload": name, "batch": w.batch, "window": w.window, "kv_dtype": w.kv_dtype,
-            "head_dim": w.head_dim, "page_size": w.page_size, "kv_layout": w.layout,
-            "identity_table": w.identity_table, "splits": m["splits"],
-            "us_per_call": round(us, 2),
-            "GB_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "eager_us_per_call": round(m["ms_eager"] * 1e3, 2), "per_call_us": m["per_call_us"],
-            "decode_us": round(m["decode_ms"] * 1e3, 2), "decode_GB_s": round(dec_gbs, 1),
-            "algorithmic_bytes": m["bytes"]}
+    key = workload_key(name, over, kernel)
+    rec = {"workload": key, "batch": w.batch, "window": w.window, "kv_dtype": w.kv_dtype,
+           "head_dim": w.head_dim, "page_size": w.page_size, "kv_layout": w.layout,
+           "identity_table": w.identity_table, "splits": m["splits"], "kernel": kernel,
+           "us_per_call": round(us, 2), "GB_s": round(gbs, 1),
+           "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "eager_us_per_call": round(m["ms_eager"] * 1e3, 2), "per_call_us": m["per_call_us"],
+           "decode_us": round(m["decode_ms"] * 1e3, 2), "decode_GB_s": round(dec_gbs, 1),
+           "algorithmic_bytes": m["bytes"]}
+    if roof_gbs:
+        rec["frac_of_measured_roof"] = round(gbs / roof_gbs, 4)
+    return rec
+
+
+def roofline_record(m, kernel, key, roof_gbs=None):
+    dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
+    family = "decode_vector" if kernel == "vector" else "decode_mfma"
+    rec = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(key),
+           "kernel": "pda_decode_kernel" if kernel == "vector" else "pda_decode_mfma_kernel",
+           "decode_us": round(m["decode_ms"] * 1e3, 3),
+           "kernel_source_hash": kernel_source_hash(family)}
+    if roof_gbs:
+        rec["measured_roof_GB_s"] = roof_gbs
+        rec["frac_of_measured_roof"] = round(dec_gbs / roof_gbs, 4)
+    return rec
 
 
 def measure_cell(spec: str, steps: int, kernel: str, device):
-    """One extra cell ("decode:i", "prefill:i" or "writer:i" of CELLS,
-    PREFILL_CELLS, WRITER_CELLS)."""
+    """One workload measured on its own ("line:i", "decode:i", "vector:i",
+    "prefill:i", "writer:i" or "probe:0")."""
     from synth import WORKLOADS, make_case
 
     kind, i = spec.split(":")
     i = int(i)
     n = max(50, steps // 2)  # at least 50 calls per cell (percentiles)
-    if kind == "decode":
-        name, over = CELLS[i]
+    if kind == "probe":
+        return measure_probe(device)
+    if kind in ("line", "decode", "vector"):
+        name, over = {"line": LINES, "decode": CELLS, "vector": VECTOR_CELLS}[kind][i]
+        kern = "vector" if kind == "vector" else kernel
         wc = WORKLOADS[name].with_(**over)
-        return cell_record(name, wc, measure(make_case(wc, device=device), n, 10,
-                                             wc.num_splits, device, kernel))
+        m = measure(make_case(wc, device=device), n if kind != "line" else steps, 10,
+                    wc.num_splits, device, kern)
+        rec = decode_record(name, over, wc, m, kern)
+        if kind in ("line", "vector"):
+            rec["roofline"] = roofline_record(m, kern, rec["workload"])
+        return rec
     if kind == "prefill":
         c = make_case(WORKLOADS[PREFILL_CELLS[i]], device=device)
         return prefill_record(PREFILL_CELLS[i], c, measure(c, n, 10, 1, device, kernel))
     T, Hkv, D, kv = WRITER_CELLS[i]
     return measure_writer(T, Hkv, D, kv, n, device)
+
+
+def run_cell(spec: str, steps: int, kernel: str) -> dict:
+    """measure_cell in a process of its own."""
+    r = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), "--cell", spec,
+                        "--steps", str(steps), "--kernel", kernel],
+                       capture_output=True, text=True, timeout=900)
+    if r.returncode != 0:
+        raise RuntimeError(f"cell {spec} failed:\n{r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def _with_roof(rec, roof):
+    """Add the fractions of the measured read roof to a record."""
+    if not roof:
+        return rec
+    rec["frac_of_measured_roof"] = round(rec["GB_s"] / roof, 4)
+    if "roofline" in rec:
+        rec["roofline"]["measured_roof_GB_s"] = roof
+        rec["roofline"]["frac_of_measured_roof"] = round(rec["roofline"]["achieved"] / roof, 4)
+    return rec
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/)
+# ---------------------------------------------------------------------------
+
+
+def _csv_rows(root: str, suffix: str):
+    import csv
+
+    rows = []
+    for dirpath, _, files in os.walk(root):
+        for fn in sorted(files):
+            if fn.endswith(suffix):
+                with open(os.path.join(dirpath, fn), newline="") as f:
+                    rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _kernel_family(name: str) -> str:
+    if "pda_prefill_mfma_kernel" in name:
+        return "prefill_mfma"
+    if "pda_decode_mfma_kernel" in name:
+        return "decode_mfma"
+    if "pda_decode_kernel" in name:
+        return "decode_vector"
+    return ""
+
+
+def summarize(run_dir: str, workload: str, over: dict, kernel: str, command: str,
+              out_dir: str) -> str:
+    """Write profiles/<family>_<key>.txt (and traffic_<key>.json when the
+    FETCH_SIZE and WRITE_SIZE runs are there) from a directory holding the
+    rocprofv3 output of `command`: trace/ (--kernel-trace --stats),
+    FETCH_SIZE/, WRITE_SIZE/ (--pmc, with --reference-copy-mib 1024), and
+    optionally one directory per further counter set."""
+    from synth import WORKLOADS, workload_algorithmic_bytes, workload_visible_pairs
+
+    w = WORKLOADS[workload].with_(**over)
+    key = workload_key(workload, over, kernel)
+    stats = _csv_rows(os.path.join(run_dir, "trace"), "kernel_stats.csv")
+    mine = [r for r in stats if r.get("Name", "").find("pda::") >= 0]
+    fam_rows = [r for r in mine if _kernel_family(r["Name"])]
+    if not fam_rows:
+        raise RuntimeError(f"no pda kernel in {run_dir}/trace")
+    main_row = max(fam_rows, key=lambda r: float(r["TotalDurationNs"]))
+    family = _kernel_family(main_row["Name"])
+    avg_ns = float(main_row["AverageNs"])
+    nbytes = workload_algorithmic_bytes(w)
+    lines = [f"# {family} kernel, workload {key}", "",
+             "Commands (run from the repository root on one MI355X, TMPDIR=/tmp; OUT = the",
+             "output directory):",
+             f"  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- {command}",
+             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/FETCH_SIZE -o run -- "
+             f"{command} --steps 10 --warmup 2 --reference-copy-mib 1024",
+             "  rocprofv3 --pmc WRITE_SIZE (same as above, -d OUT/WRITE_SIZE)",
+             "  python bench.py --summarize OUT " + command.split("--no-cpu ", 1)[1], "",
+             "Kernel trace (rocprofv3 --stats, rows of this library):",
+             "  name | calls | average ns | min ns | max ns"]
+    for r in sorted(mine, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"  {r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{r['MinNs']} | {r['MaxNs']}")
+    lines.append("")
+    traffic = None
+    if family == "prefill_mfma":
+        flops = 4 * w.head_dim * workload_visible_pairs(w)
+        tf = flops / (avg_ns * 1e-9) / 1e12
+        lines.append(f"Algorithmic work per launch: {flops} flops (4 * D per visible (row, key))")
+        lines.append(f"{family} kernel average duration: {avg_ns / 1e3:.2f} us -> {tf:.1f} TFLOP/s "
+                     f"= {tf / 2500.0:.3f} of 2.5 PFLOP/s")
+    else:
+        gbs = nbytes / (avg_ns * 1e-9) / 1e9
+        lines.append(f"Algorithmic bytes per launch (K+V visible keys once, q, out): {nbytes}")
+        lines.append(f"{family} kernel average duration: {avg_ns / 1e3:.2f} us -> {gbs:.1f} GB/s "
+                     f"= {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s")
+    # HBM counters
+    fetch = _counter_means(os.path.join(run_dir, "FETCH_SIZE"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(run_dir, "WRITE_SIZE"), "WRITE_SIZE")
+    if fetch and write and family in fetch[0] and family in write[0]:
+        (fk, fref), (wk, wref) = (fetch[0][family], fetch[1]), (write[0][family], write[1])
+        fscale = (1 << 30) / (fref * 1024.0)
+        wscale = (1 << 30) / (wref * 1024.0)
+        hbm = int(fk[0] * 1024 * fscale + wk[0] * 1024 * wscale)
+        base = nbytes
+        lines += ["", "HBM counters (rocprofv3 --pmc, KiB per dispatch, averaged over "
+                      f"{fk[1]} dispatches of the kernel):",
+                  f"  kernel FETCH_SIZE = {fk[0]:.1f} KiB, WRITE_SIZE = {wk[0]:.1f} KiB",
+                  f"  reference plain copy of 1 GiB: FETCH_SIZE = {fref:.1f} KiB, "
+                  f"WRITE_SIZE = {wref:.1f} KiB",
+                  f"  calibration: bytes = FETCH_SIZE x 1024 x {fscale:.4f} + WRITE_SIZE x 1024 "
+                  f"x {wscale:.4f}",
+                  f"  HBM bytes per launch = {hbm} ({hbm / base:.4f} x algorithmic)"]
+        traffic = {"workload": key, "kernel": family, "hbm_bytes_per_launch": hbm,
+                   "algorithmic_bytes": base, "fetch_kib": round(fk[0], 1),
+                   "write_kib": round(wk[0], 1), "fetch_scale": round(fscale, 4),
+                   "write_scale": round(wscale, 4),
+                   "kernel_source_hash": kernel_source_hash(family),
+                   "source": f"{family}_{key}.txt"}
+    # further counter sets: every directory other than the three above
+    extra = []
+    for d in sorted(os.listdir(run_dir)):
+        if d in ("trace", "FETCH_SIZE", "WRITE_SIZE") or not os.path.isdir(os.path.join(run_dir, d)):
+            continue
+        means = _all_counter_means(os.path.join(run_dir, d), family)
+        if means:
+            extra.append(f"  {d}: " + ", ".join(f"{k} = {v:.4g}" for k, v in sorted(means.items())))
+    if extra:
+        lines += ["", "Other counters (rocprofv3 --pmc <set> with the first command's arguments "
+                      "and --steps 10 --warmup 2; mean per dispatch of the kernel):"] + extra
+    lines += ["", f"kernel_source_hash: {kernel_source_hash(family)}", ""]
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, f"{family}_{key}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    if traffic is not None:
+        with open(os.path.join(out_dir, f"traffic_{key}.json"), "w") as f:
+            json.dump(traffic, f, indent=1)
+            f.write("\n")
+    return path
+
+
+def _counter_means(run_dir: str, counter: str):
+    """({family: (mean KiB per dispatch, dispatches)}, reference copy value)
+    from one --pmc run, or None. The reference copy is the largest value of
+    the counter among the runtime's buffer-copy kernels (the 1 GiB copy that
+    --reference-copy-mib runs is the largest of them)."""
+    rows = _csv_rows(run_dir, "counter_collection.csv")
+    if not rows:
+        return None
+    per, ref = {}, 0.0
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        name, v = r.get("Kernel_Name", ""), float(r.get("Counter_Value", 0.0))
+        fam = _kernel_family(name)
+        if fam:
+            per.setdefault(fam, []).append(v)
+        elif "copyBuffer" in name:  # the runtime's device-to-device copy (torch copy_)
+            ref = max(ref, v)
+    if not per or ref <= 0:
+        return None
+    return {k: (sum(v) / len(v), len(v)) for k, v in per.items()}, ref
+
+
+def _all_counter_means(run_dir: str, family: str) -> dict:
+    rows = _csv_rows(run_dir, "counter_collection.csv")
+    acc = {}
+    for r in rows:
+        if _kernel_family(r.get("Kernel_Name", "")) != family:
+            continue
+        acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
 def main(argv=None):
@@ -434,13 +776,28 @@ def main(argv=None):
     ap.add_argument("--reference-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
-    ap.add_argument("--no-cells", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--no-cells", action="store_true", help="skip the lines and extra cells")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cell", default=None,
-                    help="measure one extra cell (decode:i, prefill:i or writer:i) and print "
-                         "its record; the full run measures each cell this way, in a process "
-                         "of its own")
+                    help="measure one extra workload (line:i, decode:i, vector:i, prefill:i, "
+                         "writer:i or probe:0) and print its record; the full run measures each "
+                         "this way, in a process of its own")
+    ap.add_argument("--summarize", default=None, metavar="DIR",
+                    help="write the profiles/ summary of the rocprofv3 output in DIR for the "
+                         "workload given by --workload / --batch / --window / --splits / "
+                         "--kernel (no GPU needed)")
     args = ap.parse_args(argv)
+    over = {k: v for k, v in (("batch", args.batch), ("window", args.window),
+                              ("num_splits", args.splits)) if v is not None}
+    if args.summarize:
+        cmd = "python -u bench.py --no-cells --no-cpu --workload " + args.workload + "".join(
+            f" --{k.replace('num_splits', 'splits')} {v}" for k, v in sorted(over.items()))
+        if args.kernel != "auto":
+            cmd += f" --kernel {args.kernel}"
+        cmd += f" --steps {args.steps} --warmup {args.warmup}"
+        print(summarize(args.summarize, args.workload, over, args.kernel, cmd,
+                        os.path.join(ROOT, "profiles")))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this operator runs on a single MI355X)", file=sys.stderr)
@@ -463,60 +820,61 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     w = WORKLOADS[args.workload]
-    over = {k: v for k, v in (("batch", args.batch), ("window", args.window),
-                              ("num_splits", args.splits)) if v is not None}
     if over:
         w = w.with_(**over)
     case = make_case(w, device=device)
     m = measure(case, args.steps, args.warmup, w.num_splits, device, args.kernel)
     gbs = m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9
-    dec_gbs = m["bytes"] / (m["decode_ms"] * 1e-3) / 1e9
-    traffic = traffic_for(workload_key(args.workload, over))
+    key = workload_key(args.workload, over, args.kernel)
     rec = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": w.batch, "seq_len": w.seq_len,
+        "config": {"workload": key, "batch": w.batch, "seq_len": w.seq_len,
                    "q_len": w.q_len, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "page_size": w.page_size, "kv_dtype": w.kv_dtype, "num_splits": m["splits"],
+                   "page_size": w.page_size, "kv_dtype": w.kv_dtype, "window": w.window,
+                   "num_splits": m["splits"],
                    "us_per_call": round(m["ms_per_step"] * 1e3, 2),
                    "eager_us_per_call": round(m["ms_eager"] * 1e3, 2),
                    "per_call_us": m["per_call_us"],
                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                    "algorithmic_bytes": m["bytes"], "input_replicas": m["replicas"],
-                   "settle_steps": m["settle"],
-                   "kernel": args.kernel,
+                   "settle_steps": m["settle"], "kernel": args.kernel,
                    "accumulate": "fp32"},
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "pda_decode_mfma_kernel" if args.kernel != "vector" else "pda_decode_kernel",
-                     "decode_us": round(m["decode_ms"] * 1e3, 3),
-                     "kernel_source_hash": kernel_source_hash()},
+        "roofline": roofline_record(m, args.kernel, key),
     }
+    gpu_us = {key: rec["config"]["us_per_call"]}
     if not args.no_cells:
-        # Each cell in a fresh process: a KV pool allocated after other large
-        # buffers were freed measured up to 4.5% slower (D=256, 32 x 16384:
-        # 369 against 354 us per decode), while a serving process allocates
-        # its pool once.
+        # Each workload in a fresh process: a KV pool allocated after other
+        # large buffers were freed measured up to 4.5% slower (D=256, 32 x
+        # 16384: 369 against 354 us per decode), while a serving process
+        # allocates its pool once.
         del case
         torch.cuda.empty_cache()
-        for kind, n, key in (("decode", len(CELLS), "cells"), ("prefill", len(PREFILL_CELLS),
-                                                            "prefill_cells"),
-                             ("writer", len(WRITER_CELLS), "writer_cells")):
-            rec[key] = []
+        probe = run_cell("probe:0", args.steps, args.kernel)
+        print(json.dumps({"probe": probe}), file=sys.stderr, flush=True)
+        roof = probe["GB_s"]
+        rec["hbm_read_roof"] = probe
+        rec["config"]["frac_of_measured_roof"] = round(gbs / roof, 4)
+        rec["roofline"]["measured_roof_GB_s"] = roof
+        rec["roofline"]["frac_of_measured_roof"] = round(rec["roofline"]["achieved"] / roof, 4)
+        for kind, n, field in (("line", len(LINES), "lines"), ("decode", len(CELLS), "cells"),
+                               ("vector", len(VECTOR_CELLS), "vector_cells"),
+                               ("prefill", len(PREFILL_CELLS), "prefill_cells"),
+                               ("writer", len(WRITER_CELLS), "writer_cells")):
+            rec[field] = []
             for i in range(n):
-                r = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), "--cell",
-                                    f"{kind}:{i}", "--steps", str(args.steps), "--kernel",
-                                    args.kernel], capture_output=True, text=True, timeout=900)
-                if r.returncode != 0:
-                    raise RuntimeError(f"cell {kind}:{i} failed:\n{r.stderr[-2000:]}")
-                rec[key].append(json.loads(r.stdout.strip().splitlines()[-1]))
-                print(json.dumps({f"{kind}_cell": rec[key][-1]}), file=sys.stderr, flush=True)
-        case = make_case(w, device=device)
+                r = run_cell(f"{kind}:{i}", args.steps, args.kernel)
+                if kind in ("line", "decode", "vector"):
+                    r = _with_roof(r, roof)
+                    gpu_us[r["workload"]] = r["us_per_call"]
+                rec[field].append(r)
+                print(json.dumps({f"{kind}_cell": r}), file=sys.stderr, flush=True)
+        case = None
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(case)
+        rec["cpu_baseline"] = cpu_baseline(device, gpu_us, case)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -317,6 +317,18 @@ int64_t pda_decode_workspace_bytes(const pda_decode_dims* dims, int32_t window,
 int64_t pda_decode_partials_bytes(const pda_decode_dims* dims, int32_t window,
                                   int32_t num_splits);
 
+/*
+ * Measurement aid (not part of the attention path): reads `bytes` of device
+ * memory at `src` (both multiples of 16) once, as fast as one launch of
+ * `workgroups` workgroups of 256 threads can (16-byte non-temporal loads in
+ * a grid-stride loop), and writes one XOR word per workgroup to `sink`
+ * (uint32 [workgroups], device memory). Timed over a buffer larger than the
+ * on-package caches, it gives the streaming-read rate of this device's HBM,
+ * the practical roof of the decode kernels. One launch on `stream`.
+ */
+pda_status pda_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                              int32_t workgroups, hipStream_t stream);
+
 /* Message of the calling thread's last non-OK status ("" if none). */
 const char* pda_last_error(void);
 

@@ -22,7 +22,7 @@ __all__ = [
     "resolve_splits", "workspace_bytes", "attention_stages", "partials_bytes", "decode_dims",
     "load_library", "library_path", "KV_DTYPES", "PDA_MAX_ROWS", "PDA_MAX_SPLITS",
     "PdaError", "partials_views", "KERNELS", "paged_decode_attention_noalloc",
-    "noalloc_scratch_bytes",
+    "noalloc_scratch_bytes", "hbm_read_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +84,7 @@ _SIGNATURES = {
         _VP, _VP, _VP, _I32P, _I32P, _I32P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
         _VP, _VP, _VP, _DIMS, _VP]),
     "pda_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "pda_hbm_read_probe": (ctypes.c_int, [_VP, ctypes.c_size_t, _VP, ctypes.c_int32, _VP]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -238,6 +239,17 @@ def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, seq_lens, q
 
 def noalloc_scratch_bytes() -> int:
     return int(load_library().pda_noalloc_scratch_bytes())
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None):
+    """One launch of the streaming-read probe over all of ``src`` (a
+    contiguous device tensor); ``sink`` holds at least ``workgroups`` int32."""
+    _contig(src, sink)
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < 4 * workgroups:
+        raise ValueError("sink must hold one 32-bit word per workgroup")
+    _check(load_library().pda_hbm_read_probe(_ptr(src), nbytes, _ptr(sink), int(workgroups),
+                                             _stream(stream)))
 
 
 def attention_stages(q, k_cache, v_cache, block_table, seq_lens, q_lens, scale, window,

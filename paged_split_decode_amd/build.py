@@ -25,7 +25,7 @@ ARCH = "gfx950"
 
 SOURCES = ["pda_api.hip", "pda_combine.hip", "pda_decode_f16.hip",
            "pda_decode_fp8.hip", "pda_decode_i8.hip", "pda_writer.hip", "pda_prefill.hip",
-           "pda_noalloc.hip"]
+           "pda_noalloc.hip", "pda_probe.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

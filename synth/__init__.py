@@ -16,4 +16,7 @@ from .workloads import (  # noqa: F401
     WriteCase,
     make_write_case,
     visible_pairs,
+    workload_lengths,
+    workload_algorithmic_bytes,
+    workload_visible_pairs,
 )

@@ -314,6 +314,33 @@ def visible_keys_of_sequence(L: int, Q: int, window: int) -> int:
     return max(0, L - lo)
 
 
+def workload_lengths(w: Workload) -> np.ndarray:
+    """The seeded sequence lengths of a workload, as make_case draws them
+    (the first draw of its generator), without building the pool."""
+    return _seq_lens(w, np.random.default_rng(w.seed))
+
+
+def workload_algorithmic_bytes(w: Workload) -> int:
+    """algorithmic_bytes of the case make_case(w) builds, from the lengths
+    alone (no pool)."""
+    e = 2 if w.kv_dtype == "f16" else 1
+    keys = sum(visible_keys_of_sequence(int(L), w.q_len, w.window) for L in workload_lengths(w))
+    return keys * w.num_kv_heads * w.head_dim * e * 2 + w.batch * w.q_len * w.num_q_heads * w.head_dim * 4
+
+
+def workload_visible_pairs(w: Workload) -> int:
+    """visible_pairs of the case make_case(w) builds, from the lengths alone."""
+    total = 0
+    for L in workload_lengths(w).tolist():
+        for i in range(w.q_len):
+            p = int(L) - w.q_len + i
+            if p < 0:
+                continue
+            lo = max(0, p - w.window + 1) if w.window > 0 else 0
+            total += p - lo + 1
+    return total * w.num_q_heads
+
+
 def algorithmic_bytes(case: Case) -> int:
     """Bytes one call must move: every visible key of K and V once, plus q
     and out (fp16). Scales, block table and split partials are excluded."""

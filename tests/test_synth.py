@@ -66,3 +66,15 @@ def test_unit_subcase_identity_table():
     assert u["k_cache"].shape == (13, 16, 1, 128)
     assert u["block_table"].tolist() == [list(range(13))]
     np.testing.assert_array_equal(u["q"], c.q[2:3, 2:4].numpy())
+
+
+def test_workload_sizes_without_a_pool():
+    """The pool-free byte and pair counts equal those of the built case."""
+    from synth import (visible_pairs, workload_algorithmic_bytes, workload_lengths,
+                       workload_visible_pairs)
+    for w in (WORKLOADS["tiny_d128"], WORKLOADS["verify_q3_d128_b32"].with_(ragged_max=900),
+              WORKLOADS["gqa6_d256_l16384"].with_(batch=2, seq_len=700, window=300)):
+        c = make_case(w)
+        assert workload_lengths(w).tolist() == c.seq_lens_host.tolist()
+        assert workload_algorithmic_bytes(w) == algorithmic_bytes(c)
+        assert workload_visible_pairs(w) == visible_pairs(c)
