@@ -129,8 +129,12 @@ def workload_key(workload: str, over: dict, kernel: str = "auto") -> str:
     """Name of a workload with the command line's overrides (batch, window,
     split count) and, for the vector kernel family, that family, as profiles/
     files are keyed."""
-    tags = {"batch": "b", "window": "w", "num_splits": "s"}
+    tags = {"batch": "b", "window": "w", "num_splits": "s", "page_size": "p"}
     key = workload + "".join(f"_{tags[k]}{v}" for k, v in sorted(over.items()) if k in tags)
+    if over.get("layout", "NHD") != "NHD":
+        key += "_" + over["layout"].lower()
+    if over.get("identity_table"):
+        key += "_identity"
     return key + ("_vector" if kernel == "vector" else "")
 
 
@@ -427,17 +431,16 @@ def time_oracle_units(case, units, threads: int, repeats: int = 1) -> float:
 
 
 # Oracle timings per workload: (workload, overrides, units timed (None: all),
-# repeats, also with one thread). The two large quantized workloads are timed
-# on 64 of their 256 units spread over the batch (whole-call time scaled by
-# units: every unit of those has the same length).
+# repeats, also with one thread). Every workload is timed whole (all its
+# (sequence, KV head) units); a sample would scale the time by units.
 CPU_CONFIGS = [
     ("tiny_d128", {}, None, 5, True),
     ("gqa4_d128_b8_l4096", {}, None, 3, True),
     ("gqa6_d256_l16384", dict(batch=32), None, 1, False),
     ("gqa6_d256_l16384", dict(batch=32, window=4096), None, 1, False),
     ("verify_q3_d128_b32", {}, None, 1, False),
-    ("quant_fp8_d256_b64_l32768", {}, 64, 1, False),
-    ("quant_int8_d256_b64_l32768", {}, 64, 1, False),
+    ("quant_fp8_d256_b64_l32768", {}, None, 1, False),
+    ("quant_int8_d256_b64_l32768", {}, None, 1, False),
 ]
 
 
@@ -486,9 +489,8 @@ def cpu_baseline(device, gpu_us: dict, headline_case=None):
             torch.cuda.empty_cache()
     return {"value": head["GB_s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{head['units_timed']} of the {head['units']} (sequence, KV head) units of "
-                      f"{HEADLINE}, spread over the batch, on {threads} host threads (one BLAS "
-                      f"thread each); whole-call time scaled by units "
-                      f"({head['wall_s']} s measured)",
+                      f"{HEADLINE} (one whole call), on {threads} host threads (one BLAS thread "
+                      f"each): {head['wall_s']} s",
             "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(), "per_workload": per}
 
 
@@ -505,7 +507,7 @@ def measure_probe(device, steps: int = 20):
     buf.fill_(1)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     best, rows = None, []
-    for per_cu in (4, 8, 16, 32):
+    for per_cu in (4, 8, 16, 32, 64):
         wg = n_cu * per_cu
         sink = torch.zeros(wg, dtype=torch.int32, device=device)
         for _ in range(3):
