@@ -74,6 +74,28 @@ def test_writer_every_fp16_value(kv, scale):
     assert_cache_equal(c, h)
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
+@pytest.mark.parametrize("scale", [1.0 / 3.0, 0.1, 0.0123, 7.7e-4, 2.9e-3])
+def test_writer_every_fp16_value_inexact_scales(kv, scale):
+    """Every fp16 value again at scales whose quotients are rarely exact: the
+    writer first takes x * (1 / scale) and falls back to the IEEE division
+    only where the codes at the two ends of a small bracket around that
+    product differ; many values land next to a rounding boundary here."""
+    test_writer_every_fp16_value(kv, float(np.float32(scale)))
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
+@pytest.mark.parametrize("Hkv,D,layout", [(16, 256, "NHD"), (32, 128, "HND"), (3, 1000, "NHD")])
+def test_writer_wide_tokens(kv, Hkv, D, layout):
+    """Tokens of more than 256 16-byte chunks (all heads of K): a token takes
+    several workgroups."""
+    c = make_write_case(45, Hkv, D, 16, num_pages=8, kv_dtype=kv, seed=Hkv + D, device=DEV,
+                        layout=layout)
+    h = c.host()
+    run_writer(c)
+    assert_cache_equal(c, h)
+
+
 def test_writer_no_tokens_is_a_no_op():
     c = make_write_case(0, 2, 128, 16, num_pages=4, kv_dtype="fp8_e4m3", seed=1, device=DEV)
     before = c.k_cache.clone()
