@@ -85,9 +85,25 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   constexpr bool PAIR = D == 256 && WAVES == 8;
   const int rg = PAIR ? (wave & 3) : wave;  // row block
   const int dh = PAIR ? (wave >> 2) : 0;    // output dim half
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int blk = gridDim.x - 1 - blockIdx.x;  // the most keys first
+  // Workgroup -> (token block, KV head, sequence), XCD-aware: the dispatcher
+  // hands workgroups to the 8 XCDs in turn (id % 8), and each XCD has its own
+  // L2. The token blocks of one (sequence, KV head) read the same keys, so
+  // they should run on one XCD at about the same time: XCD x takes a
+  // contiguous run of logical indices (token block fastest), in dispatch
+  // order. Within a (sequence, KV head) the blocks with the most keys go
+  // first.
+  int g, b, blk;
+  {
+    const uint32_t nx = gridDim.x, ny = gridDim.y;
+    const uint32_t n = nx * ny * gridDim.z;
+    const uint32_t p = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const uint32_t xcd = p & 7u, k = p >> 3;
+    const uint32_t lg = xcd * (n >> 3) + min(xcd, n & 7u) + k;
+    const uint32_t rest = lg / nx;
+    blk = (int)(nx - 1 - (lg - rest * nx));
+    g = (int)(rest % ny);
+    b = (int)(rest / ny);
+  }
   const int G = a.group;
   const int Hq = a.num_q_heads;
   const int BQ = a.rows / G;                   // tokens per workgroup
