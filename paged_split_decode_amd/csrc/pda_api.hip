@@ -239,7 +239,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
       return fail(PDA_ERR_UNSUPPORTED, "the prefill kernel runs one split (num_splits 0 or 1)");
     const int G = d->num_q_heads / d->num_kv_heads;
     const int waves = pda::prefill_waves(d->head_dim, d->max_q_len,
-                                         (int64_t)d->max_pages_per_seq * d->page_size);
+                                         (int64_t)d->max_pages_per_seq * d->page_size, G);
     const int bq = 32 * (d->head_dim == 256 ? waves / 2 : waves) / G;  // tokens per workgroup
     p->rows = bq * G;                      // rows per workgroup
     p->row_tiles = (d->max_q_len + bq - 1) / bq;  // grid x: token blocks

@@ -43,16 +43,18 @@ def test_prefill_parity(kv, D, G):
 
 
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
-@pytest.mark.parametrize("table_pad", [1, 200])
-def test_prefill_both_workgroup_shapes(kv, table_pad):
+@pytest.mark.parametrize("table_pad,G", [(1, 1), (200, 1), (1, 4)])
+def test_prefill_both_workgroup_shapes(kv, table_pad, G):
     # The same batch through a tight block table (capacity 320 keys < 4 x 300
-    # new tokens: 4-wave workgroups) and a roomy one (3504 keys: 8-wave
-    # workgroups at D=128, with two steps of loads in flight).
+    # new tokens) with 300 query rows per KV head: 4-wave workgroups; through
+    # a roomy table (3504 keys) or with 1200 rows per KV head: 8-wave
+    # workgroups at D=128, with two steps of loads in flight.
     c = _ragged(77, q_lens=[300, 61, 190], ctx=[0, 40, 10], kv_dtype=kv, table_pad=table_pad,
-                num_q_heads=16, num_kv_heads=4)
+                num_q_heads=4 * G, num_kv_heads=4)
     cap = c.block_table.shape[1] * c.workload.page_size
     assert (4 * 300 <= cap) == (table_pad == 200)
-    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv, f"prefill pad={table_pad} {kv}")
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), kv,
+                  f"prefill pad={table_pad} G={G} {kv}")
 
 
 @pytest.mark.parametrize("D", [128, 256])
@@ -128,3 +130,25 @@ def sampled_tokens(c, n_per_seq, seed):
 def test_prefill_workloads_sampled(name):
     c = make_case(WORKLOADS[name], device=DEV)
     sampled_tokens(c, 12, seed=len(name))
+
+
+@pytest.mark.parametrize("pattern", ["rising", "zigzag", "window_edge"])
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_score_ramps_move_the_maximum(pattern, D):
+    """Scores shaped so that the running maximum of a row jumps by more than
+    the lazy reference's slack (8, base 2) between the two 32-key halves of a
+    64-key step and across steps: rising over the sequence (about 16 base-2
+    units per 32 keys), alternating per 16-key tile, and, under a window, the
+    first 3 keys of every 32 scoring low. The rescale of o and l must cover
+    every weight not yet multiplied into o."""
+    import dataclasses
+    from tests.test_gpu_parity import _shape_scores
+    W = 70 if pattern == "window_edge" else 0
+    c = _ragged(211 + D, q_lens=[150, 70], ctx=[400, 30], window=W, num_q_heads=16,
+                num_kv_heads=4, head_dim=D)
+    top = 150.0 / (0.25 * D / np.sqrt(D))
+    fn = {"rising": lambda j, L: top * j / L,
+          "zigzag": lambda j, L: top * ((j // 16) % 2) * (0.5 + 0.5 * j / L),
+          "window_edge": lambda j, L: top * (0.2 if (j % 32) < 3 else 1.0) * (j / L)}[pattern]
+    _shape_scores(c, fn)
+    assert_parity(run_gpu(c, num_splits=1), oracle_full(c), "f16", f"prefill {pattern} D={D}")
