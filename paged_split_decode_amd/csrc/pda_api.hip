@@ -246,7 +246,7 @@ pda_status make_plan(const pda_decode_dims* d, int32_t window, int32_t num_split
     p->matrix = 1;
     p->splits = 1;
     p->threads = 64 * waves;
-    p->lds = pda::prefill_lds_bytes(d->head_dim);
+    p->lds = pda::prefill_lds_bytes(d->head_dim, kv_kind(d->kv_dtype), waves);
     p->wave_lds = 0;
     p->rows_per_wave = 32;
     p->row_groups = 4;

@@ -141,25 +141,34 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
   return (size_t)waves * rows_per_wave * (head_dim + 2) * sizeof(float);
 }
 
-// Long-query (prefill) kernel: 32 (token, head) rows per wave; K/V staged
-// through LDS prefill_tiles(D) 16-key tiles at a time, in two buffers of fp16
-// rows (K: D + 8 halves, V: D + 32). A workgroup has 8 waves at D=128 when
-// the keys before the new tokens are long (at least 3 times as many as the
-// new tokens, from the table's capacity) or a KV head has at least 512 query
-// rows: each thread then stages half as much of a step, so two steps of
-// loads fit in flight, and a staged key serves twice the rows (with the
-// token blocks of a sequence on one XCD, 8-wave workgroups measured 3.7%
-// faster than two 4-wave ones per CU on a fresh prefill of 4 x 2048 tokens).
-// Fewer rows take 4 waves (128 rows per workgroup). At D=256 a workgroup has 8 waves
-// in pairs that share 32 rows and split the output dims (128 rows per
-// workgroup).
+// Long-query (prefill) kernel: 32 (token, head) rows per wave; K and V go
+// through LDS 64 keys (four 16-key tiles) per step, as fp16 in the order the
+// matrix instructions read them. A workgroup has 8 waves at D=128 when the
+// keys before the new tokens are long (at least 3 times as many as the new
+// tokens, from the table's capacity) or a KV head has at least 512 query
+// rows: a staged key then serves twice the rows (with the token blocks of a
+// sequence on one XCD, 8-wave workgroups measured 3.7% faster than two 4-wave
+// ones per CU on a fresh prefill of 4 x 2048 tokens). Fewer rows take 4 waves
+// (128 rows per workgroup). At D=256 a workgroup has 8 waves in pairs that
+// share 32 rows and split the output dims (128 rows per workgroup).
 inline int prefill_waves(int head_dim, int max_q_len, int64_t key_capacity, int group) {
   if (head_dim == 256) return 8;
   return (4 * (int64_t)max_q_len <= key_capacity || (int64_t)group * max_q_len >= 512) ? 8 : 4;
 }
 constexpr int prefill_tiles(int) { return 4; }  // 64 keys per LDS step (two halves of 32)
-inline size_t prefill_lds_bytes(int head_dim) {
-  return (size_t)2 * prefill_tiles(head_dim) * 16 * ((head_dim + 8) + (head_dim + 32)) * 2;
+// Bytes of one step of K and V in LDS (fp16, unpadded).
+constexpr int prefill_step_bytes(int head_dim) {
+  return 2 * prefill_tiles(head_dim) * 16 * head_dim * 2;
+}
+// Step buffers in LDS: fp16 caches load straight into LDS, three steps deep
+// for 8-wave workgroups at D=128 (96 KB, one workgroup per CU) and two
+// otherwise (64 KB at D=128: two 4-wave workgroups per CU; 128 KB at D=256);
+// 1-byte codes are converted in registers and stored into two buffers.
+constexpr int prefill_buffers(int head_dim, int kv_kind, int waves) {
+  return kv_kind == kKvF16 && head_dim == 128 && waves == 8 ? 3 : 2;
+}
+inline size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
+  return (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim);
 }
 hipError_t launch_prefill_f16(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);

@@ -41,37 +41,46 @@ struct IntC {
   static constexpr int value = I;
 };
 
+// LDS allows one workgroup per CU (two at D=128 with 4 waves), so at most two
+// waves share a SIMD; the compiler is told so, and keeps loads ahead in
+// registers instead of trimming them for a third wave that never comes.
 template <int D, int KV, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, (D == 128 || WAVES == 8) ? 2 : 1)
+__attribute__((amdgpu_waves_per_eu(1, (D == 128 || WAVES == 8) ? 2 : 1)))
 pda_prefill_mfma_kernel(const DecodeArgs a) {
-  // LDS row strides (halves): K rows D + 8 (4 dwords mod 64: the 16 rows of a
-  // 128-bit fragment read pass hit disjoint banks), V rows D + 32 (16 dwords
-  // mod 64: a 32-lane pass of the transposing reads covers 4 rows of 64
-  // bytes, on disjoint banks; with D + 16 they overlapped 2-way).
-  constexpr int LRK = D + 8;
-  constexpr int LRV = D + 32;
-  constexpr int TILEK = 16 * LRK;  // halves of one 16-key K tile
-  constexpr int TILEV = 16 * LRV;
-  constexpr int KT = prefill_tiles(D);
-  constexpr int EB = KV == kKvF16 ? 2 : 1;
-  constexpr int PIECES = D * EB / 16;                // 16-byte pieces of a cache row
-  constexpr int NPIECE = 2 * KT * 16 * PIECES;      // K and V pieces of one step
+  // LDS holds K and V of 64-key steps as fp16, each in the order the matrix
+  // instructions read it, so that every read is a contiguous run with no
+  // bank conflict and no padding:
+  //  - K of a 32-key half h and k-step t (16 dims): one 1 KB block whose
+  //    16-byte slot l holds key 32 h + l % 32, dims 16 t + 8 (l / 32) .. + 7,
+  //    which is lane l's A fragment of v_mfma_f32_32x32x16_f16;
+  //  - V of a 16-key tile and 32 dims (group dg): one 1 KB block whose slot s
+  //    holds key 8 (s / 32) + 4 (s / 16 % 2) + s / 4 % 4 of the tile, dims
+  //    32 dg + 8 (s % 4) .. + 7; each 32-lane pass of the transposing reads
+  //    then covers 256 contiguous bytes.
+  // fp16 caches go to LDS by direct 16-byte loads (global_load_lds_dwordx4:
+  // lane l of a wave's load lands at 16 l bytes from the block start), NBUF
+  // step buffers deep with no staging registers; 1-byte codes go through
+  // registers (NREG sets) to be converted to fp16 on the way.
+  constexpr int KT = prefill_tiles(D);  // 16-key tiles per step
+  constexpr int NK = D / 16;            // QK k-steps = K blocks of a half
+  constexpr int NDV = D / 32;           // V blocks of a tile
+  constexpr int KH_BYTES = NK * 1024;   // K of one 32-key half
+  constexpr int VT_BYTES = NDV * 1024;  // V of one 16-key tile
+  constexpr int BUF_BYTES = 2 * KH_BYTES + KT * VT_BYTES;
+  static_assert(BUF_BYTES == prefill_step_bytes(D), "host and kernel agree on the step size");
+  constexpr int NBUF = prefill_buffers(D, KV, WAVES);
+  constexpr bool DMA = KV == kKvF16;
   constexpr int NTHREADS = 64 * WAVES;
-  constexpr int LOADS = NPIECE / NTHREADS;           // per thread and step
-  // Steps whose loads are in flight in registers (each in its own set): the
-  // loads of step s + NREG + 1 are issued when step s ends and go to LDS when
-  // step s + NREG ends.
-#ifdef PDA_PREFILL_NREG8
-  constexpr int NREG = WAVES == 8 ? PDA_PREFILL_NREG8 : 1;  // tuning override
-#else
-  constexpr int NREG = (WAVES == 8 && D == 128) ? 2 : 1;
-#endif
-  static_assert(NREG >= 1 && NREG <= 3, "one to three register sets");
+  constexpr int CHUNKS = 2 * KT * 16 * (D / 16);     // 16-byte code chunks of a step (1-byte KV)
+  constexpr int LOADS = DMA ? 1 : CHUNKS / NTHREADS;  // per thread and step
+  // Steps whose loads are in flight in registers (1-byte KV, each in its own
+  // set): the loads of step s + NREG + 1 are issued when step s ends and go
+  // to LDS when step s + NREG ends.
+  constexpr int NREG = DMA ? 1 : (WAVES == 8 && D == 128) ? 2 : 1;
+  static_assert(DMA || (NBUF == 2 && CHUNKS % NTHREADS == 0), "register staging: two buffers");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
-  _Float16* lds = reinterpret_cast<_Float16*>(lds_raw);
-  // buffer x: K tiles at lds + x * KT * (TILEK + TILEV), V tiles KT * TILEK later
-  constexpr int BUF = KT * (TILEK + TILEV);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,35 +166,130 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     return (size_t)bt[u >> tshift] * a.page_bytes + (size_t)((u & tmask) * kPageSize) * key_stride;
   };
 
-  // Staging: thread piece p = tid + NTHREADS l (< NPIECE) is K or V (kv),
-  // tile tt of the step, key row, 16-byte piece; all of that is fixed per
-  // thread, so its byte offset within a tile and its LDS position are computed
-  // once. Each step only moves the (scalar) tile bases.
-  static_assert(NPIECE % NTHREADS == 0, "every thread stages whole pieces");
+  // Tile tt of step `step`; tiles past the workgroup's range are read from
+  // its last tile (in bounds; all their keys are masked).
+  const int last_tile = t_lo + n_tiles - 1;
+  auto tile_at = [&](int step, int tt) __attribute__((always_inline)) {
+    return tile_base(min(t_lo + step * KT + tt, last_tile));
+  };
+  const uint32_t lds_u32 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds_raw;
+  // One direct 16-byte load per lane into LDS at byte dst + 16 lane (dst
+  // wave-uniform, in M0; one wait state after M0 is written). Written as asm
+  // so that the compiler's wait insertion does not track an LDS write in
+  // flight: it would make LDS reads wait for every outstanding load,
+  // including those of the steps ahead. The waits this pipeline needs are
+  // explicit (wait_vm before each barrier).
+  auto lds_load16 = [](const uint8_t* src, uint32_t dst) __attribute__((always_inline)) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(dst)));
+  };
+
+  // fp16 caches, direct loads: waves [0, WAVES / 2) load K, the others V, in
+  // whole 1 KB blocks, PER per wave and step; a K wave's blocks lie in one
+  // half, a V wave's cover whole tiles. Each lane's byte offset within a
+  // tile is fixed: K, key lane % 16 of the lane's tile (lane / 16 % 2 of the
+  // half) at dims 8 (lane / 32) ..; V, the key row of slot `lane` at dims
+  // 8 (lane % 4) ...
+  constexpr int PER = 2 * NK / (WAVES / 2);
+  static_assert(PER == KT * NDV / (WAVES / 2), "K and V waves load as many blocks");
+  static_assert(NK % PER == 0 && PER % NDV == 0, "a wave's blocks: one half, or whole tiles");
+  const bool kwave = wave < WAVES / 2;
+  const int wk = kwave ? wave : wave - WAVES / 2;
+  const int vrow = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 2) & 3);
+  const uint32_t lane_off = kwave ? (uint32_t)(lane & 15) * key_stride + head_off + 16u * (lane >> 5)
+                                  : (uint32_t)vrow * key_stride + head_off + 16u * (lane & 3);
+  auto dma_step = [&](int step, int buf) __attribute__((always_inline)) {
+    const uint32_t dst0 = lds_u32 + (uint32_t)(buf * BUF_BYTES);
+    if (kwave) {
+      const int h = (wk * PER) / NK, t0 = (wk * PER) % NK;
+      const size_t b0 = tile_at(step, 2 * h), b1 = tile_at(step, 2 * h + 1);
+      const uint8_t* src = a.k + ((lane & 16) ? b1 : b0) + lane_off + 32 * t0;
+      const uint32_t dst = dst0 + (uint32_t)(h * KH_BYTES + t0 * 1024);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) lds_load16(src + 32 * i, dst + 1024u * i);
+    } else {
+#pragma unroll
+      for (int q = 0; q < PER / NDV; ++q) {
+        const int tt = (wk * PER) / NDV + q;
+        const uint8_t* src = a.v + tile_at(step, tt) + lane_off;
+        const uint32_t dst = dst0 + (uint32_t)(2 * KH_BYTES + tt * VT_BYTES);
+#pragma unroll
+        for (int dg = 0; dg < NDV; ++dg) lds_load16(src + 64 * dg, dst + 1024u * dg);
+      }
+    }
+  };
+  // After a V wave's loads of a step have landed: V slots of keys at or past
+  // the sequence's end hold whatever the page has there (a weight 0 times a
+  // NaN would spoil P.V), so they become zeros. (For a tile read in place of
+  // one past the range, keys counted at the tile's own place are past every
+  // slot it copies that lies past the end.) K there only meets masked scores.
+  auto dma_zero_tail = [&](int step, int buf) __attribute__((always_inline)) {
+    const int key_base = (t_lo + step * KT) * kPageSize;
+    if (kwave || key_base + KT * kPageSize <= L) return;
+    uint8_t* const dst0 = lds_raw + buf * BUF_BYTES + 2 * KH_BYTES;
+#pragma unroll
+    for (int q = 0; q < PER / NDV; ++q) {
+      const int tt = (wk * PER) / NDV + q;
+      if (key_base + tt * kPageSize + vrow >= L) {
+#pragma unroll
+        for (int dg = 0; dg < NDV; ++dg)
+          *reinterpret_cast<u32x4*>(dst0 + tt * VT_BYTES + dg * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // s_waitcnt with vmcnt(VM) and lgkmcnt(0) (expcnt untouched).
+  auto wait_vm = [](auto vm_c) __attribute__((always_inline)) {
+    constexpr int VM = decltype(vm_c)::value;
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+  };
+  // Workgroup barrier without a memory fence (the waits before it are
+  // explicit); the empty asm statements keep the compiler from moving memory
+  // accesses across it.
+  auto barrier = []() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // 1-byte codes, register staging: chunk c = tid + NTHREADS l of a step is
+  // K or V (kv), key row r64 of the step's 64, dims 16 j .. + 15; its 16
+  // codes become two fp16 slots (K: k-step j of the row's half, slot
+  // r64 % 32 and that + 32; V: block j / 2 of the row's tile, slots s and
+  // s + 1). All of that is fixed per thread; each step only moves the
+  // (scalar) tile bases.
   uint32_t src_off[LOADS];
-  uint32_t lds_off[LOADS];  // in halves
+  uint32_t lds_off[LOADS], lds_off2[LOADS];
   int row_of[LOADS], tt_of[LOADS];
   bool is_v[LOADS];
+  if constexpr (!DMA) {
 #pragma unroll
-  for (int l = 0; l < LOADS; ++l) {
-    const int p = tid + NTHREADS * l;
-    const int kv = p / (KT * 16 * PIECES);
-    const int rem = p - kv * (KT * 16 * PIECES);
-    tt_of[l] = rem / (16 * PIECES);
-    row_of[l] = (rem / PIECES) % 16;
-    const int piece = rem % PIECES;
-    is_v[l] = kv != 0;
-    src_off[l] = (uint32_t)row_of[l] * key_stride + head_off + 16u * piece;
-    lds_off[l] = (uint32_t)(kv ? KT * TILEK + tt_of[l] * TILEV + row_of[l] * LRV
-                               : tt_of[l] * TILEK + row_of[l] * LRK) + piece * (16 / EB);
+    for (int l = 0; l < LOADS; ++l) {
+      const int c = tid + NTHREADS * l;
+      const int kv = c / (CHUNKS / 2);
+      const int rem = c - kv * (CHUNKS / 2);
+      const int r64 = rem / (D / 16), j = rem % (D / 16);
+      tt_of[l] = r64 >> 4;
+      row_of[l] = r64 & 15;
+      is_v[l] = kv != 0;
+      src_off[l] = (uint32_t)row_of[l] * key_stride + head_off + 16u * j;
+      if (!kv) {
+        lds_off[l] = (uint32_t)((r64 >> 5) * KH_BYTES + j * 1024 + 16 * (r64 & 31));
+        lds_off2[l] = lds_off[l] + 512;
+      } else {
+        const int r = r64 & 15;
+        const int slot = 32 * (r >> 3) + 16 * ((r >> 2) & 1) + 4 * (r & 3) + 2 * (j & 1);
+        lds_off[l] = (uint32_t)(2 * KH_BYTES + tt_of[l] * VT_BYTES + (j >> 1) * 1024 + 16 * slot);
+        lds_off2[l] = lds_off[l] + 16;
+      }
+    }
   }
   uint32_t stage_regs[NREG][LOADS][4];
   auto stage_load = [&](int step, auto set_c) __attribute__((always_inline)) {
     auto& stage = stage_regs[decltype(set_c)::value];
-    const int u0 = t_lo + step * KT;
     size_t base[KT];
 #pragma unroll
-    for (int tt = 0; tt < KT; ++tt) base[tt] = tile_base(min(u0 + tt, t_lo + n_tiles - 1));
+    for (int tt = 0; tt < KT; ++tt) base[tt] = tile_at(step, tt);
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) {
       const uint8_t* src = (is_v[l] ? a.v : a.k) + base[tt_of[l]] + src_off[l];
@@ -197,10 +301,10 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   auto stage_store = [&](int step, int buf, auto set_c) __attribute__((always_inline)) {
     auto& stage = stage_regs[decltype(set_c)::value];
     const int j0 = (t_lo + step * KT) * kPageSize;
-    _Float16* dst0 = lds + (size_t)buf * BUF;
+    uint8_t* const dst0 = lds_raw + buf * BUF_BYTES;
     // Slots past the sequence (arbitrary contents), and tiles past this
-    // workgroup's range (staged from a clamped tile), become zeros. Only a
-    // step that reaches past either needs the per-slot test (wave-uniform).
+    // workgroup's range, become zeros. Only a step that reaches past either
+    // needs the per-slot test (wave-uniform).
     auto put = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
       for (int l = 0; l < LOADS; ++l) {
@@ -209,24 +313,16 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
           const int u = t_lo + step * KT + tt_of[l];
           live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
         }
-        _Float16* dst = dst0 + lds_off[l];
-        if constexpr (KV == kKvF16) {
-          u32x4 w;
+        h2_t hv[8];
+        to_pairs<KV>(stage[l], hv);
+        u32x4 w0, w1;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = live ? stage[l][e] : 0u;
-          *reinterpret_cast<u32x4*>(dst) = w;
-        } else {
-          h2_t hv[8];
-          to_pairs<KV>(stage[l], hv);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              w[e] = live ? __builtin_bit_cast(uint32_t, hv[4 * hh + e]) : 0u;
-            *reinterpret_cast<u32x4*>(dst + 8 * hh) = w;
-          }
+        for (int e = 0; e < 4; ++e) {
+          w0[e] = live ? __builtin_bit_cast(uint32_t, hv[e]) : 0u;
+          w1[e] = live ? __builtin_bit_cast(uint32_t, hv[4 + e]) : 0u;
         }
+        *reinterpret_cast<u32x4*>(dst0 + lds_off[l]) = w0;
+        *reinterpret_cast<u32x4*>(dst0 + lds_off2[l]) = w1;
       }
     };
     if ((step + 1) * KT <= n_tiles && j0 + KT * kPageSize <= L)
@@ -253,7 +349,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
   const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
   qk = fabsf(qk);
-  constexpr int NK = D / 16;   // QK k-steps
   constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
   const int dcol = dh * (D / 2);
   h8_t qb[NK];
@@ -279,13 +374,19 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 
   typedef short s4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4_t lds_s4_t;
-  auto tr_read = [&](const _Float16* src) __attribute__((always_inline)) {
+  auto tr_read = [&](const uint8_t* src) __attribute__((always_inline)) {
     return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s4_t*)(__attribute__((address_space(3))) _Float16*)src));
+        (lds_s4_t*)(__attribute__((address_space(3))) uint8_t*)src));
   };
   const int q16 = lane >> 4, i16 = lane & 15;  // 16-lane group and lane in it
+  // The transposing V reads: lane l takes 4 dims (8 bytes) of key row
+  // 4 hh + i16 / 4 (+ 8 for the upper 8 keys of a k-step) at dims
+  // 16 (q16 % 2) + 4 (i16 % 4) of a 32-dim group: slot
+  // 16 hh + 4 (i16 / 4) + 2 (q16 % 2) + (i16 % 4) / 2 of the group's block,
+  // second 8 bytes when i16 is odd.
+  const uint32_t v_lane = 16u * (16 * hh + 4 * (i16 >> 2) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
+                          8u * (i16 & 1);
 
-  // One step of 32 keys (K rows kb[0..31], V rows vb[0..31] in LDS).
   // Whether this wave has work on the 32 keys from key0 (wave-uniform).
   auto active = [&](int key0) { return hi_max >= 0 && key0 <= hi_max && key0 + 31 >= lo_min; };
   // S^T[key][row] of 32 keys: lane l gets row rr, keys 8 j + 4 hh + i in
@@ -293,10 +394,10 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // (scores2), with each k-step's K fragments read one step ahead. (At D=256,
   // one wave per SIMD, this order measured 0.8% faster than computing each
   // half's scores just before its softmax; its extra registers go to AGPRs.)
-  auto frag = [&](const _Float16* kb, int t) __attribute__((always_inline)) {
-    return *reinterpret_cast<const h8_t*>(kb + rr * LRK + 16 * t + 8 * hh);
+  auto frag = [&](const uint8_t* kh, int t) __attribute__((always_inline)) {
+    return *reinterpret_cast<const h8_t*>(kh + 1024 * t + 16 * lane);
   };
-  auto scores2 = [&](const _Float16* kb0, const _Float16* kb1, f16v_t& s0, f16v_t& s1) __attribute__((always_inline)) {
+  auto scores2 = [&](const uint8_t* kb0, const uint8_t* kb1, f16v_t& s0, f16v_t& s1) __attribute__((always_inline)) {
     h8_t k0 = frag(kb0, 0), k1 = frag(kb1, 0);
     s0 = f16v_t{};
     s1 = f16v_t{};
@@ -313,27 +414,38 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       k1 = n1;
     }
   };
-  // Softmax and P.V of 32 keys from key0 whose scores are st.
-  auto softmax_pv = [&](f16v_t st, const _Float16* vb, int key0) __attribute__((always_inline)) {
-    const bool full = key0 >= lo_max && key0 + 31 <= hi_min;
-    uint32_t vis = 0xFFFFu;  // bit 4 j + i: key key0 + 8 j + 4 hh + i visible to row rr
-    float mt;
-    if (full) {
-      float a0 = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
-      float a1 = fmaxf(fmaxf(st[4], st[5]), fmaxf(st[6], st[7]));
-      float a2 = fmaxf(fmaxf(st[8], st[9]), fmaxf(st[10], st[11]));
-      float a3 = fmaxf(fmaxf(st[12], st[13]), fmaxf(st[14], st[15]));
-      mt = fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
-    } else {
-      vis = 0u;
-      mt = -INFINITY;
+  // Softmax and P.V of the 64 keys from key0 whose scores are st[0] (keys
+  // key0 ..) and st[1] (key0 + 32 ..). Where some row of the wave sees only
+  // part of the keys (a uniform test), the scores of keys a row does not see
+  // become -inf first: they leave the maximum alone and get weight
+  // exp2(-inf) = 0. Every other step runs no per-key test. One maximum and
+  // one rescale test cover both halves, so the weights and P.V of both run in
+  // one block (the exponentials of one half can issue under the other's
+  // matrix instructions).
+  auto softmax_pv = [&](f16v_t (&st)[2], const uint8_t* vb, int key0) __attribute__((always_inline)) {
+    if (!(key0 >= lo_max && key0 + 63 <= hi_min)) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = key0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const bool ok = j >= my_lo && j <= my_hi;
-        vis |= ok ? 1u << v : 0u;
-        mt = fmaxf(mt, ok ? st[v] : -INFINITY);
+      for (int h = 0; h < 2; ++h) {
+        // lane's key of slot v: key0 + 32 h + 8 (v / 4) + 4 hh + v % 4
+        const int d_lo = my_lo - key0 - 32 * h - 4 * hh, d_hi = my_hi - key0 - 32 * h - 4 * hh;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 8 * (v >> 2) + (v & 3);
+          st[h][v] = (c >= d_lo && c <= d_hi) ? st[h][v] : -INFINITY;
+        }
       }
+    }
+    float mt;
+    {
+      float a[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          a[4 * h + q] = fmaxf(fmaxf(st[h][4 * q], st[h][4 * q + 1]),
+                               fmaxf(st[h][4 * q + 2], st[h][4 * q + 3]));
+      mt = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+                 fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
     }
     {  // the other half of the row's keys sits in lane l ^ 32
       auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mt),
@@ -349,77 +461,110 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       m = mx;
     }
-    float p[16];
-    if (full) {
+    // O^T[dim][row] += V^T . P^T over four 16-key k-steps. k-step 2 h + ks
+    // takes the lane's keys of half h, j = 2 ks, 2 ks + 1 (slots 8 hh + e:
+    // key 32 h + 16 ks + 4 hh + e, then 32 h + 16 ks + 8 + 4 hh + e); V^T's A
+    // operand uses the same key order: two transposing reads of 4
+    // consecutive key rows at this lane's dim. The denominator adds the same
+    // fp16 weights that P.V multiplies V by (v_dot2 with ones: each fp16
+    // value enters the fp32 sum exactly).
+    const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    h8_t pb[2][2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], qk, -m));
-    } else {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], qk, -m));
-        p[v] = (vis >> v) & 1u ? e : 0.0f;
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[h][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[h][8 * ks + e], qk, -m));
+          pb[h][ks][4 + e] =
+              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[h][8 * ks + 4 + e], qk, -m));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lsum = __builtin_amdgcn_fdot2(h2_t{pb[h][ks][e], pb[h][ks][e + 1]}, one2, lsum, false);
       }
     }
-    // O^T[dim][row] += V^T . P^T over two 16-key k-steps. k-step ks takes the
-    // lane's keys of j = 2 ks, 2 ks + 1 (slots 8 hh + e: key 16 ks + 4 hh + e,
-    // then 16 ks + 8 + 4 hh + e); V^T's A operand uses the same key order:
-    // two transposing reads of 4 consecutive key rows at this lane's dim.
-    // The denominator adds the same fp16 weights that P.V multiplies V by
-    // (v_dot2 with ones: each fp16 value enters the fp32 sum exactly).
-    const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      h8_t pb;
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = (_Float16)p[8 * ks + e];
-        pb[4 + e] = (_Float16)p[8 * ks + 4 + e];
-      }
+      for (int ks = 0; ks < 2; ++ks) {
+        // tile 2 h + ks; its block of dims dcol + 32 dt
+        const uint8_t* vt = vb + (2 * h + ks) * VT_BYTES + (dcol / 32) * 1024 + v_lane;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        lsum = __builtin_amdgcn_fdot2(h2_t{pb[e], pb[e + 1]}, one2, lsum, false);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int col = dcol + 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3);
-        const h4_t lo = tr_read(vb + (16 * ks + 4 * hh + (i16 >> 2)) * LRV + col);
-        const h4_t hi = tr_read(vb + (16 * ks + 8 + 4 * hh + (i16 >> 2)) * LRV + col);
-        const h8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[dt], 0, 0, 0);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const h4_t lo = tr_read(vt + 1024 * dt);
+          const h4_t hi = tr_read(vt + 1024 * dt + 512);
+          const h8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[h][ks], o[dt], 0, 0, 0);
+        }
       }
     }
   };
 
-  if (n_steps > 0) {
+  // One step's compute on LDS buffer buf. A step no row of the wave sees is
+  // skipped. (A half that no row sees still gets scores, from finite LDS
+  // data, when the other half is needed; they are masked to weight 0. The
+  // score registers live only inside the branch that uses them: a value
+  // merged from a path that skips them would be zero-filled every step.)
+  auto compute = [&](int step, int buf) __attribute__((always_inline)) {
+    const uint8_t* kb = lds_raw + buf * BUF_BYTES;
+    const int key0 = (t_lo + step * KT) * kPageSize;
+    if (active(key0) || active(key0 + 32)) {
+      f16v_t st[2];
+      scores2(kb, kb + KH_BYTES, st[0], st[1]);
+      softmax_pv(st, kb + 2 * KH_BYTES, key0);
+    }
+  };
+
+  if constexpr (DMA) {
+    // Step s computes on buffer s % NBUF; its start issues the loads of step
+    // s + NBUF - 1 (that buffer was last read in step s - 1, which every
+    // wave has left at the barrier); its end waits for this wave's loads of
+    // step s + 1 (the PER loads of step s + 2 may stay in flight), zeroes
+    // that step's tail, and meets the other waves at the barrier.
+    static_assert(NBUF == 2 || NBUF == 3, "two or three step buffers");
+    if (n_steps > 0) {
+      dma_step(0, 0);
+      if (NBUF == 3 && n_steps > 1) {
+        dma_step(1, 1);
+        wait_vm(IntC<PER>{});
+      } else {
+        wait_vm(IntC<0>{});
+      }
+      dma_zero_tail(0, 0);
+      wait_vm(IntC<63>{});
+      barrier();
+      int buf = 0;
+      for (int step = 0; step < n_steps; ++step) {
+        const int nb = buf + 1 == NBUF ? 0 : buf + 1;  // buffer of step + 1
+        const int fb = nb + 1 == NBUF ? 0 : nb + 1;    // of step + 2
+        if (step + NBUF - 1 < n_steps) dma_step(step + NBUF - 1, NBUF == 3 ? fb : nb);
+        compute(step, buf);
+        if (step + 1 < n_steps) {
+          if (NBUF == 3 && step + 2 < n_steps)
+            wait_vm(IntC<PER>{});
+          else
+            wait_vm(IntC<0>{});
+          dma_zero_tail(step + 1, nb);
+          wait_vm(IntC<63>{});
+          barrier();
+        }
+        buf = nb;
+      }
+    }
+  } else if (n_steps > 0) {
     stage_load(0, IntC<0>{});
     stage_store(0, 0, IntC<0>{});
     if (n_steps > 1) stage_load(1, IntC<0>{});
     if constexpr (NREG >= 2) {
       if (n_steps > 2) stage_load(2, IntC<1>{});
     }
-    if constexpr (NREG >= 3) {
-      if (n_steps > 3) stage_load(3, IntC<2>{});
-    }
     __syncthreads();
     // Step `step` reads LDS buffer step & 1; register set SET holds step + 1.
     auto step_body = [&](int step, auto set_c) __attribute__((always_inline)) {
       const int buf = step & 1;
-      const _Float16* kb = lds + (size_t)buf * BUF;
-      const _Float16* vb = kb + KT * TILEK;
-      const int key0 = (t_lo + step * KT) * kPageSize;
-      // Both halves' scores first: the second half's softmax can run under
-      // the first half's P.V. (A half that no row of the wave sees still gets
-      // scores, from finite LDS data, when the other half is needed; its
-      // softmax and P.V are skipped.)
-      const bool a0 = active(key0), a1 = active(key0 + 32);
-      // (The score registers live only inside the branch that uses them: a
-      // value merged from a path that skips them would be zero-filled every
-      // step.)
-      if (a0 || a1) {
-        f16v_t st0, st1;
-        scores2(kb, kb + 2 * TILEK, st0, st1);
-        if (a0) softmax_pv(st0, vb, key0);
-        if (a1) softmax_pv(st1, vb + 2 * TILEV, key0 + 32);
-      }
+      compute(step, buf);
       if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1, set_c);
       if (step + 1 + NREG < n_steps) stage_load(step + 1 + NREG, set_c);
       __syncthreads();
@@ -428,9 +573,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       step_body(step, IntC<0>{});
       if constexpr (NREG >= 2) {
         if (step + 1 < n_steps) step_body(step + 1, IntC<1>{});
-      }
-      if constexpr (NREG >= 3) {
-        if (step + 2 < n_steps) step_body(step + 2, IntC<2>{});
       }
     }
   }
