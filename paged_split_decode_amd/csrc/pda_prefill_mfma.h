@@ -120,12 +120,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int Qb = a.q_lens ? a.q_lens[b] : 1;
   const int i0 = blk * BQ;
   if (i0 >= Qb) return;  // the whole workgroup: no barrier is skipped by a part of it
-  int off = b;
-  if (a.q_lens) {
-    int sum = 0;
-    for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
-    off = wave_sum_int(sum);
-  }
   const int pos0 = L - Qb;  // position of token 0
   const int W = a.window;
   auto lo_of = [&](int pos) { return W > 0 ? max(0, pos - W + 1) : 0; };
@@ -139,17 +133,20 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int n_tiles = khi >= 0 ? khi / kPageSize - t_lo + 1 : 0;
   const int n_steps = (n_tiles + KT - 1) / KT;
 
-  // This wave's rows (16 rt + c of its 32): bounds per lane, and wave-uniform
-  // summaries for the skip / unmasked tests.
+  // Wave-uniform summaries of this wave's rows 32 rg .. + 31 for the skip /
+  // unmasked tests: their tokens run from i_a to i_b (rows past the
+  // workgroup's, tokens past the sequence's and negative positions left
+  // out), and the bounds of a token's keys grow with its position.
   int lo_min = 0x7fffffff, lo_max = 0, hi_min = 0x7fffffff, hi_max = -1;
-  for (int r = 32 * rg; r < 32 * rg + 32 && r < a.rows; ++r) {
-    const int i = i0 + r / G;
-    const int pos = pos0 + i;
-    if (i < Qb && pos >= 0) {
-      lo_min = min(lo_min, lo_of(pos));
-      lo_max = max(lo_max, lo_of(pos));
-      hi_min = min(hi_min, pos);
-      hi_max = max(hi_max, pos);
+  {
+    const int r_b = min(32 * rg + 31, a.rows - 1);
+    const int i_a = max(i0 + (32 * rg) / G, -pos0);
+    const int i_b = min(i0 + r_b / G, Qb - 1);
+    if (32 * rg <= r_b && i_a <= i_b) {
+      hi_min = pos0 + i_a;
+      hi_max = pos0 + i_b;
+      lo_min = lo_of(hi_min);
+      lo_max = lo_of(hi_max);
     }
   }
 
@@ -331,6 +328,22 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       put(BoolC<true>{});
   };
 
+  // The first steps' loads go out first: the Q loads and the token offset
+  // below do not hold them up.
+  if constexpr (DMA) {
+    if (n_steps > 0) dma_step(0, 0);
+    if (NBUF == 3 && n_steps > 1) dma_step(1, 1);
+  } else {
+    if (n_steps > 0) stage_load(0, IntC<0>{});
+  }
+  // First token of sequence b in q and out.
+  int off = b;
+  if (a.q_lens) {
+    int sum = 0;
+    for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
+    off = wave_sum_int(sum);
+  }
+
   // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
   // with h = l / 32; B: column l % 32, same k; C: column l % 32, rows
   // 8 j + 4 h + i in element 4 j + i). So lane l works on query row rr = l % 32
@@ -348,20 +361,28 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // k-step t. A negative scale flips q's sign.
   float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
   const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
-  qk = fabsf(qk);
+  // Scores of keys a row does not see are set to -inf before the softmax;
+  // with a zero scale -inf * 0 would be NaN, so a zero multiplier becomes
+  // the smallest normal float: every product with a finite score is then
+  // too small to change exp2 in fp32, and the weights stay exactly 1.
+  qk = fabsf(qk) > 0.0f ? fabsf(qk) : __FLT_MIN__;
   constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
   const int dcol = dh * (D / 2);
   h8_t qb[NK];
   {
+    // (a lane without a row reads its token clamped into the sequence, in
+    // bounds, and keeps zeros)
     const uint8_t* qrow =
-        a.q + ((size_t)(off + my_i) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
+        a.q + ((size_t)(off + min(my_i, Qb - 1)) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
+    u32x4 x[NK];
+#pragma unroll
+    for (int t = 0; t < NK; ++t) x[t] = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
+    const uint32_t keep = my_row ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (my_row) x = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] ^= qflip;
-      qb[t] = __builtin_bit_cast(h8_t, x);
+      for (int e = 0; e < 4; ++e) x[t][e] = (x[t][e] & keep) ^ qflip;
+      qb[t] = __builtin_bit_cast(h8_t, x[t]);
     }
   }
 
@@ -525,13 +546,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     // that step's tail, and meets the other waves at the barrier.
     static_assert(NBUF == 2 || NBUF == 3, "two or three step buffers");
     if (n_steps > 0) {
-      dma_step(0, 0);
-      if (NBUF == 3 && n_steps > 1) {
-        dma_step(1, 1);
+      // (steps 0 and 1 were issued above; Q loads may follow them)
+      if (NBUF == 3 && n_steps > 1)
         wait_vm(IntC<PER>{});
-      } else {
+      else
         wait_vm(IntC<0>{});
-      }
       dma_zero_tail(0, 0);
       wait_vm(IntC<63>{});
       barrier();
@@ -554,7 +573,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       }
     }
   } else if (n_steps > 0) {
-    stage_load(0, IntC<0>{});
     stage_store(0, 0, IntC<0>{});
     if (n_steps > 1) stage_load(1, IntC<0>{});
     if constexpr (NREG >= 2) {
@@ -588,6 +606,9 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   }
   if (my_row) {
     const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
+    // one division per row: o is multiplied by alpha * vs / l (0 for a row
+    // that sees no key)
+    const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
     const size_t hrow = (size_t)(off + my_i) * Hq + g * G + (myr - (myr / G) * G);
     uint16_t* dst = a.out + hrow * D + dcol + 4 * hh;
 #pragma unroll
@@ -596,8 +617,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       for (int j = 0; j < 4; ++j) {
         h4_t y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[e] = lsum > 0.0f ? (_Float16)((o[dt][4 * j + e] * alpha * vs) / lsum) : (_Float16)0.0f;
+        for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[dt][4 * j + e] * f);
         *reinterpret_cast<h4_t*>(dst + 32 * dt + 8 * j) = y;
       }
     }
