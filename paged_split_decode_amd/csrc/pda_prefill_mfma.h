@@ -196,25 +196,32 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int vrow = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 2) & 3);
   const uint32_t lane_off = kwave ? (uint32_t)(lane & 15) * key_stride + head_off + 16u * (lane >> 5)
                                   : (uint32_t)vrow * key_stride + head_off + 16u * (lane & 3);
-  auto dma_step = [&](int step, int buf) __attribute__((always_inline)) {
+  // The tiles a wave loads each step: a K wave tiles ta and ta + 1 (its
+  // half), a V wave tiles ta .. ta + PER / NDV - 1 (at most two). Inside the
+  // step loop their bases come from the block table before the barrier of
+  // the step before, so the scalar loads' latency hides under the barrier.
+  const int ta = kwave ? 2 * ((wk * PER) / NK) : (wk * PER) / NDV;
+  static_assert(PER / NDV <= 2, "a V wave loads at most two tiles a step");
+  auto dma_bases = [&](size_t b0, size_t b1, int buf) __attribute__((always_inline)) {
     const uint32_t dst0 = lds_u32 + (uint32_t)(buf * BUF_BYTES);
     if (kwave) {
-      const int h = (wk * PER) / NK, t0 = (wk * PER) % NK;
-      const size_t b0 = tile_at(step, 2 * h), b1 = tile_at(step, 2 * h + 1);
+      const int t0 = (wk * PER) % NK;
       const uint8_t* src = a.k + ((lane & 16) ? b1 : b0) + lane_off + 32 * t0;
-      const uint32_t dst = dst0 + (uint32_t)(h * KH_BYTES + t0 * 1024);
+      const uint32_t dst = dst0 + (uint32_t)((ta / 2) * KH_BYTES + t0 * 1024);
 #pragma unroll
       for (int i = 0; i < PER; ++i) lds_load16(src + 32 * i, dst + 1024u * i);
     } else {
 #pragma unroll
       for (int q = 0; q < PER / NDV; ++q) {
-        const int tt = (wk * PER) / NDV + q;
-        const uint8_t* src = a.v + tile_at(step, tt) + lane_off;
-        const uint32_t dst = dst0 + (uint32_t)(2 * KH_BYTES + tt * VT_BYTES);
+        const uint8_t* src = a.v + (q == 0 ? b0 : b1) + lane_off;
+        const uint32_t dst = dst0 + (uint32_t)(2 * KH_BYTES + (ta + q) * VT_BYTES);
 #pragma unroll
         for (int dg = 0; dg < NDV; ++dg) lds_load16(src + 64 * dg, dst + 1024u * dg);
       }
     }
+  };
+  auto dma_step = [&](int step, int buf) __attribute__((always_inline)) {
+    dma_bases(tile_at(step, ta), tile_at(step, ta + 1), buf);
   };
   // After a V wave's loads of a step have landed: V slots of keys at or past
   // the sequence's end hold whatever the page has there (a weight 0 times a
@@ -555,10 +562,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       wait_vm(IntC<63>{});
       barrier();
       int buf = 0;
+      size_t nb0 = tile_at(NBUF - 1, ta), nb1 = tile_at(NBUF - 1, ta + 1);
       for (int step = 0; step < n_steps; ++step) {
         const int nb = buf + 1 == NBUF ? 0 : buf + 1;  // buffer of step + 1
         const int fb = nb + 1 == NBUF ? 0 : nb + 1;    // of step + 2
-        if (step + NBUF - 1 < n_steps) dma_step(step + NBUF - 1, NBUF == 3 ? fb : nb);
+        if (step + NBUF - 1 < n_steps) dma_bases(nb0, nb1, NBUF == 3 ? fb : nb);
         compute(step, buf);
         if (step + 1 < n_steps) {
           if (NBUF == 3 && step + 2 < n_steps)
@@ -567,6 +575,9 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
             wait_vm(IntC<0>{});
           dma_zero_tail(step + 1, nb);
           wait_vm(IntC<63>{});
+          // (tile_at clamps, so a step past the last reads a valid entry)
+          nb0 = tile_at(step + NBUF, ta);
+          nb1 = tile_at(step + NBUF, ta + 1);
           barrier();
         }
         buf = nb;
