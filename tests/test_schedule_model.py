@@ -1,0 +1,211 @@
+"""Host models of the GPU kernels' lane maps and LDS schedules (no GPU).
+
+These check properties of index maps that the HIP sources compute, the way a
+reviewer would check them by hand: every element of a staged step lands in
+exactly one LDS slot and is read back by the lane that the matrix
+instruction's operand layout expects; the reads of one LDS pass fall on
+distinct banks; and the step pipelines never overwrite a buffer another wave
+may still read, nor read one whose loads have not been waited for. The maps
+below restate the kernels' formulas (pda_prefill_mfma.h, pda_decode_mfma.h);
+a change there must be mirrored here, and the properties re-proved.
+
+LDS is modelled as 64 banks of 4 bytes; a 16-byte read (ds_read_b128) is
+served 16 lanes per pass, an 8-byte read (ds_read_b64_tr_b16) 32 lanes per
+pass.
+"""
+
+import itertools
+
+import pytest
+
+BANKS = 64
+
+
+def banks_of(addr: int, nbytes: int) -> set:
+    return {((addr + b) // 4) % BANKS for b in range(0, nbytes, 4)}
+
+
+def conflict_free(addrs, nbytes, lanes_per_pass):
+    for p in range(0, len(addrs), lanes_per_pass):
+        seen = set()
+        for a in addrs[p:p + lanes_per_pass]:
+            b = banks_of(a, nbytes)
+            if seen & b:
+                return False
+            seen |= b
+    return True
+
+
+# ---- prefill kernel: one 64-key step of K and V in LDS (fp16) ----
+
+def prefill_geometry(D, waves):
+    NK = D // 16                 # K blocks (16-dim k-steps) per 32-key half
+    NDV = D // 32                # V blocks (32 dims) per 16-key tile
+    KH = NK * 1024               # bytes of K of one half
+    VT = NDV * 1024              # bytes of V of one tile
+    PER = 2 * NK // (waves // 2)  # 1 KB loads per wave and step
+    return NK, NDV, KH, VT, PER
+
+
+def prefill_dma_writes(D, waves):
+    """(lds byte offset in the step buffer) -> ('K' or 'V', key, first dim)
+    for every lane of every direct load of one step, as the kernel issues
+    them (K waves: wave < waves / 2)."""
+    NK, NDV, KH, VT, PER = prefill_geometry(D, waves)
+    out = {}
+    for wave in range(waves):
+        kwave = wave < waves // 2
+        wk = wave if kwave else wave - waves // 2
+        ta = 2 * ((wk * PER) // NK) if kwave else (wk * PER) // NDV
+        for lane in range(64):
+            if kwave:
+                t0 = (wk * PER) % NK
+                tile = ta + ((lane >> 4) & 1)
+                row = lane & 15
+                for i in range(PER):
+                    byte_in_row = 32 * (t0 + i) + 16 * (lane >> 5)
+                    dst = (ta // 2) * KH + (t0 + i) * 1024 + 16 * lane
+                    assert dst not in out
+                    out[dst] = ("K", 16 * tile + row, byte_in_row // 2)
+            else:
+                vrow = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 2) & 3)
+                for q in range(PER // NDV):
+                    for dg in range(NDV):
+                        byte_in_row = 64 * dg + 16 * (lane & 3)
+                        dst = 2 * KH + (ta + q) * VT + dg * 1024 + 16 * lane
+                        assert dst not in out
+                        out[dst] = ("V", 16 * (ta + q) + vrow, byte_in_row // 2)
+    return out
+
+
+@pytest.mark.parametrize("D,waves", [(128, 8), (128, 4), (256, 8), (256, 4)])
+def test_prefill_step_is_covered_once(D, waves):
+    """Every 16-byte piece of the step's 64 K rows and 64 V rows is loaded
+    into exactly one slot, and the slots tile the buffer."""
+    NK, NDV, KH, VT, PER = prefill_geometry(D, waves)
+    w = prefill_dma_writes(D, waves)
+    assert sorted(w) == list(range(0, 2 * KH + 4 * VT, 16))
+    pieces = set(w.values())
+    assert len(pieces) == len(w)
+    want = {(kv, key, d) for kv in "KV" for key in range(64) for d in range(0, D, 8)}
+    assert pieces == want
+
+
+@pytest.mark.parametrize("D,waves", [(128, 8), (256, 8)])
+def test_prefill_k_fragments_are_the_mfma_a_operand(D, waves):
+    """Lane l's 16-byte read at k-step t of half h holds key 32 h + l % 32,
+    dims 16 t + 8 (l / 32) .. + 7: the A fragment of v_mfma_f32_32x32x16_f16
+    (row l % 32, k = 8 (l / 32) .. + 7)."""
+    NK, NDV, KH, VT, PER = prefill_geometry(D, waves)
+    w = prefill_dma_writes(D, waves)
+    for h in range(2):
+        for t in range(NK):
+            addrs = [h * KH + 1024 * t + 16 * lane for lane in range(64)]
+            for lane, a in enumerate(addrs):
+                assert w[a] == ("K", 32 * h + lane % 32, 16 * t + 8 * (lane // 32))
+            assert conflict_free(addrs, 16, 16)
+
+
+@pytest.mark.parametrize("D,pair", [(128, False), (256, True)])
+def test_prefill_v_transposing_reads(D, pair):
+    """The transposing reads of tile 2 h + ks, dims dcol + 32 dt: lane
+    (hh, q16, i16) reads 8 bytes that must hold V[key 16 (2h + ks) + 8 hi +
+    4 hh + i16 / 4][dims dcol + 32 dt + 16 (q16 % 2) + 4 (i16 % 4) .. + 3],
+    the elements a row-major V tile gave the same lane (so the transposing
+    read still hands the MFMA its V^T operand). Both 32-lane passes are
+    conflict-free."""
+    NK, NDV, KH, VT, PER = prefill_geometry(D, 8)
+    w = prefill_dma_writes(D, 8)
+    NDT = (D // 2 if pair else D) // 32
+    for dh in (range(2) if pair else [0]):
+        dcol = dh * (D // 2)
+        for h, ks, dt, hi in itertools.product(range(2), range(2), range(NDT), range(2)):
+            addrs = []
+            for lane in range(64):
+                hh, q16, i16 = lane >> 5, lane >> 4, lane & 15
+                v_lane = 16 * (16 * hh + 4 * (i16 >> 2) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) + 8 * (i16 & 1)
+                a = 2 * KH + (2 * h + ks) * VT + (dcol // 32 + dt) * 1024 + 512 * hi + v_lane
+                addrs.append(a)
+                slot, half = a - (a % 16), (a % 16) // 2   # which 16-byte slot, which 4-dim half
+                kv, key, d0 = w[slot]
+                assert kv == "V"
+                assert key == 16 * (2 * h + ks) + 8 * hi + 4 * hh + (i16 >> 2)
+                assert d0 + half == dcol + 32 * dt + 16 * (q16 & 1) + 4 * (i16 & 3)
+            assert conflict_free(addrs, 8, 32)
+
+
+# ---- prefill pipeline: buffers, waits and barriers ----
+
+def simulate_prefill_pipeline(nbuf, n_steps, per=4):
+    """The fp16 step loop: steps 0 and (three buffers) 1 are issued before
+    the loop; step s computes on buffer s % nbuf and first issues the loads
+    of step s + nbuf - 1; its end waits vmcnt(per) when the loads of step
+    s + 2 are in flight (three buffers), else vmcnt(0), then a barrier.
+    Returns the events for the checks."""
+    issued = []             # order of issue: (step, buffer)
+    waits = []              # (position in issue order, allowed outstanding)
+    events = []             # ('issue', step, buf, epoch) / ('read', step, buf, epoch)
+    epoch = 0               # barriers passed
+    for j in range(min(nbuf - 1, n_steps)):
+        issued.append((j, j % nbuf))
+        events.append(("issue", j, j % nbuf, epoch))
+    waits.append((len(issued), per if (nbuf == 3 and n_steps > 1) else 0, 0))
+    epoch += 1
+    for s in range(n_steps):
+        j = s + nbuf - 1
+        if j < n_steps:
+            issued.append((j, j % nbuf))
+            events.append(("issue", j, j % nbuf, epoch))
+        events.append(("read", s, s % nbuf, epoch))
+        if s + 1 < n_steps:
+            waits.append((len(issued), per if (nbuf == 3 and s + 2 < n_steps) else 0, s + 1))
+            epoch += 1
+    return issued, waits, events
+
+
+@pytest.mark.parametrize("nbuf", [2, 3])
+@pytest.mark.parametrize("n_steps", range(1, 9))
+def test_prefill_pipeline_is_race_free(nbuf, n_steps):
+    per = 4
+    issued, waits, events = simulate_prefill_pipeline(nbuf, n_steps, per)
+    assert sorted(s for s, _ in issued) == list(range(n_steps))
+    # Each wait before the barrier that precedes step s's reads leaves at
+    # most `allowed` loads in flight; loads complete in issue order, so the
+    # loads of step s (each wave's per of them) are complete.
+    for n_issued, allowed, s in waits:
+        last_of_s = max(i for i, (j, _) in enumerate(issued) if j == s) + 1
+        assert n_issued - last_of_s >= 0
+        assert (n_issued - last_of_s) * per <= allowed or n_issued == last_of_s, (s, allowed)
+        # allowed never exceeds what was issued after step s (no waiting on nothing)
+        assert allowed <= (n_issued - last_of_s) * per
+    # A load into a buffer is issued in a later barrier epoch than every read
+    # of the step that buffer held before.
+    for kind, j, b, ep in events:
+        if kind != "issue":
+            continue
+        for kind2, s2, b2, ep2 in events:
+            if kind2 == "read" and b2 == b and s2 < j:
+                assert ep2 < ep, (j, s2, b)
+    # Every read happens in an epoch after its step's load was issued and waited.
+    for kind, s, b, ep in events:
+        if kind == "read":
+            issue_ep = next(e for k, j, _, e in events if k == "issue" and j == s)
+            assert issue_ep < ep
+
+
+# ---- decode kernel: the wave-private V tile and its transposing reads ----
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_decode_v_tile_reads_are_conflict_free(D):
+    """The matrix decode kernel's V tile has rows of D + 16 halves; lane
+    (s, c) of a transposing read points at row 4 s + c / 4, dims 16 dt +
+    4 (c % 4): each 32-lane pass (8 rows x 32 bytes) falls on distinct banks
+    (with D + 8 they overlap 2-way)."""
+    def addrs(lr):
+        out = []
+        for dt in range(D // 16):
+            out.append([2 * ((4 * (lane >> 4) + ((lane & 15) >> 2)) * lr + 16 * dt + 4 * (lane & 3))
+                        for lane in range(64)])
+        return out
+    assert all(conflict_free(a, 8, 32) for a in addrs(D + 16))
+    assert not all(conflict_free(a, 8, 32) for a in addrs(D + 8))
