@@ -167,8 +167,15 @@ constexpr int prefill_step_bytes(int head_dim) {
 constexpr int prefill_buffers(int head_dim, int kv_kind, int waves) {
   return kv_kind == kKvF16 && head_dim == 128 && waves == 8 ? 3 : 2;
 }
+// LDS the output tiles take after the loop: 32 rows per wave of the dims it
+// writes (half of D in the 8-wave D=256 pairs), each row 16 bytes longer.
+constexpr size_t prefill_out_lds_bytes(int head_dim, int waves) {
+  return (size_t)waves * 32 * (2 * ((head_dim == 256 && waves == 8) ? head_dim / 2 : head_dim) + 16);
+}
 inline size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
-  return (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim);
+  const size_t steps = (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim);
+  const size_t out = prefill_out_lds_bytes(head_dim, waves);
+  return steps > out ? steps : out;
 }
 hipError_t launch_prefill_f16(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);

@@ -606,8 +606,12 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     }
   }
 
-  // Bring o, l to the row maximum, add the two lane halves' l, write fp16 out
-  // (a row that sees no key is 0). Lane l writes dims 32 dt + 8 j + 4 hh .. + 3.
+  // Bring o, l to the row maximum, add the two lane halves' l, and write
+  // fp16 out (a row that sees no key is 0), one division per row: o times
+  // alpha * v_scale / l. Lane l holds dims 32 dt + 8 j + 4 hh .. + 3 of row
+  // rr; the rows go through a wave-private LDS tile (row stride DW + 8
+  // halves, 16-byte aligned) so that the global stores are whole rows, 16
+  // lanes x 16 bytes each, instead of 8-byte pieces of 32 rows.
   const float alpha = __builtin_amdgcn_exp2f(m - mx);
   lsum *= alpha;
   {
@@ -615,22 +619,35 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
                                                __builtin_bit_cast(int, lsum), false, false);
     lsum = __builtin_bit_cast(float, (int)sw[0]) + __builtin_bit_cast(float, (int)sw[1]);
   }
-  if (my_row) {
-    const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
-    // one division per row: o is multiplied by alpha * vs / l (0 for a row
-    // that sees no key)
-    const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
-    const size_t hrow = (size_t)(off + my_i) * Hq + g * G + (myr - (myr / G) * G);
-    uint16_t* dst = a.out + hrow * D + dcol + 4 * hh;
+  const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
+  const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
+  constexpr int DW = PAIR ? D / 2 : D;  // dims this wave writes
+  constexpr int RS = 2 * DW + 16;      // LDS bytes per row
+  static_assert(WAVES * 32 * RS <= (int)prefill_out_lds_bytes(D, WAVES), "out tile fits");
+  // Every wave has left the last step's LDS reads before any tile is written.
+  __syncthreads();
+  uint8_t* const tile = lds_raw + wave * 32 * RS;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+  for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h4_t y;
+    for (int j = 0; j < 4; ++j) {
+      h4_t y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[dt][4 * j + e] * f);
-        *reinterpret_cast<h4_t*>(dst + 32 * dt + 8 * j) = y;
-      }
+      for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[dt][4 * j + e] * f);
+      *reinterpret_cast<h4_t*>(tile + rr * RS + 2 * (32 * dt + 8 * j + 4 * hh)) = y;
+    }
+  }
+  constexpr int PPR = DW / 8;  // 16-byte pieces of a row
+#pragma unroll
+  for (int it = 0; it < 32 * PPR / 64; ++it) {
+    const int idx = 64 * it + lane;
+    const int r = idx / PPR, pc = idx % PPR;
+    const int wr = 32 * rg + r;  // the workgroup row
+    const int i = i0 + wr / G;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + 16 * pc);
+    if (wr < a.rows && i < Qb) {
+      const size_t hrow = (size_t)(off + i) * Hq + g * G + (wr - (wr / G) * G);
+      *reinterpret_cast<u32x4*>(a.out + hrow * D + dcol + 8 * pc) = v;
     }
   }
 }
