@@ -179,7 +179,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   auto lds_load16 = [](const uint8_t* src, uint32_t dst) __attribute__((always_inline)) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(dst)));
+                 : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                 : "memory");
   };
 
   // fp16 caches, direct loads: waves [0, WAVES / 2) load K, the others V, in
@@ -243,9 +244,13 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     }
   };
   // s_waitcnt with vmcnt(VM) and lgkmcnt(0) (expcnt untouched).
+  // The empty asm after it keeps the compiler from moving LDS accesses (the
+  // zeroing of a step's tail, say) above the wait for the direct loads they
+  // depend on; the loads' asm carries a memory clobber for the same reason.
   auto wait_vm = [](auto vm_c) __attribute__((always_inline)) {
     constexpr int VM = decltype(vm_c)::value;
     __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+    asm volatile("" ::: "memory");
   };
   // Workgroup barrier without a memory fence (the waits before it are
   // explicit); the empty asm statements keep the compiler from moving memory
