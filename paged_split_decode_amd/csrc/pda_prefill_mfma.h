@@ -4,24 +4,24 @@
 //
 // A workgroup takes a block of new tokens of one sequence and all G query
 // heads of one KV head: 32 (token, head) rows per wave, 4 or 8 waves (8 at
-// D=128 when the keys before the new tokens are long: chunked prefill); at
-// D=256, 8 waves in pairs that share 32 rows and split the output dims. K and
-// V go through LDS once per workgroup and serve all its waves: each step the
-// threads gather 64 keys (four 16-key tiles) of K and V from the paged cache
-// with 16-byte loads, convert 1-byte codes to fp16 (exactly), and write them
-// to one of two fp16 LDS buffers while the waves compute on the other; one
-// barrier per step. A step's loads are issued when the step before the one
-// that stores them ends (NREG = 1), or one step earlier still with 8 waves
-// (NREG = 2: each thread stages half as much, so two register sets fit).
+// D=128 when the keys before the new tokens are long, or a KV head has many
+// rows); at D=256, 8 waves in pairs that share 32 rows and split the output
+// dims. K and V go through LDS once per workgroup and serve all its waves,
+// 64 keys (four 16-key tiles) per step, stored as fp16 in the order the
+// matrix instructions read them. fp16 pages go straight from the paged cache
+// into LDS (16-byte direct loads, half the waves loading K and half V, two or
+// three steps deep, explicit waits and one barrier per step); 1-byte codes
+// are loaded into registers, converted to fp16 exactly and stored, two
+// buffers deep.
 //
-// Per wave and 32 keys: S^T = K . Q^T with v_mfma_f32_32x32x16_f16 (K
-// fragments read from the LDS tile, the wave's 32 Q rows as the B operand;
-// lane l then holds 16 scores of query row l % 32), an online softmax with a
+// Per wave and 64 keys: S^T = K . Q^T with v_mfma_f32_32x32x16_f16 (K
+// fragments read from LDS, the wave's 32 Q rows as the B operand; lane l then
+// holds 16 scores of query row l % 32 per 32 keys), an online softmax with a
 // lazily moved reference, and O^T += V^T . P^T with the same instruction: P
 // from the score registers, V^T from ds_read_b64_tr_b16. Each row has its own
-// causal limit (its position) and window; 32 keys after all of a wave's rows,
-// or before all their windows, are skipped by that wave. Workgroups with the
-// most keys (the last token blocks) are dispatched first.
+// causal limit (its position) and window; a step no row of the wave sees is
+// skipped, and keys a row does not see get score -inf. Workgroups run in an
+// XCD-aware order, the token blocks with the most keys first.
 #pragma once
 
 #include "pda_decode_mfma.h"
