@@ -164,8 +164,11 @@ constexpr int prefill_step_bytes(int head_dim) {
 // for 8-wave workgroups at D=128 (96 KB, one workgroup per CU) and two
 // otherwise (64 KB at D=128: two 4-wave workgroups per CU; 128 KB at D=256);
 // 1-byte codes are converted in registers and stored into two buffers.
+#ifndef PDA_PREFILL_NBUF8
+#define PDA_PREFILL_NBUF8 3
+#endif
 constexpr int prefill_buffers(int head_dim, int kv_kind, int waves) {
-  return kv_kind == kKvF16 && head_dim == 128 && waves == 8 ? 3 : 2;
+  return kv_kind == kKvF16 && head_dim == 128 && waves == 8 ? PDA_PREFILL_NBUF8 : 2;
 }
 // LDS the output tiles take after the loop: 32 rows per wave of the dims it
 // writes (half of D in the 8-wave D=256 pairs), each row 16 bytes longer.

@@ -343,8 +343,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // The first steps' loads go out first: the Q loads and the token offset
   // below do not hold them up.
   if constexpr (DMA) {
-    if (n_steps > 0) dma_step(0, 0);
-    if (NBUF == 3 && n_steps > 1) dma_step(1, 1);
+    for (int j = 0; j < NBUF - 1 && j < n_steps; ++j) dma_step(j, j);
   } else {
     if (n_steps > 0) stage_load(0, IntC<0>{});
   }
@@ -556,13 +555,21 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     // wave has left at the barrier); its end waits for this wave's loads of
     // step s + 1 (the PER loads of step s + 2 may stay in flight), zeroes
     // that step's tail, and meets the other waves at the barrier.
-    static_assert(NBUF == 2 || NBUF == 3, "two or three step buffers");
-    if (n_steps > 0) {
-      // (steps 0 and 1 were issued above; Q loads may follow them)
-      if (NBUF == 3 && n_steps > 1)
+    static_assert(NBUF >= 2 && NBUF <= 4, "two to four step buffers");
+    // Wait for this wave's loads of step `need`, with the loads of the steps
+    // after it that were issued (up to `issued_to`, at most two) in flight.
+    auto wait_step = [&](int need, int issued_to) __attribute__((always_inline)) {
+      const int after = min(issued_to, n_steps - 1) - need;
+      if (after >= 2)
+        wait_vm(IntC<2 * PER>{});
+      else if (after == 1)
         wait_vm(IntC<PER>{});
       else
         wait_vm(IntC<0>{});
+    };
+    if (n_steps > 0) {
+      // (steps 0 .. NBUF - 2 were issued above; Q loads may follow them)
+      wait_step(0, NBUF - 2);
       dma_zero_tail(0, 0);
       wait_vm(IntC<63>{});
       barrier();
@@ -570,14 +577,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       size_t nb0 = tile_at(NBUF - 1, ta), nb1 = tile_at(NBUF - 1, ta + 1);
       for (int step = 0; step < n_steps; ++step) {
         const int nb = buf + 1 == NBUF ? 0 : buf + 1;  // buffer of step + 1
-        const int fb = nb + 1 == NBUF ? 0 : nb + 1;    // of step + 2
-        if (step + NBUF - 1 < n_steps) dma_bases(nb0, nb1, NBUF == 3 ? fb : nb);
+        const int lb = buf == 0 ? NBUF - 1 : buf - 1;  // of step + NBUF - 1
+        if (step + NBUF - 1 < n_steps) dma_bases(nb0, nb1, lb);
         compute(step, buf);
         if (step + 1 < n_steps) {
-          if (NBUF == 3 && step + 2 < n_steps)
-            wait_vm(IntC<PER>{});
-          else
-            wait_vm(IntC<0>{});
+          wait_step(step + 1, step + NBUF - 1);
           dma_zero_tail(step + 1, nb);
           wait_vm(IntC<63>{});
           // (tile_at clamps, so a step past the last reads a valid entry)

@@ -137,19 +137,24 @@ def test_prefill_v_transposing_reads(D, pair):
 # ---- prefill pipeline: buffers, waits and barriers ----
 
 def simulate_prefill_pipeline(nbuf, n_steps, per=4):
-    """The fp16 step loop: steps 0 and (three buffers) 1 are issued before
-    the loop; step s computes on buffer s % nbuf and first issues the loads
-    of step s + nbuf - 1; its end waits vmcnt(per) when the loads of step
-    s + 2 are in flight (three buffers), else vmcnt(0), then a barrier.
-    Returns the events for the checks."""
+    """The fp16 step loop: steps 0 .. nbuf - 2 are issued before the loop;
+    step s computes on buffer s % nbuf and first issues the loads of step
+    s + nbuf - 1 (into the buffer step s - 1 used); its end waits for step
+    s + 1 with the issued steps after it (at most two) in flight (vmcnt of
+    their loads), then a barrier. Returns the events for the checks."""
     issued = []             # order of issue: (step, buffer)
-    waits = []              # (position in issue order, allowed outstanding)
+    waits = []              # (loads issued so far, allowed outstanding, step needed)
     events = []             # ('issue', step, buf, epoch) / ('read', step, buf, epoch)
     epoch = 0               # barriers passed
+
+    def allowed(need, issued_to):
+        after = min(issued_to, n_steps - 1) - need
+        return per * min(max(after, 0), 2)
+
     for j in range(min(nbuf - 1, n_steps)):
         issued.append((j, j % nbuf))
         events.append(("issue", j, j % nbuf, epoch))
-    waits.append((len(issued), per if (nbuf == 3 and n_steps > 1) else 0, 0))
+    waits.append((len(issued), allowed(0, nbuf - 2), 0))
     epoch += 1
     for s in range(n_steps):
         j = s + nbuf - 1
@@ -158,26 +163,25 @@ def simulate_prefill_pipeline(nbuf, n_steps, per=4):
             events.append(("issue", j, j % nbuf, epoch))
         events.append(("read", s, s % nbuf, epoch))
         if s + 1 < n_steps:
-            waits.append((len(issued), per if (nbuf == 3 and s + 2 < n_steps) else 0, s + 1))
+            waits.append((len(issued), allowed(s + 1, s + nbuf - 1), s + 1))
             epoch += 1
     return issued, waits, events
 
 
-@pytest.mark.parametrize("nbuf", [2, 3])
-@pytest.mark.parametrize("n_steps", range(1, 9))
+@pytest.mark.parametrize("nbuf", [2, 3, 4])
+@pytest.mark.parametrize("n_steps", range(1, 10))
 def test_prefill_pipeline_is_race_free(nbuf, n_steps):
     per = 4
     issued, waits, events = simulate_prefill_pipeline(nbuf, n_steps, per)
     assert sorted(s for s, _ in issued) == list(range(n_steps))
     # Each wait before the barrier that precedes step s's reads leaves at
     # most `allowed` loads in flight; loads complete in issue order, so the
-    # loads of step s (each wave's per of them) are complete.
+    # loads of step s (each wave's per of them) are complete exactly when
+    # no more than the loads issued after them may stay outstanding.
     for n_issued, allowed, s in waits:
         last_of_s = max(i for i, (j, _) in enumerate(issued) if j == s) + 1
-        assert n_issued - last_of_s >= 0
-        assert (n_issued - last_of_s) * per <= allowed or n_issued == last_of_s, (s, allowed)
-        # allowed never exceeds what was issued after step s (no waiting on nothing)
-        assert allowed <= (n_issued - last_of_s) * per
+        assert allowed <= (n_issued - last_of_s) * per, (s, allowed)
+        assert allowed == (n_issued - last_of_s) * per or allowed == 2 * per
     # A load into a buffer is issued in a later barrier epoch than every read
     # of the step that buffer held before.
     for kind, j, b, ep in events:
@@ -191,6 +195,26 @@ def test_prefill_pipeline_is_race_free(nbuf, n_steps):
         if kind == "read":
             issue_ep = next(e for k, j, _, e in events if k == "issue" and j == s)
             assert issue_ep < ep
+
+
+@pytest.mark.parametrize("mistake", ["load_one_step_further", "skip_a_wait"])
+def test_prefill_pipeline_model_catches_planted_mistakes(mistake):
+    """The checks above fail on a schedule that loads into the buffer the
+    current step reads, or that waits too little."""
+    nbuf, n_steps, per = 3, 6, 4
+    issued, waits, events = simulate_prefill_pipeline(nbuf, n_steps, per)
+    if mistake == "load_one_step_further":
+        # step s loads step s + nbuf into buffer s % nbuf, read by step s itself
+        events = [("issue", j + 1, (j + 1) % nbuf, ep) if k == "issue" and ep > 0 else (k, j, b, ep)
+                  for k, j, b, ep in events]
+        bad = any(k == "issue" and any(k2 == "read" and b2 == b and s2 < j and ep2 >= ep
+                                       for k2, s2, b2, ep2 in events)
+                  for k, j, b, ep in events)
+        assert bad
+    else:
+        n_issued, allowed, s = waits[1]
+        last_of_s = max(i for i, (j, _) in enumerate(issued) if j == s) + 1
+        assert allowed + per > (n_issued - last_of_s) * per
 
 
 # ---- decode kernel: the wave-private V tile and its transposing reads ----
