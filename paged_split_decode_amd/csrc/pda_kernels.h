@@ -150,7 +150,8 @@ inline size_t decode_lds_bytes(int waves, int rows_per_wave, int head_dim) {
 // sequence on one XCD, 8-wave workgroups measured 3.7% faster than two 4-wave
 // ones per CU on a fresh prefill of 4 x 2048 tokens). Fewer rows take 4 waves
 // (128 rows per workgroup). At D=256 a workgroup has 8 waves in pairs that
-// share 32 rows and split the output dims (128 rows per workgroup).
+// share 32 rows, split the scores by key half (exchanged through LDS) and
+// the output by dims (128 rows per workgroup).
 inline int prefill_waves(int head_dim, int max_q_len, int64_t key_capacity, int group) {
   if (head_dim == 256) return 8;
   return (4 * (int64_t)max_q_len <= key_capacity || (int64_t)group * max_q_len >= 512) ? 8 : 4;
@@ -162,7 +163,8 @@ constexpr int prefill_step_bytes(int head_dim) {
 }
 // Step buffers in LDS: fp16 caches load straight into LDS, three steps deep
 // for 8-wave workgroups at D=128 (96 KB, one workgroup per CU) and two
-// otherwise (64 KB at D=128: two 4-wave workgroups per CU; 128 KB at D=256);
+// otherwise (64 KB at D=128: two 4-wave workgroups per CU; 128 KB at D=256,
+// plus 32 KB for the pairs' score exchange);
 // 1-byte codes are converted in registers and stored into two buffers.
 #ifndef PDA_PREFILL_NBUF8
 #define PDA_PREFILL_NBUF8 3
@@ -175,8 +177,13 @@ constexpr int prefill_buffers(int head_dim, int kv_kind, int waves) {
 constexpr size_t prefill_out_lds_bytes(int head_dim, int waves) {
   return (size_t)waves * 32 * (2 * ((head_dim == 256 && waves == 8) ? head_dim / 2 : head_dim) + 16);
 }
+// The score exchange of the D=256 pairs: 16 floats per lane and wave.
+constexpr size_t prefill_xchg_bytes(int head_dim, int waves) {
+  return head_dim == 256 && waves == 8 ? (size_t)waves * 64 * 16 * 4 : 0;
+}
 inline size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
-  const size_t steps = (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim);
+  const size_t steps = (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim) +
+                       prefill_xchg_bytes(head_dim, waves);
   const size_t out = prefill_out_lds_bytes(head_dim, waves);
   return steps > out ? steps : out;
 }

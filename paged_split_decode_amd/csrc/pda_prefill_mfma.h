@@ -5,14 +5,15 @@
 // A workgroup takes a block of new tokens of one sequence and all G query
 // heads of one KV head: 32 (token, head) rows per wave, 4 or 8 waves (8 at
 // D=128 when the keys before the new tokens are long, or a KV head has many
-// rows); at D=256, 8 waves in pairs that share 32 rows and split the output
-// dims. K and V go through LDS once per workgroup and serve all its waves,
-// 64 keys (four 16-key tiles) per step, stored as fp16 in the order the
-// matrix instructions read them. fp16 pages go straight from the paged cache
-// into LDS (16-byte direct loads, half the waves loading K and half V, two or
-// three steps deep, explicit waits and one barrier per step); 1-byte codes
-// are loaded into registers, converted to fp16 exactly and stored, two
-// buffers deep.
+// rows); at D=256, 8 waves in pairs that share 32 rows, each computing the
+// scores of half of a step's keys (the halves are swapped through LDS) and
+// accumulating half of the output dims. K and V go through LDS once per
+// workgroup and serve all its waves, 64 keys (four 16-key tiles) per step,
+// stored as fp16 in the order the matrix instructions read them. fp16 pages
+// go straight from the paged cache into LDS (16-byte direct loads, half the
+// waves loading K and half V, two or three steps deep, explicit waits and one
+// barrier per step); 1-byte codes are loaded into registers, converted to
+// fp16 exactly and stored, two buffers deep.
 //
 // Per wave and 64 keys: S^T = K . Q^T with v_mfma_f32_32x32x16_f16 (K
 // fragments read from LDS, the wave's 32 Q rows as the B operand; lane l then
@@ -29,6 +30,7 @@
 namespace pda {
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // A compile-time bool carried by value (selects a lambda body variant).
 template <bool B>
@@ -85,15 +87,17 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // At D=256 waves w and w + 4 share the rows 32 (w % 4) .. + 31 and each
-  // accumulates half of the output dims: both compute the rows' scores and
-  // softmax, but o takes 64 registers instead of 128, so two waves fit per
-  // SIMD and hide each other's LDS latency (a single wave waited for every K
-  // fragment read right before its MFMA). Measured 6% faster than one wave
-  // per row block.
+  // At D=256 (8 waves) waves 2 r and 2 r + 1 share the rows 32 r .. + 31:
+  // each computes the scores of one 32-key half of a step (all D dims) and
+  // hands them to the other through LDS; both then run the softmax over all
+  // 64 keys, and each accumulates half of the output dims. o takes 64
+  // registers instead of 128, so two waves fit per SIMD, and no score is
+  // computed twice. The partners sit on different SIMDs (waves w and w + 4
+  // share one), so that while one pair waits for its scores, the other
+  // pair's wave on the same SIMD keeps the matrix unit busy.
   constexpr bool PAIR = D == 256 && WAVES == 8;
-  const int rg = PAIR ? (wave & 3) : wave;  // row block
-  const int dh = PAIR ? (wave >> 2) : 0;    // output dim half
+  const int rg = PAIR ? (wave >> 1) : wave;  // row block
+  const int dh = PAIR ? (wave & 1) : 0;      // key half of the scores, output dim half
   // Workgroup -> (token block, KV head, sequence), XCD-aware: the dispatcher
   // hands workgroups to the 8 XCDs in turn (id % 8), and each XCD has its own
   // L2. The token blocks of one (sequence, KV head) read the same keys, so
@@ -113,6 +117,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     g = (int)(rest % ny);
     b = (int)(rest / ny);
   }
+  const int dcol = dh * (D / 2);  // first output dim of this wave
   const int G = a.group;
   const int Hq = a.num_q_heads;
   const int BQ = a.rows / G;                   // tokens per workgroup
@@ -163,11 +168,14 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     return (size_t)bt[u >> tshift] * a.page_bytes + (size_t)((u & tmask) * kPageSize) * key_stride;
   };
 
+  // First tile of step `step` (past the last step: tiles past the range,
+  // which tile_at clamps).
+  auto step_tile = [&](int step) __attribute__((always_inline)) { return t_lo + step * KT; };
   // Tile tt of step `step`; tiles past the workgroup's range are read from
   // its last tile (in bounds; all their keys are masked).
   const int last_tile = t_lo + n_tiles - 1;
   auto tile_at = [&](int step, int tt) __attribute__((always_inline)) {
-    return tile_base(min(t_lo + step * KT + tt, last_tile));
+    return tile_base(min(step_tile(step) + tt, last_tile));
   };
   const uint32_t lds_u32 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds_raw;
   // One direct 16-byte load per lane into LDS at byte dst + 16 lane (dst
@@ -184,36 +192,36 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   };
 
   // fp16 caches, direct loads: waves [0, WAVES / 2) load K, the others V, in
-  // whole 1 KB blocks, PER per wave and step; a K wave's blocks lie in one
-  // half, a V wave's cover whole tiles. Each lane's byte offset within a
-  // tile is fixed: K, key lane % 16 of the lane's tile (lane / 16 % 2 of the
-  // half) at dims 8 (lane / 32) ..; V, the key row of slot `lane` at dims
-  // 8 (lane % 4) ...
-  constexpr int PER = 2 * NK / (WAVES / 2);
-  static_assert(PER == KT * NDV / (WAVES / 2), "K and V waves load as many blocks");
-  static_assert(NK % PER == 0 && PER % NDV == 0, "a wave's blocks: one half, or whole tiles");
+  // whole 1 KB blocks, PERK per K wave and PERV per V wave and step; a K
+  // wave's blocks lie in one half, a V wave's cover whole tiles. Each lane's
+  // byte offset within a tile is fixed: K, key lane % 16 of the lane's tile
+  // (lane / 16 % 2 of the half) at dims 8 (lane / 32) ..; V, the key row of
+  // slot `lane` at dims 8 (lane % 4) ...
+  constexpr int PERK = 2 * NK / (WAVES / 2);
+  constexpr int PERV = KT * NDV / (WAVES / 2);
+  static_assert(NK % PERK == 0 && PERV % NDV == 0, "a wave's blocks: one half, or whole tiles");
   const bool kwave = wave < WAVES / 2;
   const int wk = kwave ? wave : wave - WAVES / 2;
   const int vrow = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 2) & 3);
   const uint32_t lane_off = kwave ? (uint32_t)(lane & 15) * key_stride + head_off + 16u * (lane >> 5)
                                   : (uint32_t)vrow * key_stride + head_off + 16u * (lane & 3);
   // The tiles a wave loads each step: a K wave tiles ta and ta + 1 (its
-  // half), a V wave tiles ta .. ta + PER / NDV - 1 (at most two). Inside the
+  // half), a V wave tiles ta .. ta + PERV / NDV - 1 (at most two). Inside the
   // step loop their bases come from the block table before the barrier of
   // the step before, so the scalar loads' latency hides under the barrier.
-  const int ta = kwave ? 2 * ((wk * PER) / NK) : (wk * PER) / NDV;
-  static_assert(PER / NDV <= 2, "a V wave loads at most two tiles a step");
+  const int ta = kwave ? 2 * ((wk * PERK) / NK) : (wk * PERV) / NDV;
+  static_assert(PERV / NDV <= 2, "a V wave loads at most two tiles a step");
   auto dma_bases = [&](size_t b0, size_t b1, int buf) __attribute__((always_inline)) {
     const uint32_t dst0 = lds_u32 + (uint32_t)(buf * BUF_BYTES);
     if (kwave) {
-      const int t0 = (wk * PER) % NK;
+      const int t0 = (wk * PERK) % NK;
       const uint8_t* src = a.k + ((lane & 16) ? b1 : b0) + lane_off + 32 * t0;
       const uint32_t dst = dst0 + (uint32_t)((ta / 2) * KH_BYTES + t0 * 1024);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) lds_load16(src + 32 * i, dst + 1024u * i);
+      for (int i = 0; i < PERK; ++i) lds_load16(src + 32 * i, dst + 1024u * i);
     } else {
 #pragma unroll
-      for (int q = 0; q < PER / NDV; ++q) {
+      for (int q = 0; q < PERV / NDV; ++q) {
         const uint8_t* src = a.v + (q == 0 ? b0 : b1) + lane_off;
         const uint32_t dst = dst0 + (uint32_t)(2 * KH_BYTES + (ta + q) * VT_BYTES);
 #pragma unroll
@@ -230,12 +238,12 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // one past the range, keys counted at the tile's own place are past every
   // slot it copies that lies past the end.) K there only meets masked scores.
   auto dma_zero_tail = [&](int step, int buf) __attribute__((always_inline)) {
-    const int key_base = (t_lo + step * KT) * kPageSize;
+    const int key_base = step_tile(step) * kPageSize;
     if (kwave || key_base + KT * kPageSize <= L) return;
     uint8_t* const dst0 = lds_raw + buf * BUF_BYTES + 2 * KH_BYTES;
 #pragma unroll
-    for (int q = 0; q < PER / NDV; ++q) {
-      const int tt = (wk * PER) / NDV + q;
+    for (int q = 0; q < PERV / NDV; ++q) {
+      const int tt = (wk * PERV) / NDV + q;
       if (key_base + tt * kPageSize + vrow >= L) {
 #pragma unroll
         for (int dg = 0; dg < NDV; ++dg)
@@ -309,7 +317,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   };
   auto stage_store = [&](int step, int buf, auto set_c) __attribute__((always_inline)) {
     auto& stage = stage_regs[decltype(set_c)::value];
-    const int j0 = (t_lo + step * KT) * kPageSize;
+    const int t0 = step_tile(step);
+    const int j0 = t0 * kPageSize;
     uint8_t* const dst0 = lds_raw + buf * BUF_BYTES;
     // Slots past the sequence (arbitrary contents), and tiles past this
     // workgroup's range, become zeros. Only a step that reaches past either
@@ -319,7 +328,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       for (int l = 0; l < LOADS; ++l) {
         bool live = true;
         if constexpr (decltype(checked)::value) {
-          const int u = t_lo + step * KT + tt_of[l];
+          const int u = t0 + tt_of[l];
           live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
         }
         h2_t hv[8];
@@ -334,20 +343,14 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
         *reinterpret_cast<u32x4*>(dst0 + lds_off2[l]) = w1;
       }
     };
-    if ((step + 1) * KT <= n_tiles && j0 + KT * kPageSize <= L)
+    if (t0 - t_lo + KT <= n_tiles && j0 + KT * kPageSize <= L)
       put(BoolC<false>{});
     else
       put(BoolC<true>{});
   };
 
-  // The first steps' loads go out first: the Q loads and the token offset
-  // below do not hold them up.
-  if constexpr (DMA) {
-    for (int j = 0; j < NBUF - 1 && j < n_steps; ++j) dma_step(j, j);
-  } else {
-    if (n_steps > 0) stage_load(0, IntC<0>{});
-  }
-  // First token of sequence b in q and out.
+  // First token of sequence b in q and out (read before any cache load
+  // goes out, so that the wait for it waits for nothing else).
   int off = b;
   if (a.q_lens) {
     int sum = 0;
@@ -370,7 +373,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 
   // Q^T as the B operand: lane l holds row rr, dims 16 t + 8 hh .. + 7 of
   // k-step t. A negative scale flips q's sign.
-  float qk = a.qk_mult * (a.k_scale ? a.k_scale[g] : 1.0f);
+  typedef const __attribute__((address_space(4))) float* scale_ptr_t;
+  float qk = a.qk_mult * (a.k_scale ? ((scale_ptr_t)a.k_scale)[g] : 1.0f);
   const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
   // Scores of keys a row does not see are set to -inf before the softmax;
   // with a zero scale -inf * 0 would be NaN, so a zero multiplier becomes
@@ -378,24 +382,44 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // too small to change exp2 in fp32, and the weights stay exactly 1.
   qk = fabsf(qk) > 0.0f ? fabsf(qk) : __FLT_MIN__;
   constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
-  const int dcol = dh * (D / 2);
-  h8_t qb[NK];
+  // The Q loads go out before the first steps' cache loads, and Q is first
+  // read after the wait for those: the two latencies overlap, and the cache
+  // loads stay the youngest, as the explicit waits below count on. (A lane
+  // without a row reads its token clamped into the sequence, in bounds, and
+  // keeps zeros.)
+  u32x4 qx[NK];
   {
-    // (a lane without a row reads its token clamped into the sequence, in
-    // bounds, and keeps zeros)
     const uint8_t* qrow =
         a.q + ((size_t)(off + min(my_i, Qb - 1)) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
-    u32x4 x[NK];
 #pragma unroll
-    for (int t = 0; t < NK; ++t) x[t] = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
+    for (int t = 0; t < NK; ++t) qx[t] = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
+  }
+  if constexpr (DMA) {
+    // (the tile bases of all these steps first, with no branch between
+    // them: one wait for their scalar loads instead of one per step; an
+    // index clamped to 0 is in bounds when there are no steps)
+    size_t tb[NBUF - 1][2];
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) {
+      tb[j][0] = tile_base(max(min(step_tile(j) + ta, last_tile), 0));
+      tb[j][1] = tile_base(max(min(step_tile(j) + ta + 1, last_tile), 0));
+    }
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j)
+      if (j < n_steps) dma_bases(tb[j][0], tb[j][1], j);
+  } else {
+    if (n_steps > 0) stage_load(0, IntC<0>{});
+  }
+  h8_t qb[NK];
+  auto q_ready = [&]() __attribute__((always_inline)) {
     const uint32_t keep = my_row ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[t][e] = (x[t][e] & keep) ^ qflip;
-      qb[t] = __builtin_bit_cast(h8_t, x[t]);
+      for (int e = 0; e < 4; ++e) qx[t][e] = (qx[t][e] & keep) ^ qflip;
+      qb[t] = __builtin_bit_cast(h8_t, qx[t]);
     }
-  }
+  };
 
   constexpr float kNoMax = -1e30f;
   constexpr float kLazy = 8.0f;
@@ -444,6 +468,19 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qb[t], s1, 0, 0, 0);
       k0 = n0;
       k1 = n1;
+    }
+  };
+  // Scores of one 32-key half (PAIR): one chain of MFMAs, K read a k-step
+  // ahead (the partner wave on the SIMD fills the matrix unit between them).
+  auto scores1 = [&](const uint8_t* kh, f16v_t& s) __attribute__((always_inline)) {
+    h8_t k = frag(kh, 0);
+    s = f16v_t{};
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      h8_t n = k;
+      if (t + 1 < NK) n = frag(kh, t + 1);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qb[t], s, 0, 0, 0);
+      k = n;
     }
   };
   // Softmax and P.V of the 64 keys from key0 whose scores are st[0] (keys
@@ -539,10 +576,78 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // data, when the other half is needed; they are masked to weight 0. The
   // score registers live only inside the branch that uses them: a value
   // merged from a path that skips them would be zero-filled every step.)
+  // PAIR: the score exchange, after the step buffers: wave w's 16 scores
+  // per lane in four 1 KB blocks (floats 4 c .. 4 c + 3 of lane l at
+  // 1024 c + 16 l, conflict-free). The two waves meet there without a
+  // workgroup barrier: each score's lowest mantissa bit carries the parity
+  // of the pair's count of computed steps (a change of at most 2^-23
+  // relative, and both waves use the same tagged values), so the reader
+  // waits until every word it reads carries this step's tag. The blocks
+  // start out tagged 1 (before the first barrier), the first step writes
+  // tag 0. A word is read after it is written (the reader polls) and
+  // written again only after the next barrier, which the reader reaches
+  // after reading it.
+  uint8_t* const xs = lds_raw + NBUF * BUF_BYTES;
+  int x_count = 0;  // steps this pair has computed
+  if constexpr (PAIR) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<u32x4*>(xs + wave * 4096 + 1024 * c + 16 * lane) = u32x4{1u, 1u, 1u, 1u};
+  }
+  static_assert(!PAIR || WAVES * 4096 == (int)prefill_xchg_bytes(D, WAVES), "exchange size");
   auto compute = [&](int step, int buf) __attribute__((always_inline)) {
     const uint8_t* kb = lds_raw + buf * BUF_BYTES;
-    const int key0 = (t_lo + step * KT) * kPageSize;
-    if (active(key0) || active(key0 + 32)) {
+    const int key0 = step_tile(step) * kPageSize;
+    if constexpr (PAIR) {
+      // Both waves of a pair have the same rows, hence the same test.
+      if (active(key0) || active(key0 + 32)) {
+        const uint32_t tag = (uint32_t)(x_count & 1);
+        ++x_count;
+        f16v_t mine;
+        scores1(kb + dh * KH_BYTES, mine);
+        // (through a scalar: __builtin_bit_cast of a vector element lvalue
+        // reads element 0)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float x = mine[v];
+          mine[v] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~1u) | tag);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<f32x4_t*>(xs + wave * 4096 + 1024 * c + 16 * lane) =
+              f32x4_t{mine[4 * c], mine[4 * c + 1], mine[4 * c + 2], mine[4 * c + 3]};
+        asm volatile("" ::: "memory");  // the writes stay ahead of the polls
+        // The partner's scores: poll until all of them carry the tag. (A
+        // bound on the polls keeps every wave finite whatever happens; the
+        // partner writes within the same step, so it is never reached.)
+        typedef const volatile __attribute__((address_space(3))) u32x4 lds_vu4_t;
+        lds_vu4_t* src = (lds_vu4_t*)(__attribute__((address_space(3))) uint8_t*)(xs + (wave ^ 1) * 4096 + 16 * lane);
+        u32x4 w[4];
+        for (int polls = 0; polls < (1 << 20); ++polls) {
+          uint32_t bad = 0u;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            w[c] = src[64 * c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bad |= (w[c][e] & 1u) ^ tag;
+          }
+          if (__builtin_amdgcn_ballot_w64(bad != 0u) == 0) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        f16v_t other;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = w[c][e];
+            other[4 * c + e] = __builtin_bit_cast(float, x);
+          }
+        f16v_t st[2];
+        st[0] = dh ? other : mine;
+        st[1] = dh ? mine : other;
+        softmax_pv(st, kb + 2 * KH_BYTES, key0);
+      }
+    } else if (active(key0) || active(key0 + 32)) {
       f16v_t st[2];
       scores2(kb, kb + KH_BYTES, st[0], st[1]);
       softmax_pv(st, kb + 2 * KH_BYTES, key0);
@@ -553,19 +658,26 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     // Step s computes on buffer s % NBUF; its start issues the loads of step
     // s + NBUF - 1 (that buffer was last read in step s - 1, which every
     // wave has left at the barrier); its end waits for this wave's loads of
-    // step s + 1 (the PER loads of step s + 2 may stay in flight), zeroes
+    // step s + 1 (the loads of step s + 2 may stay in flight), zeroes
     // that step's tail, and meets the other waves at the barrier.
     static_assert(NBUF >= 2 && NBUF <= 4, "two to four step buffers");
     // Wait for this wave's loads of step `need`, with the loads of the steps
     // after it that were issued (up to `issued_to`, at most two) in flight.
     auto wait_step = [&](int need, int issued_to) __attribute__((always_inline)) {
       const int after = min(issued_to, n_steps - 1) - need;
-      if (after >= 2)
-        wait_vm(IntC<2 * PER>{});
-      else if (after == 1)
-        wait_vm(IntC<PER>{});
-      else
+      if (after >= 2) {
+        if (kwave)
+          wait_vm(IntC<2 * PERK>{});
+        else
+          wait_vm(IntC<2 * PERV>{});
+      } else if (after == 1) {
+        if (kwave)
+          wait_vm(IntC<PERK>{});
+        else
+          wait_vm(IntC<PERV>{});
+      } else {
         wait_vm(IntC<0>{});
+      }
     };
     if (n_steps > 0) {
       // (steps 0 .. NBUF - 2 were issued above; Q loads may follow them)
@@ -573,6 +685,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       dma_zero_tail(0, 0);
       wait_vm(IntC<63>{});
       barrier();
+      q_ready();
       int buf = 0;
       size_t nb0 = tile_at(NBUF - 1, ta), nb1 = tile_at(NBUF - 1, ta + 1);
       for (int step = 0; step < n_steps; ++step) {
@@ -599,6 +712,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       if (n_steps > 2) stage_load(2, IntC<1>{});
     }
     __syncthreads();
+    q_ready();
     // Step `step` reads LDS buffer step & 1; register set SET holds step + 1.
     auto step_body = [&](int step, auto set_c) __attribute__((always_inline)) {
       const int buf = step & 1;
@@ -628,7 +742,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
                                                __builtin_bit_cast(int, lsum), false, false);
     lsum = __builtin_bit_cast(float, (int)sw[0]) + __builtin_bit_cast(float, (int)sw[1]);
   }
-  const float vs = a.v_scale ? a.v_scale[g] : 1.0f;
+  const float vs = a.v_scale ? ((scale_ptr_t)a.v_scale)[g] : 1.0f;
   const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
   constexpr int DW = PAIR ? D / 2 : D;  // dims this wave writes
   constexpr int RS = 2 * DW + 16;      // LDS bytes per row

@@ -233,3 +233,71 @@ def test_decode_v_tile_reads_are_conflict_free(D):
         return out
     assert all(conflict_free(a, 8, 32) for a in addrs(D + 16))
     assert not all(conflict_free(a, 8, 32) for a in addrs(D + 8))
+
+
+# ---- prefill at D=256: the pairs' score exchange ----
+
+def test_prefill_pair_score_exchange():
+    """Waves 2 r and 2 r + 1 of an 8-wave D=256 workgroup share the row
+    block r and compute opposite 32-key halves, and sit on different SIMDs
+    (waves w and w + 4 share one); wave w writes its 16 scores per lane to
+    its own 4 KB (float 4 c + e of lane l at 1024 c + 16 l + 4 e) and reads
+    its partner's at the same offsets: every float is read by the lane of
+    the same row (the MFMA C layout puts row l % 32 in lane l), no two waves
+    write the same byte, each 16-lane pass of the 16-byte accesses is
+    conflict-free, and the region fits after the two 64 KB step buffers in
+    the 160 KB of LDS."""
+    waves, step_bytes, nbuf = 8, 2 * 4 * 16 * 256 * 2, 2
+    base = nbuf * step_bytes
+    written = {}
+    for w in range(waves):
+        for lane in range(64):
+            for c in range(4):
+                for e in range(4):
+                    a = base + w * 4096 + 1024 * c + 16 * lane + 4 * e
+                    assert a not in written
+                    written[a] = (w, lane, 4 * c + e)
+    for w in range(waves):
+        p = w ^ 1
+        assert p >> 1 == w >> 1 and (p & 1) != (w & 1) and p % 4 != w % 4
+        for lane in range(64):
+            for c in range(4):
+                for e in range(4):
+                    src_w, src_lane, idx = written[base + p * 4096 + 1024 * c + 16 * lane + 4 * e]
+                    assert (src_w, src_lane % 32, idx) == (p, lane % 32, 4 * c + e)
+        for c in range(4):
+            assert conflict_free([base + w * 4096 + 1024 * c + 16 * lane for lane in range(64)], 16, 16)
+    assert max(written) < 160 * 1024 and base + waves * 4096 == 160 * 1024
+
+
+def pair_exchange_reads(active, tag_of):
+    """The pair handshake over a run of steps: the writer's block starts
+    tagged 1; at each step both waves of the pair compute or both skip
+    (same rows); a computing wave writes all its words with tag_of(k, step)
+    (k: steps computed so far) and accepts the partner's words once they
+    carry that tag. Returns, per computing step, the step whose data a
+    reader polling right away (before the partner's write lands) would
+    accept: None when it would wait, as it must."""
+    block = ("init", 1)  # (step written, tag)
+    accepted = []
+    k = 0
+    for step, act in enumerate(active):
+        if not act:
+            continue
+        tag = tag_of(k, step)
+        accepted.append(block[0] if block[1] == tag else None)
+        block = (step, tag)  # the partner's write lands
+        k += 1
+    return accepted
+
+
+@pytest.mark.parametrize("pattern", ["all", "gap", "gaps", "late"])
+def test_prefill_pair_handshake_never_takes_old_scores(pattern):
+    """With the tag = parity of the count of computed steps, a reader never
+    accepts a block left from an earlier step, whatever steps the pair skips;
+    a tag from the step index (planted mistake) does, after a skipped step."""
+    active = {"all": [1] * 8, "gap": [1, 1, 0, 1, 1], "gaps": [1, 0, 1, 0, 0, 1, 1, 0, 1],
+              "late": [0, 0, 0, 1, 1, 1]}[pattern]
+    assert all(a is None for a in pair_exchange_reads(active, lambda k, step: k & 1))
+    wrong = pair_exchange_reads(active, lambda k, step: step & 1)
+    assert all(a is None for a in wrong) == (pattern == "all")
