@@ -349,13 +349,24 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       put(BoolC<true>{});
   };
 
+  // The tile bases of the first steps (their scalar loads, with no branch
+  // between them, are in flight together with the offset's loads below; an
+  // index clamped to 0 is in bounds when there are no steps).
+  size_t tb[NBUF - 1][2];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) {
+      tb[j][0] = tile_base(max(min(step_tile(j) + ta, last_tile), 0));
+      tb[j][1] = tile_base(max(min(step_tile(j) + ta + 1, last_tile), 0));
+    }
+  }
   // First token of sequence b in q and out (read before any cache load
   // goes out, so that the wait for it waits for nothing else).
   int off = b;
   if (a.q_lens) {
     int sum = 0;
     for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
-    off = wave_sum_int(sum);
+    off = wave_sum_i(sum);
   }
 
   // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
@@ -395,15 +406,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     for (int t = 0; t < NK; ++t) qx[t] = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
   }
   if constexpr (DMA) {
-    // (the tile bases of all these steps first, with no branch between
-    // them: one wait for their scalar loads instead of one per step; an
-    // index clamped to 0 is in bounds when there are no steps)
-    size_t tb[NBUF - 1][2];
-#pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) {
-      tb[j][0] = tile_base(max(min(step_tile(j) + ta, last_tile), 0));
-      tb[j][1] = tile_base(max(min(step_tile(j) + ta + 1, last_tile), 0));
-    }
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j)
       if (j < n_steps) dma_bases(tb[j][0], tb[j][1], j);
