@@ -630,7 +630,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
         typedef const volatile __attribute__((address_space(3))) u32x4 lds_vu4_t;
         lds_vu4_t* src = (lds_vu4_t*)(__attribute__((address_space(3))) uint8_t*)(xs + (wave ^ 1) * 4096 + 16 * lane);
         u32x4 w[4];
-        for (int polls = 0; polls < (1 << 20); ++polls) {
+        uint32_t stale = ~0u;  // no poll yet; left nonzero if the bound ends the polls
+        for (int polls = 0; polls < (1 << 20) && stale != 0u; ++polls) {
           uint32_t bad = 0u;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -638,15 +639,17 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) bad |= (w[c][e] & 1u) ^ tag;
           }
-          if (__builtin_amdgcn_ballot_w64(bad != 0u) == 0) break;
-          __builtin_amdgcn_s_sleep(1);
+          stale = __builtin_amdgcn_ballot_w64(bad != 0u) != 0 ? 1u : 0u;
+          if (stale != 0u) __builtin_amdgcn_s_sleep(1);
         }
+        // (should the bound ever end the polls, the scores become NaN, so the
+        // rows' output shows it instead of silently using old scores)
         f16v_t other;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t x = w[c][e];
+            const uint32_t x = stale != 0u ? 0x7fc00000u : w[c][e];
             other[4 * c + e] = __builtin_bit_cast(float, x);
           }
         f16v_t st[2];
