@@ -807,8 +807,7 @@ hipError_t launch_prefill_kv(int head_dim, int waves, dim3 grid, size_t lds, hip
   }
   PDA_PCASE(128, 4)
   PDA_PCASE(128, 8)
-  PDA_PCASE(256, 4)
-  PDA_PCASE(256, 8)
+  PDA_PCASE(256, 8)  // (D=256 always takes 8 waves)
 #undef PDA_PCASE
   return hipErrorInvalidValue;
 }
