@@ -466,6 +466,8 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
         n0 = frag(kb0, t + 1);
         n1 = frag(kb1, t + 1);
       }
+      // (the next k-step's reads stay ahead of this one's MFMAs)
+      __builtin_amdgcn_sched_barrier(0);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qb[t], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qb[t], s1, 0, 0, 0);
       k0 = n0;
@@ -556,20 +558,36 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
           lsum = __builtin_amdgcn_fdot2(h2_t{pb[h][ks][e], pb[h][ks][e + 1]}, one2, lsum, false);
       }
     }
+    // V^T fragment of tile g = 2 h + ks, dims dcol + 32 dt
+    auto vfrag = [&](int g, int dt) __attribute__((always_inline)) {
+      const uint8_t* vt = vb + g * VT_BYTES + (dcol / 32) * 1024 + v_lane + 1024 * dt;
+      const h4_t lo = tr_read(vt);
+      const h4_t hi = tr_read(vt + 512);
+      return h8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    if constexpr (!PAIR) {
+      // (each tile's fragments read one tile ahead of their MFMAs; the
+      // scheduling barriers keep them there)
+      h8_t vf[2][NDT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+      for (int dt = 0; dt < NDT; ++dt) vf[0][dt] = vfrag(0, dt);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // tile 2 h + ks; its block of dims dcol + 32 dt
-        const uint8_t* vt = vb + (2 * h + ks) * VT_BYTES + (dcol / 32) * 1024 + v_lane;
+      for (int g = 0; g < 4; ++g) {
+        if (g + 1 < 4) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const h4_t lo = tr_read(vt + 1024 * dt);
-          const h4_t hi = tr_read(vt + 1024 * dt + 512);
-          const h8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[h][ks], o[dt], 0, 0, 0);
+          for (int dt = 0; dt < NDT; ++dt) vf[(g + 1) & 1][dt] = vfrag(g + 1, dt);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[g & 1][dt], pb[g >> 1][g & 1], o[dt], 0, 0, 0);
       }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag(g, dt), pb[g >> 1][g & 1], o[dt], 0, 0, 0);
     }
   };
 
