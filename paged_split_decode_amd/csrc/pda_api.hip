@@ -392,17 +392,20 @@ pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArg
                          hipStream_t stream) {
   hipError_t e;
   if (p.prefill) {
-    const dim3 pgrid(p.row_tiles, d->num_kv_heads, d->batch);
+    // (items: token blocks x KV heads x sequences; the launcher sizes the grid)
+    const dim3 items(p.row_tiles, d->num_kv_heads, d->batch);
+    const int cus = device_cu_count();
+    if (cus <= 0) return fail(PDA_ERR_DEVICE, "cannot read the device's CU count");
     const int waves = p.threads / 64;
     switch (kv_kind(d->kv_dtype)) {
       case pda::kKvF16:
-        e = pda::launch_prefill_f16(d->head_dim, waves, pgrid, p.lds, stream, args);
+        e = pda::launch_prefill_f16(d->head_dim, waves, items, cus, p.lds, stream, args);
         break;
       case pda::kKvFp8:
-        e = pda::launch_prefill_fp8(d->head_dim, waves, pgrid, p.lds, stream, args);
+        e = pda::launch_prefill_fp8(d->head_dim, waves, items, cus, p.lds, stream, args);
         break;
       default:
-        e = pda::launch_prefill_i8(d->head_dim, waves, pgrid, p.lds, stream, args);
+        e = pda::launch_prefill_i8(d->head_dim, waves, items, cus, p.lds, stream, args);
         break;
     }
     if (e != hipSuccess) return fail(PDA_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
@@ -476,6 +479,8 @@ pda::DecodeArgs make_args(const void* q, const void* k, const void* v, const int
   a.balanced = p.balanced;
   a.chunks = p.chunks;
   a.min_chunk = p.min_chunk;
+  a.prefill_blocks = p.prefill ? p.row_tiles : 0;
+  a.prefill_items = p.prefill ? p.row_tiles * d->num_kv_heads * d->batch : 0;
   return a;
 }
 

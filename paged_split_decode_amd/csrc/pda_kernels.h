@@ -90,6 +90,10 @@ struct DecodeArgs {
   int32_t chunks;
   int32_t min_chunk;           // fewest 16-key tiles in a chunk
   int32_t* meta;               // [T][4]
+  // Prefill kernel: token blocks per (sequence, KV head), and items (token
+  // blocks x KV heads x sequences) shared by its workgroups.
+  int32_t prefill_blocks;
+  int32_t prefill_items;
 };
 
 // Launch the decode kernel for (head_dim, kv_kind, rows_per_wave) with
@@ -187,11 +191,11 @@ inline size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
   const size_t out = prefill_out_lds_bytes(head_dim, waves);
   return steps > out ? steps : out;
 }
-hipError_t launch_prefill_f16(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_f16(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);
-hipError_t launch_prefill_fp8(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_fp8(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);
-hipError_t launch_prefill_i8(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_i8(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                              const DecodeArgs& args);
 
 // Host-side error state shared by every entry point: records a message for

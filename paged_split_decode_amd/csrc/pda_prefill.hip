@@ -3,17 +3,17 @@
 
 namespace pda {
 
-hipError_t launch_prefill_f16(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_f16(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                               const DecodeArgs& args) {
-  return launch_prefill_kv<kKvF16>(head_dim, waves, grid, lds, stream, args);
+  return launch_prefill_kv<kKvF16>(head_dim, waves, items, cus, lds, stream, args);
 }
-hipError_t launch_prefill_fp8(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_fp8(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                               const DecodeArgs& args) {
-  return launch_prefill_kv<kKvFp8>(head_dim, waves, grid, lds, stream, args);
+  return launch_prefill_kv<kKvFp8>(head_dim, waves, items, cus, lds, stream, args);
 }
-hipError_t launch_prefill_i8(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_i8(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                              const DecodeArgs& args) {
-  return launch_prefill_kv<kKvI8>(head_dim, waves, grid, lds, stream, args);
+  return launch_prefill_kv<kKvI8>(head_dim, waves, items, cus, lds, stream, args);
 }
 
 }  // namespace pda

@@ -85,7 +85,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane0 = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // At D=256 (8 waves) waves 2 r and 2 r + 1 share the rows 32 r .. + 31:
   // each computes the scores of one 32-key half of a step (all D dims) and
@@ -96,732 +96,782 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // share one), so that while one pair waits for its scores, the other
   // pair's wave on the same SIMD keeps the matrix unit busy.
   constexpr bool PAIR = D == 256 && WAVES == 8;
+  // Persistent workgroups at D=128 (below); at D=256 one item per workgroup
+  // measured faster.
+  constexpr bool PERSIST = !PAIR;
   const int rg = PAIR ? (wave >> 1) : wave;  // row block
   const int dh = PAIR ? (wave & 1) : 0;      // key half of the scores, output dim half
-  // Workgroup -> (token block, KV head, sequence), XCD-aware: the dispatcher
-  // hands workgroups to the 8 XCDs in turn (id % 8), and each XCD has its own
-  // L2. The token blocks of one (sequence, KV head) read the same keys, so
-  // they should run on one XCD at about the same time: XCD x takes a
-  // contiguous run of logical indices (token block fastest), in dispatch
-  // order. Within a (sequence, KV head) the blocks with the most keys go
-  // first.
-  int g, b, blk;
-  {
-    const uint32_t nx = gridDim.x, ny = gridDim.y;
-    const uint32_t n = nx * ny * gridDim.z;
-    const uint32_t p = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-    const uint32_t xcd = p & 7u, k = p >> 3;
-    const uint32_t lg = xcd * (n >> 3) + min(xcd, n & 7u) + k;
-    const uint32_t rest = lg / nx;
-    blk = (int)(nx - 1 - (lg - rest * nx));
-    g = (int)(rest % ny);
-    b = (int)(rest / ny);
-  }
-  const int dcol = dh * (D / 2);  // first output dim of this wave
-  const int G = a.group;
-  const int Hq = a.num_q_heads;
-  const int BQ = a.rows / G;                   // tokens per workgroup
-  const int L = a.seq_lens[b];
-  const int Qb = a.q_lens ? a.q_lens[b] : 1;
-  const int i0 = blk * BQ;
-  if (i0 >= Qb) return;  // the whole workgroup: no barrier is skipped by a part of it
-  const int pos0 = L - Qb;  // position of token 0
-  const int W = a.window;
-  auto lo_of = [&](int pos) { return W > 0 ? max(0, pos - W + 1) : 0; };
-
-  // Key range of the workgroup, in tiles: [lo of its first token, its last
-  // token's position].
-  const int ilast = min(Qb, i0 + BQ) - 1;
-  const int khi = pos0 + ilast;
-  const int klo = lo_of(pos0 + i0);
-  const int t_lo = klo / kPageSize;
-  const int n_tiles = khi >= 0 ? khi / kPageSize - t_lo + 1 : 0;
-  const int n_steps = (n_tiles + KT - 1) / KT;
-
-  // Wave-uniform summaries of this wave's rows 32 rg .. + 31 for the skip /
-  // unmasked tests: their tokens run from i_a to i_b (rows past the
-  // workgroup's, tokens past the sequence's and negative positions left
-  // out), and the bounds of a token's keys grow with its position.
-  int lo_min = 0x7fffffff, lo_max = 0, hi_min = 0x7fffffff, hi_max = -1;
-  {
-    const int r_b = min(32 * rg + 31, a.rows - 1);
-    const int i_a = max(i0 + (32 * rg) / G, -pos0);
-    const int i_b = min(i0 + r_b / G, Qb - 1);
-    if (32 * rg <= r_b && i_a <= i_b) {
-      hi_min = pos0 + i_a;
-      hi_max = pos0 + i_b;
-      lo_min = lo_of(hi_min);
-      lo_max = lo_of(hi_max);
-    }
-  }
-
-  // Cache addressing (as in the decode kernel): tile u of sequence b starts
-  // at bt[u >> tile_shift] * page_bytes + (u & mask) * 16 * key_stride; slot
-  // j of head g at j * key_stride + g * head_stride inside it.
-  typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
-  const bt_ptr_t bt = (bt_ptr_t)(a.block_table + (size_t)b * a.max_pages);
-  const int tshift = a.tile_shift;
-  const int tmask = (1 << tshift) - 1;
-  const uint32_t key_stride = a.key_stride;
-  const uint32_t head_off = (uint32_t)g * a.head_stride;
-  auto tile_base = [&](int u) -> size_t {
-    return (size_t)bt[u >> tshift] * a.page_bytes + (size_t)((u & tmask) * kPageSize) * key_stride;
-  };
-
-  // First tile of step `step` (past the last step: tiles past the range,
-  // which tile_at clamps).
-  auto step_tile = [&](int step) __attribute__((always_inline)) { return t_lo + step * KT; };
-  // Tile tt of step `step`; tiles past the workgroup's range are read from
-  // its last tile (in bounds; all their keys are masked).
-  const int last_tile = t_lo + n_tiles - 1;
-  auto tile_at = [&](int step, int tt) __attribute__((always_inline)) {
-    return tile_base(min(step_tile(step) + tt, last_tile));
-  };
-  const uint32_t lds_u32 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds_raw;
-  // One direct 16-byte load per lane into LDS at byte dst + 16 lane (dst
-  // wave-uniform, in M0; one wait state after M0 is written). Written as asm
-  // so that the compiler's wait insertion does not track an LDS write in
-  // flight: it would make LDS reads wait for every outstanding load,
-  // including those of the steps ahead. The waits this pipeline needs are
-  // explicit (wait_vm before each barrier).
-  auto lds_load16 = [](const uint8_t* src, uint32_t dst) __attribute__((always_inline)) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
-                 : "memory");
-  };
-
-  // fp16 caches, direct loads: waves [0, WAVES / 2) load K, the others V, in
-  // whole 1 KB blocks, PERK per K wave and PERV per V wave and step; a K
-  // wave's blocks lie in one half, a V wave's cover whole tiles. Each lane's
-  // byte offset within a tile is fixed: K, key lane % 16 of the lane's tile
-  // (lane / 16 % 2 of the half) at dims 8 (lane / 32) ..; V, the key row of
-  // slot `lane` at dims 8 (lane % 4) ...
-  constexpr int PERK = 2 * NK / (WAVES / 2);
-  constexpr int PERV = KT * NDV / (WAVES / 2);
-  static_assert(NK % PERK == 0 && PERV % NDV == 0, "a wave's blocks: one half, or whole tiles");
-  const bool kwave = wave < WAVES / 2;
-  const int wk = kwave ? wave : wave - WAVES / 2;
-  const int vrow = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 2) & 3);
-  const uint32_t lane_off = kwave ? (uint32_t)(lane & 15) * key_stride + head_off + 16u * (lane >> 5)
-                                  : (uint32_t)vrow * key_stride + head_off + 16u * (lane & 3);
-  // The tiles a wave loads each step: a K wave tiles ta and ta + 1 (its
-  // half), a V wave tiles ta .. ta + PERV / NDV - 1 (at most two). Inside the
-  // step loop their bases come from the block table before the barrier of
-  // the step before, so the scalar loads' latency hides under the barrier.
-  const int ta = kwave ? 2 * ((wk * PERK) / NK) : (wk * PERV) / NDV;
-  static_assert(PERV / NDV <= 2, "a V wave loads at most two tiles a step");
-  auto dma_bases = [&](size_t b0, size_t b1, int buf) __attribute__((always_inline)) {
-    const uint32_t dst0 = lds_u32 + (uint32_t)(buf * BUF_BYTES);
-    if (kwave) {
-      const int t0 = (wk * PERK) % NK;
-      const uint8_t* src = a.k + ((lane & 16) ? b1 : b0) + lane_off + 32 * t0;
-      const uint32_t dst = dst0 + (uint32_t)((ta / 2) * KH_BYTES + t0 * 1024);
-#pragma unroll
-      for (int i = 0; i < PERK; ++i) lds_load16(src + 32 * i, dst + 1024u * i);
-    } else {
-#pragma unroll
-      for (int q = 0; q < PERV / NDV; ++q) {
-        const uint8_t* src = a.v + (q == 0 ? b0 : b1) + lane_off;
-        const uint32_t dst = dst0 + (uint32_t)(2 * KH_BYTES + (ta + q) * VT_BYTES);
-#pragma unroll
-        for (int dg = 0; dg < NDV; ++dg) lds_load16(src + 64 * dg, dst + 1024u * dg);
-      }
-    }
-  };
-  auto dma_step = [&](int step, int buf) __attribute__((always_inline)) {
-    dma_bases(tile_at(step, ta), tile_at(step, ta + 1), buf);
-  };
-  // After a V wave's loads of a step have landed: V slots of keys at or past
-  // the sequence's end hold whatever the page has there (a weight 0 times a
-  // NaN would spoil P.V), so they become zeros. (For a tile read in place of
-  // one past the range, keys counted at the tile's own place are past every
-  // slot it copies that lies past the end.) K there only meets masked scores.
-  auto dma_zero_tail = [&](int step, int buf) __attribute__((always_inline)) {
-    const int key_base = step_tile(step) * kPageSize;
-    if (kwave || key_base + KT * kPageSize <= L) return;
-    uint8_t* const dst0 = lds_raw + buf * BUF_BYTES + 2 * KH_BYTES;
-#pragma unroll
-    for (int q = 0; q < PERV / NDV; ++q) {
-      const int tt = (wk * PERV) / NDV + q;
-      if (key_base + tt * kPageSize + vrow >= L) {
-#pragma unroll
-        for (int dg = 0; dg < NDV; ++dg)
-          *reinterpret_cast<u32x4*>(dst0 + tt * VT_BYTES + dg * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  // s_waitcnt with vmcnt(VM) and lgkmcnt(0) (expcnt untouched).
-  // The empty asm after it keeps the compiler from moving LDS accesses (the
-  // zeroing of a step's tail, say) above the wait for the direct loads they
-  // depend on; the loads' asm carries a memory clobber for the same reason.
-  auto wait_vm = [](auto vm_c) __attribute__((always_inline)) {
-    constexpr int VM = decltype(vm_c)::value;
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-    asm volatile("" ::: "memory");
-  };
-  // Workgroup barrier without a memory fence (the waits before it are
-  // explicit); the empty asm statements keep the compiler from moving memory
-  // accesses across it.
-  auto barrier = []() __attribute__((always_inline)) {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // 1-byte codes, register staging: chunk c = tid + NTHREADS l of a step is
-  // K or V (kv), key row r64 of the step's 64, dims 16 j .. + 15; its 16
-  // codes become two fp16 slots (K: k-step j of the row's half, slot
-  // r64 % 32 and that + 32; V: block j / 2 of the row's tile, slots s and
-  // s + 1). All of that is fixed per thread; each step only moves the
-  // (scalar) tile bases.
-  uint32_t src_off[LOADS];
-  uint32_t lds_off[LOADS], lds_off2[LOADS];
-  int row_of[LOADS], tt_of[LOADS];
-  bool is_v[LOADS];
-  if constexpr (!DMA) {
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      const int c = tid + NTHREADS * l;
-      const int kv = c / (CHUNKS / 2);
-      const int rem = c - kv * (CHUNKS / 2);
-      const int r64 = rem / (D / 16), j = rem % (D / 16);
-      tt_of[l] = r64 >> 4;
-      row_of[l] = r64 & 15;
-      is_v[l] = kv != 0;
-      src_off[l] = (uint32_t)row_of[l] * key_stride + head_off + 16u * j;
-      if (!kv) {
-        lds_off[l] = (uint32_t)((r64 >> 5) * KH_BYTES + j * 1024 + 16 * (r64 & 31));
-        lds_off2[l] = lds_off[l] + 512;
-      } else {
-        const int r = r64 & 15;
-        const int slot = 32 * (r >> 3) + 16 * ((r >> 2) & 1) + 4 * (r & 3) + 2 * (j & 1);
-        lds_off[l] = (uint32_t)(2 * KH_BYTES + tt_of[l] * VT_BYTES + (j >> 1) * 1024 + 16 * slot);
-        lds_off2[l] = lds_off[l] + 16;
-      }
-    }
-  }
-  uint32_t stage_regs[NREG][LOADS][4];
-  auto stage_load = [&](int step, auto set_c) __attribute__((always_inline)) {
-    auto& stage = stage_regs[decltype(set_c)::value];
-    size_t base[KT];
-#pragma unroll
-    for (int tt = 0; tt < KT; ++tt) base[tt] = tile_at(step, tt);
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      const uint8_t* src = (is_v[l] ? a.v : a.k) + base[tt_of[l]] + src_off[l];
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) stage[l][e] = x[e];
-    }
-  };
-  auto stage_store = [&](int step, int buf, auto set_c) __attribute__((always_inline)) {
-    auto& stage = stage_regs[decltype(set_c)::value];
-    const int t0 = step_tile(step);
-    const int j0 = t0 * kPageSize;
-    uint8_t* const dst0 = lds_raw + buf * BUF_BYTES;
-    // Slots past the sequence (arbitrary contents), and tiles past this
-    // workgroup's range, become zeros. Only a step that reaches past either
-    // needs the per-slot test (wave-uniform).
-    auto put = [&](auto checked) __attribute__((always_inline)) {
-#pragma unroll
-      for (int l = 0; l < LOADS; ++l) {
-        bool live = true;
-        if constexpr (decltype(checked)::value) {
-          const int u = t0 + tt_of[l];
-          live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
-        }
-        h2_t hv[8];
-        to_pairs<KV>(stage[l], hv);
-        u32x4 w0, w1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0[e] = live ? __builtin_bit_cast(uint32_t, hv[e]) : 0u;
-          w1[e] = live ? __builtin_bit_cast(uint32_t, hv[4 + e]) : 0u;
-        }
-        *reinterpret_cast<u32x4*>(dst0 + lds_off[l]) = w0;
-        *reinterpret_cast<u32x4*>(dst0 + lds_off2[l]) = w1;
-      }
-    };
-    if (t0 - t_lo + KT <= n_tiles && j0 + KT * kPageSize <= L)
-      put(BoolC<false>{});
-    else
-      put(BoolC<true>{});
-  };
-
-  // The tile bases of the first steps (their scalar loads, with no branch
-  // between them, are in flight together with the offset's loads below; an
-  // index clamped to 0 is in bounds when there are no steps).
-  size_t tb[NBUF - 1][2];
-  if constexpr (DMA) {
-#pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) {
-      tb[j][0] = tile_base(max(min(step_tile(j) + ta, last_tile), 0));
-      tb[j][1] = tile_base(max(min(step_tile(j) + ta + 1, last_tile), 0));
-    }
-  }
-  // First token of sequence b in q and out (read before any cache load
-  // goes out, so that the wait for it waits for nothing else).
-  int off = b;
-  if (a.q_lens) {
-    int sum = 0;
-    for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
-    off = wave_sum_i(sum);
-  }
-
-  // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
-  // with h = l / 32; B: column l % 32, same k; C: column l % 32, rows
-  // 8 j + 4 h + i in element 4 j + i). So lane l works on query row rr = l % 32
-  // of this wave's 32 rows; lanes l and l + 32 share the row.
-  const int rr = lane & 31;
-  const int hh = lane >> 5;
-  const int myr = 32 * rg + rr;  // the workgroup row of this lane
-  const int my_i = i0 + myr / G;
-  const bool my_row = myr < a.rows && my_i < Qb;
-  const int my_pos = pos0 + my_i;
-  const int my_lo = (my_row && my_pos >= 0) ? lo_of(my_pos) : 0;
-  const int my_hi = (my_row && my_pos >= 0) ? my_pos : -1;
-
-  // Q^T as the B operand: lane l holds row rr, dims 16 t + 8 hh .. + 7 of
-  // k-step t. A negative scale flips q's sign.
-  typedef const __attribute__((address_space(4))) float* scale_ptr_t;
-  float qk = a.qk_mult * (a.k_scale ? ((scale_ptr_t)a.k_scale)[g] : 1.0f);
-  const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
-  // Scores of keys a row does not see are set to -inf before the softmax;
-  // with a zero scale -inf * 0 would be NaN, so a zero multiplier becomes
-  // the smallest normal float: every product with a finite score is then
-  // too small to change exp2 in fp32, and the weights stay exactly 1.
-  qk = fabsf(qk) > 0.0f ? fabsf(qk) : __FLT_MIN__;
-  constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
-  // The Q loads go out before the first steps' cache loads, and Q is first
-  // read after the wait for those: the two latencies overlap, and the cache
-  // loads stay the youngest, as the explicit waits below count on. (A lane
-  // without a row reads its token clamped into the sequence, in bounds, and
-  // keeps zeros.)
-  u32x4 qx[NK];
-  {
-    const uint8_t* qrow =
-        a.q + ((size_t)(off + min(my_i, Qb - 1)) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
-#pragma unroll
-    for (int t = 0; t < NK; ++t) qx[t] = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
-  }
-  if constexpr (DMA) {
-#pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j)
-      if (j < n_steps) dma_bases(tb[j][0], tb[j][1], j);
-  } else {
-    if (n_steps > 0) stage_load(0, IntC<0>{});
-  }
-  h8_t qb[NK];
-  auto q_ready = [&]() __attribute__((always_inline)) {
-    const uint32_t keep = my_row ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int t = 0; t < NK; ++t) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qx[t][e] = (qx[t][e] & keep) ^ qflip;
-      qb[t] = __builtin_bit_cast(h8_t, qx[t]);
-    }
-  };
-
-  constexpr float kNoMax = -1e30f;
-  constexpr float kLazy = 8.0f;
-  float m = kNoMax, mx = kNoMax, lsum = 0.0f;
-  f16v_t o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f16v_t{};
-
-  typedef short s4_t __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s4_t lds_s4_t;
-  auto tr_read = [&](const uint8_t* src) __attribute__((always_inline)) {
-    return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s4_t*)(__attribute__((address_space(3))) uint8_t*)src));
-  };
-  const int q16 = lane >> 4, i16 = lane & 15;  // 16-lane group and lane in it
-  // The transposing V reads: lane l takes 4 dims (8 bytes) of key row
-  // 4 hh + i16 / 4 (+ 8 for the upper 8 keys of a k-step) at dims
-  // 16 (q16 % 2) + 4 (i16 % 4) of a 32-dim group: slot
-  // 16 hh + 4 (i16 / 4) + 2 (q16 % 2) + (i16 % 4) / 2 of the group's block,
-  // second 8 bytes when i16 is odd.
-  const uint32_t v_lane = 16u * (16 * hh + 4 * (i16 >> 2) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
-                          8u * (i16 & 1);
-
-  // Whether this wave has work on the 32 keys from key0 (wave-uniform).
-  auto active = [&](int key0) { return hi_max >= 0 && key0 <= hi_max && key0 + 31 >= lo_min; };
-  // S^T[key][row] of 32 keys: lane l gets row rr, keys 8 j + 4 hh + i in
-  // st[4 j + i]. The two halves' chains of dependent MFMAs are interleaved
-  // (scores2), with each k-step's K fragments read one step ahead. (At D=256,
-  // one wave per SIMD, this order measured 0.8% faster than computing each
-  // half's scores just before its softmax; its extra registers go to AGPRs.)
-  auto frag = [&](const uint8_t* kh, int t) __attribute__((always_inline)) {
-    return *reinterpret_cast<const h8_t*>(kh + 1024 * t + 16 * lane);
-  };
-  auto scores2 = [&](const uint8_t* kb0, const uint8_t* kb1, f16v_t& s0, f16v_t& s1) __attribute__((always_inline)) {
-    h8_t k0 = frag(kb0, 0), k1 = frag(kb1, 0);
-    s0 = f16v_t{};
-    s1 = f16v_t{};
-#pragma unroll
-    for (int t = 0; t < NK; ++t) {
-      h8_t n0 = k0, n1 = k1;
-      if (t + 1 < NK) {
-        n0 = frag(kb0, t + 1);
-        n1 = frag(kb1, t + 1);
-      }
-      // (the next k-step's reads stay ahead of this one's MFMAs)
-      __builtin_amdgcn_sched_barrier(0);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qb[t], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qb[t], s1, 0, 0, 0);
-      k0 = n0;
-      k1 = n1;
-    }
-  };
-  // Scores of one 32-key half (PAIR): one chain of MFMAs, K read a k-step
-  // ahead (the partner wave on the SIMD fills the matrix unit between them).
-  auto scores1 = [&](const uint8_t* kh, f16v_t& s) __attribute__((always_inline)) {
-    h8_t k = frag(kh, 0);
-    s = f16v_t{};
-#pragma unroll
-    for (int t = 0; t < NK; ++t) {
-      h8_t n = k;
-      if (t + 1 < NK) n = frag(kh, t + 1);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qb[t], s, 0, 0, 0);
-      k = n;
-    }
-  };
-  // Softmax and P.V of the 64 keys from key0 whose scores are st[0] (keys
-  // key0 ..) and st[1] (key0 + 32 ..). Where some row of the wave sees only
-  // part of the keys (a uniform test), the scores of keys a row does not see
-  // become -inf first: they leave the maximum alone and get weight
-  // exp2(-inf) = 0. Every other step runs no per-key test. One maximum and
-  // one rescale test cover both halves, so the weights and P.V of both run in
-  // one block (the exponentials of one half can issue under the other's
-  // matrix instructions).
-  auto softmax_pv = [&](f16v_t (&st)[2], const uint8_t* vb, int key0) __attribute__((always_inline)) {
-    if (!(key0 >= lo_max && key0 + 63 <= hi_min)) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // lane's key of slot v: key0 + 32 h + 8 (v / 4) + 4 hh + v % 4
-        const int d_lo = my_lo - key0 - 32 * h - 4 * hh, d_hi = my_hi - key0 - 32 * h - 4 * hh;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = 8 * (v >> 2) + (v & 3);
-          st[h][v] = (c >= d_lo && c <= d_hi) ? st[h][v] : -INFINITY;
-        }
-      }
-    }
-    float mt;
+  // One item (token block, KV head, sequence) per call of `item`, by its
+  // logical index lg. Dispatch slot v goes to XCD v % 8 (the dispatcher
+  // hands workgroups to the 8 XCDs in turn), and each XCD has its own L2;
+  // the token blocks of one (sequence, KV head) read the same keys, so they
+  // should run on one XCD at about the same time: slot v takes logical index
+  // lg such that XCD x owns a contiguous run of them.
+  auto item = [&](const uint32_t lg) __attribute__((always_inline)) {
+    // (the lane index made opaque per item: what derives from it is computed
+    // inside the item, where it is used, not once before the item loop and
+    // kept in registers through every item)
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    // Item lg -> (token block, KV head, sequence): token block fastest, the
+    // blocks with the most keys first.
+    int g, b, blk;
     {
-      float a[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          a[4 * h + q] = fmaxf(fmaxf(st[h][4 * q], st[h][4 * q + 1]),
-                               fmaxf(st[h][4 * q + 2], st[h][4 * q + 3]));
-      mt = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
-                 fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+      const uint32_t nx = (uint32_t)a.prefill_blocks, ny = (uint32_t)a.num_kv_heads;
+      const uint32_t rest = lg / nx;
+      blk = (int)(nx - 1 - (lg - rest * nx));
+      g = (int)(rest % ny);
+      b = (int)(rest / ny);
     }
-    {  // the other half of the row's keys sits in lane l ^ 32
-      auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mt),
-                                                 __builtin_bit_cast(int, mt), false, false);
-      mt = fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
-    }
-    mt = mt == -INFINITY ? kNoMax : qk * mt;
-    mx = fmaxf(mx, mt);
-    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mx);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-      m = mx;
-    }
-    // O^T[dim][row] += V^T . P^T over four 16-key k-steps. k-step 2 h + ks
-    // takes the lane's keys of half h, j = 2 ks, 2 ks + 1 (slots 8 hh + e:
-    // key 32 h + 16 ks + 4 hh + e, then 32 h + 16 ks + 8 + 4 hh + e); V^T's A
-    // operand uses the same key order: two transposing reads of 4
-    // consecutive key rows at this lane's dim. The denominator adds the same
-    // fp16 weights that P.V multiplies V by (v_dot2 with ones: each fp16
-    // value enters the fp32 sum exactly).
-    const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-    h8_t pb[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pb[h][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[h][8 * ks + e], qk, -m));
-          pb[h][ks][4 + e] =
-              (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[h][8 * ks + 4 + e], qk, -m));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          lsum = __builtin_amdgcn_fdot2(h2_t{pb[h][ks][e], pb[h][ks][e + 1]}, one2, lsum, false);
-      }
-    }
-    // V^T fragment of tile g = 2 h + ks, dims dcol + 32 dt
-    auto vfrag = [&](int g, int dt) __attribute__((always_inline)) {
-      const uint8_t* vt = vb + g * VT_BYTES + (dcol / 32) * 1024 + v_lane + 1024 * dt;
-      const h4_t lo = tr_read(vt);
-      const h4_t hi = tr_read(vt + 512);
-      return h8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    if constexpr (!PAIR) {
-      // (each tile's fragments read one tile ahead of their MFMAs; the
-      // scheduling barriers keep them there)
-      h8_t vf[2][NDT];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vf[0][dt] = vfrag(0, dt);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g + 1 < 4) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vf[(g + 1) & 1][dt] = vfrag(g + 1, dt);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[g & 1][dt], pb[g >> 1][g & 1], o[dt], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag(g, dt), pb[g >> 1][g & 1], o[dt], 0, 0, 0);
-    }
-  };
+    const int dcol = dh * (D / 2);  // first output dim of this wave
+    const int G = a.group;
+    const int Hq = a.num_q_heads;
+    const int BQ = a.rows / G;                   // tokens per workgroup
+    const int L = a.seq_lens[b];
+    const int Qb = a.q_lens ? a.q_lens[b] : 1;
+    const int i0 = blk * BQ;
+    if (i0 >= Qb) return;  // the whole workgroup: no barrier is skipped by a part of it
+    const int pos0 = L - Qb;  // position of token 0
+    const int W = a.window;
+    auto lo_of = [&](int pos) { return W > 0 ? max(0, pos - W + 1) : 0; };
 
-  // One step's compute on LDS buffer buf. A step no row of the wave sees is
-  // skipped. (A half that no row sees still gets scores, from finite LDS
-  // data, when the other half is needed; they are masked to weight 0. The
-  // score registers live only inside the branch that uses them: a value
-  // merged from a path that skips them would be zero-filled every step.)
-  // PAIR: the score exchange, after the step buffers: wave w's 16 scores
-  // per lane in four 1 KB blocks (floats 4 c .. 4 c + 3 of lane l at
-  // 1024 c + 16 l, conflict-free). The two waves meet there without a
-  // workgroup barrier: each score's lowest mantissa bit carries the parity
-  // of the pair's count of computed steps (a change of at most 2^-23
-  // relative, and both waves use the same tagged values), so the reader
-  // waits until every word it reads carries this step's tag. The blocks
-  // start out tagged 1 (before the first barrier), the first step writes
-  // tag 0. A word is read after it is written (the reader polls) and
-  // written again only after the next barrier, which the reader reaches
-  // after reading it.
-  uint8_t* const xs = lds_raw + NBUF * BUF_BYTES;
-  int x_count = 0;  // steps this pair has computed
-  if constexpr (PAIR) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<u32x4*>(xs + wave * 4096 + 1024 * c + 16 * lane) = u32x4{1u, 1u, 1u, 1u};
-  }
-  static_assert(!PAIR || WAVES * 4096 == (int)prefill_xchg_bytes(D, WAVES), "exchange size");
-  // mid() runs once per step, after the scores (or at once on a skipped
-  // step): the V waves issue their loads there.
-  auto compute = [&](int step, int buf, auto&& mid) __attribute__((always_inline)) {
-    const uint8_t* kb = lds_raw + buf * BUF_BYTES;
-    const int key0 = step_tile(step) * kPageSize;
-    if constexpr (PAIR) {
-      // Both waves of a pair have the same rows, hence the same test.
-      if (!(active(key0) || active(key0 + 32))) {
-        mid();
+    // Key range of the workgroup, in tiles: [lo of its first token, its last
+    // token's position].
+    const int ilast = min(Qb, i0 + BQ) - 1;
+    const int khi = pos0 + ilast;
+    const int klo = lo_of(pos0 + i0);
+    const int t_lo = klo / kPageSize;
+    const int n_tiles = khi >= 0 ? khi / kPageSize - t_lo + 1 : 0;
+    const int n_steps = (n_tiles + KT - 1) / KT;
+
+    // Wave-uniform summaries of this wave's rows 32 rg .. + 31 for the skip /
+    // unmasked tests: their tokens run from i_a to i_b (rows past the
+    // workgroup's, tokens past the sequence's and negative positions left
+    // out), and the bounds of a token's keys grow with its position.
+    int lo_min = 0x7fffffff, lo_max = 0, hi_min = 0x7fffffff, hi_max = -1;
+    {
+      const int r_b = min(32 * rg + 31, a.rows - 1);
+      const int i_a = max(i0 + (32 * rg) / G, -pos0);
+      const int i_b = min(i0 + r_b / G, Qb - 1);
+      if (32 * rg <= r_b && i_a <= i_b) {
+        hi_min = pos0 + i_a;
+        hi_max = pos0 + i_b;
+        lo_min = lo_of(hi_min);
+        lo_max = lo_of(hi_max);
+      }
+    }
+
+    // Cache addressing (as in the decode kernel): tile u of sequence b starts
+    // at bt[u >> tile_shift] * page_bytes + (u & mask) * 16 * key_stride; slot
+    // j of head g at j * key_stride + g * head_stride inside it.
+    typedef const __attribute__((address_space(4))) int32_t* bt_ptr_t;
+    const bt_ptr_t bt = (bt_ptr_t)(a.block_table + (size_t)b * a.max_pages);
+    const int tshift = a.tile_shift;
+    const int tmask = (1 << tshift) - 1;
+    const uint32_t key_stride = a.key_stride;
+    const uint32_t head_off = (uint32_t)g * a.head_stride;
+    auto tile_base = [&](int u) -> size_t {
+      return (size_t)bt[u >> tshift] * a.page_bytes + (size_t)((u & tmask) * kPageSize) * key_stride;
+    };
+
+    // First tile of step `step` (past the last step: tiles past the range,
+    // which tile_at clamps).
+    auto step_tile = [&](int step) __attribute__((always_inline)) { return t_lo + step * KT; };
+    // Tile tt of step `step`; tiles past the workgroup's range are read from
+    // its last tile (in bounds; all their keys are masked).
+    const int last_tile = t_lo + n_tiles - 1;
+    auto tile_at = [&](int step, int tt) __attribute__((always_inline)) {
+      return tile_base(min(step_tile(step) + tt, last_tile));
+    };
+    const uint32_t lds_u32 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds_raw;
+    // One direct 16-byte load per lane into LDS at byte dst + 16 lane (dst
+    // wave-uniform, in M0; one wait state after M0 is written). Written as asm
+    // so that the compiler's wait insertion does not track an LDS write in
+    // flight: it would make LDS reads wait for every outstanding load,
+    // including those of the steps ahead. The waits this pipeline needs are
+    // explicit (wait_vm before each barrier).
+    auto lds_load16 = [](const uint8_t* src, uint32_t dst) __attribute__((always_inline)) {
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(dst))
+                   : "memory");
+    };
+
+    // fp16 caches, direct loads: waves [0, WAVES / 2) load K, the others V, in
+    // whole 1 KB blocks, PERK per K wave and PERV per V wave and step; a K
+    // wave's blocks lie in one half, a V wave's cover whole tiles. Each lane's
+    // byte offset within a tile is fixed: K, key lane % 16 of the lane's tile
+    // (lane / 16 % 2 of the half) at dims 8 (lane / 32) ..; V, the key row of
+    // slot `lane` at dims 8 (lane % 4) ...
+    constexpr int PERK = 2 * NK / (WAVES / 2);
+    constexpr int PERV = KT * NDV / (WAVES / 2);
+    static_assert(NK % PERK == 0 && PERV % NDV == 0, "a wave's blocks: one half, or whole tiles");
+    const bool kwave = wave < WAVES / 2;
+    const int wk = kwave ? wave : wave - WAVES / 2;
+    const int vrow = 8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 2) & 3);
+    const uint32_t lane_off = kwave ? (uint32_t)(lane & 15) * key_stride + head_off + 16u * (lane >> 5)
+                                    : (uint32_t)vrow * key_stride + head_off + 16u * (lane & 3);
+    // The tiles a wave loads each step: a K wave tiles ta and ta + 1 (its
+    // half), a V wave tiles ta .. ta + PERV / NDV - 1 (at most two). Inside the
+    // step loop their bases come from the block table before the barrier of
+    // the step before, so the scalar loads' latency hides under the barrier.
+    const int ta = kwave ? 2 * ((wk * PERK) / NK) : (wk * PERV) / NDV;
+    static_assert(PERV / NDV <= 2, "a V wave loads at most two tiles a step");
+    auto dma_bases = [&](size_t b0, size_t b1, int buf) __attribute__((always_inline)) {
+      const uint32_t dst0 = lds_u32 + (uint32_t)(buf * BUF_BYTES);
+      if (kwave) {
+        const int t0 = (wk * PERK) % NK;
+        const uint8_t* src = a.k + ((lane & 16) ? b1 : b0) + lane_off + 32 * t0;
+        const uint32_t dst = dst0 + (uint32_t)((ta / 2) * KH_BYTES + t0 * 1024);
+  #pragma unroll
+        for (int i = 0; i < PERK; ++i) lds_load16(src + 32 * i, dst + 1024u * i);
       } else {
-        const uint32_t tag = (uint32_t)(x_count & 1);
-        ++x_count;
-        f16v_t mine;
-        scores1(kb + dh * KH_BYTES, mine);
-        // (through a scalar: __builtin_bit_cast of a vector element lvalue
-        // reads element 0)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float x = mine[v];
-          mine[v] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~1u) | tag);
+  #pragma unroll
+        for (int q = 0; q < PERV / NDV; ++q) {
+          const uint8_t* src = a.v + (q == 0 ? b0 : b1) + lane_off;
+          const uint32_t dst = dst0 + (uint32_t)(2 * KH_BYTES + (ta + q) * VT_BYTES);
+  #pragma unroll
+          for (int dg = 0; dg < NDV; ++dg) lds_load16(src + 64 * dg, dst + 1024u * dg);
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<f32x4_t*>(xs + wave * 4096 + 1024 * c + 16 * lane) =
-              f32x4_t{mine[4 * c], mine[4 * c + 1], mine[4 * c + 2], mine[4 * c + 3]};
-        asm volatile("" ::: "memory");  // the writes stay ahead of the polls
-        mid();
-        // The partner's scores: poll until all of them carry the tag. (A
-        // bound on the polls keeps every wave finite whatever happens; the
-        // partner writes within the same step, so it is never reached.)
-        typedef const volatile __attribute__((address_space(3))) u32x4 lds_vu4_t;
-        lds_vu4_t* src = (lds_vu4_t*)(__attribute__((address_space(3))) uint8_t*)(xs + (wave ^ 1) * 4096 + 16 * lane);
-        u32x4 w[4];
-        uint32_t stale = ~0u;  // no poll yet; left nonzero if the bound ends the polls
-        for (int polls = 0; polls < (1 << 20) && stale != 0u; ++polls) {
-          uint32_t bad = 0u;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            w[c] = src[64 * c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bad |= (w[c][e] & 1u) ^ tag;
+      }
+    };
+    auto dma_step = [&](int step, int buf) __attribute__((always_inline)) {
+      dma_bases(tile_at(step, ta), tile_at(step, ta + 1), buf);
+    };
+    // After a V wave's loads of a step have landed: V slots of keys at or past
+    // the sequence's end hold whatever the page has there (a weight 0 times a
+    // NaN would spoil P.V), so they become zeros. (For a tile read in place of
+    // one past the range, keys counted at the tile's own place are past every
+    // slot it copies that lies past the end.) K there only meets masked scores.
+    auto dma_zero_tail = [&](int step, int buf) __attribute__((always_inline)) {
+      const int key_base = step_tile(step) * kPageSize;
+      if (kwave || key_base + KT * kPageSize <= L) return;
+      uint8_t* const dst0 = lds_raw + buf * BUF_BYTES + 2 * KH_BYTES;
+  #pragma unroll
+      for (int q = 0; q < PERV / NDV; ++q) {
+        const int tt = (wk * PERV) / NDV + q;
+        if (key_base + tt * kPageSize + vrow >= L) {
+  #pragma unroll
+          for (int dg = 0; dg < NDV; ++dg)
+            *reinterpret_cast<u32x4*>(dst0 + tt * VT_BYTES + dg * 1024 + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    // s_waitcnt with vmcnt(VM) and lgkmcnt(0) (expcnt untouched).
+    // The empty asm after it keeps the compiler from moving LDS accesses (the
+    // zeroing of a step's tail, say) above the wait for the direct loads they
+    // depend on; the loads' asm carries a memory clobber for the same reason.
+    auto wait_vm = [](auto vm_c) __attribute__((always_inline)) {
+      constexpr int VM = decltype(vm_c)::value;
+      __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+      asm volatile("" ::: "memory");
+    };
+    // Workgroup barrier without a memory fence (the waits before it are
+    // explicit); the empty asm statements keep the compiler from moving memory
+    // accesses across it.
+    auto barrier = []() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    // 1-byte codes, register staging: chunk c = tid + NTHREADS l of a step is
+    // K or V (kv), key row r64 of the step's 64, dims 16 j .. + 15; its 16
+    // codes become two fp16 slots (K: k-step j of the row's half, slot
+    // r64 % 32 and that + 32; V: block j / 2 of the row's tile, slots s and
+    // s + 1). All of that is fixed per thread; each step only moves the
+    // (scalar) tile bases.
+    uint32_t src_off[LOADS];
+    uint32_t lds_off[LOADS], lds_off2[LOADS];
+    int row_of[LOADS], tt_of[LOADS];
+    bool is_v[LOADS];
+    if constexpr (!DMA) {
+  #pragma unroll
+      for (int l = 0; l < LOADS; ++l) {
+        const int c = tid + NTHREADS * l;
+        const int kv = c / (CHUNKS / 2);
+        const int rem = c - kv * (CHUNKS / 2);
+        const int r64 = rem / (D / 16), j = rem % (D / 16);
+        tt_of[l] = r64 >> 4;
+        row_of[l] = r64 & 15;
+        is_v[l] = kv != 0;
+        src_off[l] = (uint32_t)row_of[l] * key_stride + head_off + 16u * j;
+        if (!kv) {
+          lds_off[l] = (uint32_t)((r64 >> 5) * KH_BYTES + j * 1024 + 16 * (r64 & 31));
+          lds_off2[l] = lds_off[l] + 512;
+        } else {
+          const int r = r64 & 15;
+          const int slot = 32 * (r >> 3) + 16 * ((r >> 2) & 1) + 4 * (r & 3) + 2 * (j & 1);
+          lds_off[l] = (uint32_t)(2 * KH_BYTES + tt_of[l] * VT_BYTES + (j >> 1) * 1024 + 16 * slot);
+          lds_off2[l] = lds_off[l] + 16;
+        }
+      }
+    }
+    uint32_t stage_regs[NREG][LOADS][4];
+    auto stage_load = [&](int step, auto set_c) __attribute__((always_inline)) {
+      auto& stage = stage_regs[decltype(set_c)::value];
+      size_t base[KT];
+  #pragma unroll
+      for (int tt = 0; tt < KT; ++tt) base[tt] = tile_at(step, tt);
+  #pragma unroll
+      for (int l = 0; l < LOADS; ++l) {
+        const uint8_t* src = (is_v[l] ? a.v : a.k) + base[tt_of[l]] + src_off[l];
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) stage[l][e] = x[e];
+      }
+    };
+    auto stage_store = [&](int step, int buf, auto set_c) __attribute__((always_inline)) {
+      auto& stage = stage_regs[decltype(set_c)::value];
+      const int t0 = step_tile(step);
+      const int j0 = t0 * kPageSize;
+      uint8_t* const dst0 = lds_raw + buf * BUF_BYTES;
+      // Slots past the sequence (arbitrary contents), and tiles past this
+      // workgroup's range, become zeros. Only a step that reaches past either
+      // needs the per-slot test (wave-uniform).
+      auto put = [&](auto checked) __attribute__((always_inline)) {
+  #pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+          bool live = true;
+          if constexpr (decltype(checked)::value) {
+            const int u = t0 + tt_of[l];
+            live = u < t_lo + n_tiles && j0 + tt_of[l] * kPageSize + row_of[l] < L;
           }
-          stale = __builtin_amdgcn_ballot_w64(bad != 0u) != 0 ? 1u : 0u;
-          if (stale != 0u) __builtin_amdgcn_s_sleep(1);
-        }
-        // (should the bound ever end the polls, the scores become NaN, so the
-        // rows' output shows it instead of silently using old scores)
-        f16v_t other;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
+          h2_t hv[8];
+          to_pairs<KV>(stage[l], hv);
+          u32x4 w0, w1;
+  #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t x = stale != 0u ? 0x7fc00000u : w[c][e];
-            other[4 * c + e] = __builtin_bit_cast(float, x);
+            w0[e] = live ? __builtin_bit_cast(uint32_t, hv[e]) : 0u;
+            w1[e] = live ? __builtin_bit_cast(uint32_t, hv[4 + e]) : 0u;
           }
-        f16v_t st[2];
-        st[0] = dh ? other : mine;
-        st[1] = dh ? mine : other;
-        softmax_pv(st, kb + 2 * KH_BYTES, key0);
+          *reinterpret_cast<u32x4*>(dst0 + lds_off[l]) = w0;
+          *reinterpret_cast<u32x4*>(dst0 + lds_off2[l]) = w1;
+        }
+      };
+      if (t0 - t_lo + KT <= n_tiles && j0 + KT * kPageSize <= L)
+        put(BoolC<false>{});
+      else
+        put(BoolC<true>{});
+    };
+
+    // The tile bases of the first steps (their scalar loads, with no branch
+    // between them, are in flight together with the offset's loads below; an
+    // index clamped to 0 is in bounds when there are no steps).
+    size_t tb[NBUF - 1][2];
+    if constexpr (DMA) {
+  #pragma unroll
+      for (int j = 0; j < NBUF - 1; ++j) {
+        tb[j][0] = tile_base(max(min(step_tile(j) + ta, last_tile), 0));
+        tb[j][1] = tile_base(max(min(step_tile(j) + ta + 1, last_tile), 0));
       }
-    } else if (active(key0) || active(key0 + 32)) {
-      f16v_t st[2];
-      scores2(kb, kb + KH_BYTES, st[0], st[1]);
-      mid();
-      softmax_pv(st, kb + 2 * KH_BYTES, key0);
+    }
+    // First token of sequence b in q and out (read before any cache load
+    // goes out, so that the wait for it waits for nothing else).
+    int off = b;
+    if (a.q_lens) {
+      int sum = 0;
+      for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
+      off = wave_sum_i(sum);
+    }
+
+    // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
+    // with h = l / 32; B: column l % 32, same k; C: column l % 32, rows
+    // 8 j + 4 h + i in element 4 j + i). So lane l works on query row rr = l % 32
+    // of this wave's 32 rows; lanes l and l + 32 share the row.
+    const int rr = lane & 31;
+    const int hh = lane >> 5;
+    const int myr = 32 * rg + rr;  // the workgroup row of this lane
+    const int my_i = i0 + myr / G;
+    const bool my_row = myr < a.rows && my_i < Qb;
+    const int my_pos = pos0 + my_i;
+    const int my_lo = (my_row && my_pos >= 0) ? lo_of(my_pos) : 0;
+    const int my_hi = (my_row && my_pos >= 0) ? my_pos : -1;
+
+    // Q^T as the B operand: lane l holds row rr, dims 16 t + 8 hh .. + 7 of
+    // k-step t. A negative scale flips q's sign.
+    typedef const __attribute__((address_space(4))) float* scale_ptr_t;
+    float qk = a.qk_mult * (a.k_scale ? ((scale_ptr_t)a.k_scale)[g] : 1.0f);
+    const uint32_t qflip = qk < 0.0f ? 0x80008000u : 0u;
+    // Scores of keys a row does not see are set to -inf before the softmax;
+    // with a zero scale -inf * 0 would be NaN, so a zero multiplier becomes
+    // the smallest normal float: every product with a finite score is then
+    // too small to change exp2 in fp32, and the weights stay exactly 1.
+    qk = fabsf(qk) > 0.0f ? fabsf(qk) : __FLT_MIN__;
+    constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
+    // The Q loads go out before the first steps' cache loads, and Q is first
+    // read after the wait for those: the two latencies overlap, and the cache
+    // loads stay the youngest, as the explicit waits below count on. (A lane
+    // without a row reads its token clamped into the sequence, in bounds, and
+    // keeps zeros.)
+    u32x4 qx[NK];
+    {
+      const uint8_t* qrow =
+          a.q + ((size_t)(off + min(my_i, Qb - 1)) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
+  #pragma unroll
+      for (int t = 0; t < NK; ++t) qx[t] = *reinterpret_cast<const u32x4*>(qrow + 32 * t + 16 * hh);
+    }
+    if constexpr (DMA) {
+  #pragma unroll
+      for (int j = 0; j < NBUF - 1; ++j)
+        if (j < n_steps) dma_bases(tb[j][0], tb[j][1], j);
     } else {
-      mid();
+      if (n_steps > 0) stage_load(0, IntC<0>{});
+    }
+    h8_t qb[NK];
+    auto q_ready = [&]() __attribute__((always_inline)) {
+      const uint32_t keep = my_row ? 0xFFFFFFFFu : 0u;
+  #pragma unroll
+      for (int t = 0; t < NK; ++t) {
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) qx[t][e] = (qx[t][e] & keep) ^ qflip;
+        qb[t] = __builtin_bit_cast(h8_t, qx[t]);
+      }
+    };
+
+    constexpr float kNoMax = -1e30f;
+    constexpr float kLazy = 8.0f;
+    float m = kNoMax, mx = kNoMax, lsum = 0.0f;
+    f16v_t o[NDT];
+  #pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f16v_t{};
+
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+    auto tr_read = [&](const uint8_t* src) __attribute__((always_inline)) {
+      return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_t*)(__attribute__((address_space(3))) uint8_t*)src));
+    };
+    const int q16 = lane >> 4, i16 = lane & 15;  // 16-lane group and lane in it
+    // The transposing V reads: lane l takes 4 dims (8 bytes) of key row
+    // 4 hh + i16 / 4 (+ 8 for the upper 8 keys of a k-step) at dims
+    // 16 (q16 % 2) + 4 (i16 % 4) of a 32-dim group: slot
+    // 16 hh + 4 (i16 / 4) + 2 (q16 % 2) + (i16 % 4) / 2 of the group's block,
+    // second 8 bytes when i16 is odd.
+    const uint32_t v_lane = 16u * (16 * hh + 4 * (i16 >> 2) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
+                            8u * (i16 & 1);
+
+    // Whether this wave has work on the 32 keys from key0 (wave-uniform).
+    auto active = [&](int key0) { return hi_max >= 0 && key0 <= hi_max && key0 + 31 >= lo_min; };
+    // S^T[key][row] of 32 keys: lane l gets row rr, keys 8 j + 4 hh + i in
+    // st[4 j + i]. The two halves' chains of dependent MFMAs are interleaved
+    // (scores2), with each k-step's K fragments read one step ahead. (At D=256,
+    // one wave per SIMD, this order measured 0.8% faster than computing each
+    // half's scores just before its softmax; its extra registers go to AGPRs.)
+    auto frag = [&](const uint8_t* kh, int t) __attribute__((always_inline)) {
+      return *reinterpret_cast<const h8_t*>(kh + 1024 * t + 16 * lane);
+    };
+    auto scores2 = [&](const uint8_t* kb0, const uint8_t* kb1, f16v_t& s0, f16v_t& s1) __attribute__((always_inline)) {
+      h8_t k0 = frag(kb0, 0), k1 = frag(kb1, 0);
+      s0 = f16v_t{};
+      s1 = f16v_t{};
+  #pragma unroll
+      for (int t = 0; t < NK; ++t) {
+        h8_t n0 = k0, n1 = k1;
+        if (t + 1 < NK) {
+          n0 = frag(kb0, t + 1);
+          n1 = frag(kb1, t + 1);
+        }
+        // (the next k-step's reads stay ahead of this one's MFMAs)
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qb[t], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qb[t], s1, 0, 0, 0);
+        k0 = n0;
+        k1 = n1;
+      }
+    };
+    // Scores of one 32-key half (PAIR): one chain of MFMAs, K read a k-step
+    // ahead (the partner wave on the SIMD fills the matrix unit between them).
+    auto scores1 = [&](const uint8_t* kh, f16v_t& s) __attribute__((always_inline)) {
+      h8_t k = frag(kh, 0);
+      s = f16v_t{};
+  #pragma unroll
+      for (int t = 0; t < NK; ++t) {
+        h8_t n = k;
+        if (t + 1 < NK) n = frag(kh, t + 1);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qb[t], s, 0, 0, 0);
+        k = n;
+      }
+    };
+    // Softmax and P.V of the 64 keys from key0 whose scores are st[0] (keys
+    // key0 ..) and st[1] (key0 + 32 ..). Where some row of the wave sees only
+    // part of the keys (a uniform test), the scores of keys a row does not see
+    // become -inf first: they leave the maximum alone and get weight
+    // exp2(-inf) = 0. Every other step runs no per-key test. One maximum and
+    // one rescale test cover both halves, so the weights and P.V of both run in
+    // one block (the exponentials of one half can issue under the other's
+    // matrix instructions).
+    auto softmax_pv = [&](f16v_t (&st)[2], const uint8_t* vb, int key0) __attribute__((always_inline)) {
+      if (!(key0 >= lo_max && key0 + 63 <= hi_min)) {
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // lane's key of slot v: key0 + 32 h + 8 (v / 4) + 4 hh + v % 4
+          const int d_lo = my_lo - key0 - 32 * h - 4 * hh, d_hi = my_hi - key0 - 32 * h - 4 * hh;
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int c = 8 * (v >> 2) + (v & 3);
+            st[h][v] = (c >= d_lo && c <= d_hi) ? st[h][v] : -INFINITY;
+          }
+        }
+      }
+      float mt;
+      {
+        float a[8];
+  #pragma unroll
+        for (int h = 0; h < 2; ++h)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+            a[4 * h + q] = fmaxf(fmaxf(st[h][4 * q], st[h][4 * q + 1]),
+                                 fmaxf(st[h][4 * q + 2], st[h][4 * q + 3]));
+        mt = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+                   fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+      }
+      {  // the other half of the row's keys sits in lane l ^ 32
+        auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mt),
+                                                   __builtin_bit_cast(int, mt), false, false);
+        mt = fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+      }
+      mt = mt == -INFINITY ? kNoMax : qk * mt;
+      mx = fmaxf(mx, mt);
+      if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mx);
+        lsum *= alpha;
+  #pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        m = mx;
+      }
+      // O^T[dim][row] += V^T . P^T over four 16-key k-steps. k-step 2 h + ks
+      // takes the lane's keys of half h, j = 2 ks, 2 ks + 1 (slots 8 hh + e:
+      // key 32 h + 16 ks + 4 hh + e, then 32 h + 16 ks + 8 + 4 hh + e); V^T's A
+      // operand uses the same key order: two transposing reads of 4
+      // consecutive key rows at this lane's dim. The denominator adds the same
+      // fp16 weights that P.V multiplies V by (v_dot2 with ones: each fp16
+      // value enters the fp32 sum exactly).
+      const h2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      h8_t pb[2][2];
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb[h][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[h][8 * ks + e], qk, -m));
+            pb[h][ks][4 + e] =
+                (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[h][8 * ks + 4 + e], qk, -m));
+          }
+  #pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            lsum = __builtin_amdgcn_fdot2(h2_t{pb[h][ks][e], pb[h][ks][e + 1]}, one2, lsum, false);
+        }
+      }
+      // V^T fragment of tile g = 2 h + ks, dims dcol + 32 dt
+      auto vfrag = [&](int g, int dt) __attribute__((always_inline)) {
+        const uint8_t* vt = vb + g * VT_BYTES + (dcol / 32) * 1024 + v_lane + 1024 * dt;
+        const h4_t lo = tr_read(vt);
+        const h4_t hi = tr_read(vt + 512);
+        return h8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      if constexpr (!PAIR) {
+        // (each tile's fragments read one tile ahead of their MFMAs; the
+        // scheduling barriers keep them there)
+        h8_t vf[2][NDT];
+  #pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vf[0][dt] = vfrag(0, dt);
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (g + 1 < 4) {
+  #pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) vf[(g + 1) & 1][dt] = vfrag(g + 1, dt);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[g & 1][dt], pb[g >> 1][g & 1], o[dt], 0, 0, 0);
+        }
+      } else {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g)
+  #pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag(g, dt), pb[g >> 1][g & 1], o[dt], 0, 0, 0);
+      }
+    };
+
+    // One step's compute on LDS buffer buf. A step no row of the wave sees is
+    // skipped. (A half that no row sees still gets scores, from finite LDS
+    // data, when the other half is needed; they are masked to weight 0. The
+    // score registers live only inside the branch that uses them: a value
+    // merged from a path that skips them would be zero-filled every step.)
+    // PAIR: the score exchange, after the step buffers: wave w's 16 scores
+    // per lane in four 1 KB blocks (floats 4 c .. 4 c + 3 of lane l at
+    // 1024 c + 16 l, conflict-free). The two waves meet there without a
+    // workgroup barrier: each score's lowest mantissa bit carries the parity
+    // of the pair's count of computed steps (a change of at most 2^-23
+    // relative, and both waves use the same tagged values), so the reader
+    // waits until every word it reads carries this step's tag. The blocks
+    // start out tagged 1 (before the first barrier), the first step writes
+    // tag 0. A word is read after it is written (the reader polls) and
+    // written again only after the next barrier, which the reader reaches
+    // after reading it.
+    uint8_t* const xs = lds_raw + NBUF * BUF_BYTES;
+    int x_count = 0;  // steps this pair has computed
+    if constexpr (PAIR) {
+  #pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(xs + wave * 4096 + 1024 * c + 16 * lane) = u32x4{1u, 1u, 1u, 1u};
+    }
+    static_assert(!PAIR || WAVES * 4096 == (int)prefill_xchg_bytes(D, WAVES), "exchange size");
+    // mid() runs once per step, after the scores (or at once on a skipped
+    // step): the V waves issue their loads there.
+    auto compute = [&](int step, int buf, auto&& mid) __attribute__((always_inline)) {
+      const uint8_t* kb = lds_raw + buf * BUF_BYTES;
+      const int key0 = step_tile(step) * kPageSize;
+      if constexpr (PAIR) {
+        // Both waves of a pair have the same rows, hence the same test.
+        if (!(active(key0) || active(key0 + 32))) {
+          mid();
+        } else {
+          const uint32_t tag = (uint32_t)(x_count & 1);
+          ++x_count;
+          f16v_t mine;
+          scores1(kb + dh * KH_BYTES, mine);
+          // (through a scalar: __builtin_bit_cast of a vector element lvalue
+          // reads element 0)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float x = mine[v];
+            mine[v] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & ~1u) | tag);
+          }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<f32x4_t*>(xs + wave * 4096 + 1024 * c + 16 * lane) =
+                f32x4_t{mine[4 * c], mine[4 * c + 1], mine[4 * c + 2], mine[4 * c + 3]};
+          asm volatile("" ::: "memory");  // the writes stay ahead of the polls
+          mid();
+          // The partner's scores: poll until all of them carry the tag. (A
+          // bound on the polls keeps every wave finite whatever happens; the
+          // partner writes within the same step, so it is never reached.)
+          typedef const volatile __attribute__((address_space(3))) u32x4 lds_vu4_t;
+          lds_vu4_t* src = (lds_vu4_t*)(__attribute__((address_space(3))) uint8_t*)(xs + (wave ^ 1) * 4096 + 16 * lane);
+          u32x4 w[4];
+          uint32_t stale = ~0u;  // no poll yet; left nonzero if the bound ends the polls
+          for (int polls = 0; polls < (1 << 20) && stale != 0u; ++polls) {
+            uint32_t bad = 0u;
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              w[c] = src[64 * c];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) bad |= (w[c][e] & 1u) ^ tag;
+            }
+            stale = __builtin_amdgcn_ballot_w64(bad != 0u) != 0 ? 1u : 0u;
+            if (stale != 0u) __builtin_amdgcn_s_sleep(1);
+          }
+          // (should the bound ever end the polls, the scores become NaN, so the
+          // rows' output shows it instead of silently using old scores)
+          f16v_t other;
+  #pragma unroll
+          for (int c = 0; c < 4; ++c)
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t x = stale != 0u ? 0x7fc00000u : w[c][e];
+              other[4 * c + e] = __builtin_bit_cast(float, x);
+            }
+          f16v_t st[2];
+          st[0] = dh ? other : mine;
+          st[1] = dh ? mine : other;
+          softmax_pv(st, kb + 2 * KH_BYTES, key0);
+        }
+      } else if (active(key0) || active(key0 + 32)) {
+        f16v_t st[2];
+        scores2(kb, kb + KH_BYTES, st[0], st[1]);
+        mid();
+        softmax_pv(st, kb + 2 * KH_BYTES, key0);
+      } else {
+        mid();
+      }
+    };
+
+    if constexpr (DMA) {
+      // Step s computes on buffer s % NBUF; its start issues the loads of step
+      // s + NBUF - 1 (that buffer was last read in step s - 1, which every
+      // wave has left at the barrier); its end waits for this wave's loads of
+      // step s + 1 (the loads of step s + 2 may stay in flight), zeroes
+      // that step's tail, and meets the other waves at the barrier.
+      static_assert(NBUF >= 2 && NBUF <= 4, "two to four step buffers");
+      // Wait for this wave's loads of step `need`, with the loads of the steps
+      // after it that were issued (up to `issued_to`, at most two) in flight.
+      auto wait_step = [&](int need, int issued_to) __attribute__((always_inline)) {
+        const int after = min(issued_to, n_steps - 1) - need;
+        if (after >= 2) {
+          if (kwave)
+            wait_vm(IntC<2 * PERK>{});
+          else
+            wait_vm(IntC<2 * PERV>{});
+        } else if (after == 1) {
+          if (kwave)
+            wait_vm(IntC<PERK>{});
+          else
+            wait_vm(IntC<PERV>{});
+        } else {
+          wait_vm(IntC<0>{});
+        }
+      };
+      if (n_steps > 0) {
+        // (steps 0 .. NBUF - 2 were issued above; Q loads may follow them)
+        wait_step(0, NBUF - 2);
+        dma_zero_tail(0, 0);
+        wait_vm(IntC<63>{});
+        barrier();
+        q_ready();
+        int buf = 0;
+        size_t nb0 = tile_at(NBUF - 1, ta), nb1 = tile_at(NBUF - 1, ta + 1);
+        for (int step = 0; step < n_steps; ++step) {
+          const int nb = buf + 1 == NBUF ? 0 : buf + 1;  // buffer of step + 1
+          const int lb = buf == 0 ? NBUF - 1 : buf - 1;  // of step + NBUF - 1
+          // (At D=256 the V waves issue their loads after the scores: a
+          // step's 64 KB of loads from all waves at once back up the memory
+          // pipeline and stall the waves that issue last, and V of a step is
+          // read last. Measured 2% faster there, 3-5% slower at D=128.)
+          const bool issue = step + NBUF - 1 < n_steps;
+          constexpr bool LATE_V = PAIR;
+          if ((kwave || !LATE_V) && issue) dma_bases(nb0, nb1, lb);
+          compute(step, buf, [&]() __attribute__((always_inline)) {
+            if (LATE_V && !kwave && issue) dma_bases(nb0, nb1, lb);
+          });
+          if (step + 1 < n_steps) {
+            wait_step(step + 1, step + NBUF - 1);
+            dma_zero_tail(step + 1, nb);
+            wait_vm(IntC<63>{});
+            // (tile_at clamps, so a step past the last reads a valid entry)
+            nb0 = tile_at(step + NBUF, ta);
+            nb1 = tile_at(step + NBUF, ta + 1);
+            barrier();
+          }
+          buf = nb;
+        }
+      }
+    } else if (n_steps > 0) {
+      stage_store(0, 0, IntC<0>{});
+      if (n_steps > 1) stage_load(1, IntC<0>{});
+      if constexpr (NREG >= 2) {
+        if (n_steps > 2) stage_load(2, IntC<1>{});
+      }
+      __syncthreads();
+      q_ready();
+      // Step `step` reads LDS buffer step & 1; register set SET holds step + 1.
+      auto step_body = [&](int step, auto set_c) __attribute__((always_inline)) {
+        const int buf = step & 1;
+        compute(step, buf, []() {});
+        if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1, set_c);
+        if (step + 1 + NREG < n_steps) stage_load(step + 1 + NREG, set_c);
+        __syncthreads();
+      };
+      for (int step = 0; step < n_steps; step += NREG) {
+        step_body(step, IntC<0>{});
+        if constexpr (NREG >= 2) {
+          if (step + 1 < n_steps) step_body(step + 1, IntC<1>{});
+        }
+      }
+    }
+
+    // Bring o, l to the row maximum, add the two lane halves' l, and write
+    // fp16 out (a row that sees no key is 0), one division per row: o times
+    // alpha * v_scale / l. Lane l holds dims 32 dt + 8 j + 4 hh .. + 3 of row
+    // rr; the rows go through a wave-private LDS tile (row stride DW + 8
+    // halves, 16-byte aligned) so that the global stores are whole rows, 16
+    // lanes x 16 bytes each, instead of 8-byte pieces of 32 rows.
+    const float alpha = __builtin_amdgcn_exp2f(m - mx);
+    lsum *= alpha;
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, lsum),
+                                                 __builtin_bit_cast(int, lsum), false, false);
+      lsum = __builtin_bit_cast(float, (int)sw[0]) + __builtin_bit_cast(float, (int)sw[1]);
+    }
+    const float vs = a.v_scale ? ((scale_ptr_t)a.v_scale)[g] : 1.0f;
+    const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
+    constexpr int DW = PAIR ? D / 2 : D;  // dims this wave writes
+    constexpr int RS = 2 * DW + 16;      // LDS bytes per row
+    static_assert(WAVES * 32 * RS <= (int)prefill_out_lds_bytes(D, WAVES), "out tile fits");
+    // Every wave has left the last step's LDS reads before any tile is written.
+    __syncthreads();
+    uint8_t* const tile = lds_raw + wave * 32 * RS;
+  #pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h4_t y;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[dt][4 * j + e] * f);
+        *reinterpret_cast<h4_t*>(tile + rr * RS + 2 * (32 * dt + 8 * j + 4 * hh)) = y;
+      }
+    }
+    constexpr int PPR = DW / 8;  // 16-byte pieces of a row
+  #pragma unroll
+    for (int it = 0; it < 32 * PPR / 64; ++it) {
+      const int idx = 64 * it + lane;
+      const int r = idx / PPR, pc = idx % PPR;
+      const int wr = 32 * rg + r;  // the workgroup row
+      const int i = i0 + wr / G;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + 16 * pc);
+      if (wr < a.rows && i < Qb) {
+        const size_t hrow = (size_t)(off + i) * Hq + g * G + (wr - (wr / G) * G);
+        *reinterpret_cast<u32x4*>(a.out + hrow * D + dcol + 8 * pc) = v;
+      }
     }
   };
-
-  if constexpr (DMA) {
-    // Step s computes on buffer s % NBUF; its start issues the loads of step
-    // s + NBUF - 1 (that buffer was last read in step s - 1, which every
-    // wave has left at the barrier); its end waits for this wave's loads of
-    // step s + 1 (the loads of step s + 2 may stay in flight), zeroes
-    // that step's tail, and meets the other waves at the barrier.
-    static_assert(NBUF >= 2 && NBUF <= 4, "two to four step buffers");
-    // Wait for this wave's loads of step `need`, with the loads of the steps
-    // after it that were issued (up to `issued_to`, at most two) in flight.
-    auto wait_step = [&](int need, int issued_to) __attribute__((always_inline)) {
-      const int after = min(issued_to, n_steps - 1) - need;
-      if (after >= 2) {
-        if (kwave)
-          wait_vm(IntC<2 * PERK>{});
-        else
-          wait_vm(IntC<2 * PERV>{});
-      } else if (after == 1) {
-        if (kwave)
-          wait_vm(IntC<PERK>{});
-        else
-          wait_vm(IntC<PERV>{});
-      } else {
-        wait_vm(IntC<0>{});
-      }
-    };
-    if (n_steps > 0) {
-      // (steps 0 .. NBUF - 2 were issued above; Q loads may follow them)
-      wait_step(0, NBUF - 2);
-      dma_zero_tail(0, 0);
-      wait_vm(IntC<63>{});
-      barrier();
-      q_ready();
-      int buf = 0;
-      size_t nb0 = tile_at(NBUF - 1, ta), nb1 = tile_at(NBUF - 1, ta + 1);
-      for (int step = 0; step < n_steps; ++step) {
-        const int nb = buf + 1 == NBUF ? 0 : buf + 1;  // buffer of step + 1
-        const int lb = buf == 0 ? NBUF - 1 : buf - 1;  // of step + NBUF - 1
-        // (At D=256 the V waves issue their loads after the scores: a
-        // step's 64 KB of loads from all waves at once back up the memory
-        // pipeline and stall the waves that issue last, and V of a step is
-        // read last. Measured 2% faster there, 3-5% slower at D=128.)
-        const bool issue = step + NBUF - 1 < n_steps;
-        constexpr bool LATE_V = PAIR;
-        if ((kwave || !LATE_V) && issue) dma_bases(nb0, nb1, lb);
-        compute(step, buf, [&]() __attribute__((always_inline)) {
-          if (LATE_V && !kwave && issue) dma_bases(nb0, nb1, lb);
-        });
-        if (step + 1 < n_steps) {
-          wait_step(step + 1, step + NBUF - 1);
-          dma_zero_tail(step + 1, nb);
-          wait_vm(IntC<63>{});
-          // (tile_at clamps, so a step past the last reads a valid entry)
-          nb0 = tile_at(step + NBUF, ta);
-          nb1 = tile_at(step + NBUF, ta + 1);
-          barrier();
-        }
-        buf = nb;
-      }
-    }
-  } else if (n_steps > 0) {
-    stage_store(0, 0, IntC<0>{});
-    if (n_steps > 1) stage_load(1, IntC<0>{});
-    if constexpr (NREG >= 2) {
-      if (n_steps > 2) stage_load(2, IntC<1>{});
-    }
-    __syncthreads();
-    q_ready();
-    // Step `step` reads LDS buffer step & 1; register set SET holds step + 1.
-    auto step_body = [&](int step, auto set_c) __attribute__((always_inline)) {
-      const int buf = step & 1;
-      compute(step, buf, []() {});
-      if (step + 1 < n_steps) stage_store(step + 1, buf ^ 1, set_c);
-      if (step + 1 + NREG < n_steps) stage_load(step + 1 + NREG, set_c);
+  auto slot_item = [](uint32_t v, uint32_t n) {
+    const uint32_t xcd = v & 7u, k = v >> 3;
+    return xcd * (n >> 3) + min(xcd, n & 7u) + k;
+  };
+  const uint32_t n_items = (uint32_t)a.prefill_items;
+  if constexpr (PERSIST) {
+    // Persistent workgroups (as many as fit on the device): round r gives
+    // them the slots r P .. r P + P - 1 (P = gridDim.x); on each XCD its
+    // j-th workgroup takes the XCD's j-th slot of the round in even rounds
+    // and the j-th from the end in odd ones. Items come longest first within
+    // a (sequence, KV head), so the workgroup with the longest items of one
+    // round gets the shortest of the next. No workgroup waits to be
+    // dispatched behind another's exit. (A grid that is not a multiple of
+    // 8 has one round: one item per workgroup.)
+    const uint32_t P = gridDim.x, per = P >> 3, x8 = blockIdx.x & 7u, j8 = blockIdx.x >> 3;
+    for (uint32_t r = 0;; ++r) {
+      const uint32_t v = (P & 7u) ? blockIdx.x + r * P : 8u * (r * per + ((r & 1u) ? per - 1u - j8 : j8)) + x8;
+      if (v >= n_items) break;
+      item(slot_item(v, n_items));
+      // (the next item's loads go to LDS that this one's output tile used)
       __syncthreads();
-    };
-    for (int step = 0; step < n_steps; step += NREG) {
-      step_body(step, IntC<0>{});
-      if constexpr (NREG >= 2) {
-        if (step + 1 < n_steps) step_body(step + 1, IntC<1>{});
-      }
     }
-  }
-
-  // Bring o, l to the row maximum, add the two lane halves' l, and write
-  // fp16 out (a row that sees no key is 0), one division per row: o times
-  // alpha * v_scale / l. Lane l holds dims 32 dt + 8 j + 4 hh .. + 3 of row
-  // rr; the rows go through a wave-private LDS tile (row stride DW + 8
-  // halves, 16-byte aligned) so that the global stores are whole rows, 16
-  // lanes x 16 bytes each, instead of 8-byte pieces of 32 rows.
-  const float alpha = __builtin_amdgcn_exp2f(m - mx);
-  lsum *= alpha;
-  {
-    auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, lsum),
-                                               __builtin_bit_cast(int, lsum), false, false);
-    lsum = __builtin_bit_cast(float, (int)sw[0]) + __builtin_bit_cast(float, (int)sw[1]);
-  }
-  const float vs = a.v_scale ? ((scale_ptr_t)a.v_scale)[g] : 1.0f;
-  const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
-  constexpr int DW = PAIR ? D / 2 : D;  // dims this wave writes
-  constexpr int RS = 2 * DW + 16;      // LDS bytes per row
-  static_assert(WAVES * 32 * RS <= (int)prefill_out_lds_bytes(D, WAVES), "out tile fits");
-  // Every wave has left the last step's LDS reads before any tile is written.
-  __syncthreads();
-  uint8_t* const tile = lds_raw + wave * 32 * RS;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h4_t y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[dt][4 * j + e] * f);
-      *reinterpret_cast<h4_t*>(tile + rr * RS + 2 * (32 * dt + 8 * j + 4 * hh)) = y;
-    }
-  }
-  constexpr int PPR = DW / 8;  // 16-byte pieces of a row
-#pragma unroll
-  for (int it = 0; it < 32 * PPR / 64; ++it) {
-    const int idx = 64 * it + lane;
-    const int r = idx / PPR, pc = idx % PPR;
-    const int wr = 32 * rg + r;  // the workgroup row
-    const int i = i0 + wr / G;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + 16 * pc);
-    if (wr < a.rows && i < Qb) {
-      const size_t hrow = (size_t)(off + i) * Hq + g * G + (wr - (wr / G) * G);
-      *reinterpret_cast<u32x4*>(a.out + hrow * D + dcol + 8 * pc) = v;
-    }
+  } else {
+    item(slot_item(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), n_items));
   }
 }
 
+// At D=128 a persistent grid: as many workgroups as fit on the device at
+// once (the occupancy the runtime reports for the kernel, block and LDS
+// size, times the CU count), at most one per item; at D=256 one workgroup
+// per item (grid = token blocks x KV heads x sequences).
 template <int KV>
-hipError_t launch_prefill_kv(int head_dim, int waves, dim3 grid, size_t lds, hipStream_t stream,
+hipError_t launch_prefill_kv(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                              const DecodeArgs& args) {
-#define PDA_PCASE(DD, WW)                                                                      \
-  if (head_dim == DD && waves == WW) {                                                         \
-    hipLaunchKernelGGL((pda_prefill_mfma_kernel<DD, KV, WW>), grid, dim3(64 * WW), lds, stream, \
-                       args);                                                                  \
-    return hipGetLastError();                                                                  \
+#define PDA_PCASE(DD, WW)                                                                            \
+  if (head_dim == DD && waves == WW) {                                                               \
+    auto* kern = pda_prefill_mfma_kernel<DD, KV, WW>;                                                \
+    dim3 grid = items;                                                                               \
+    if (DD == 128) {                                                                                 \
+      static int per_cu = 0; /* the same on every MI355X; a race writes the same value */          \
+      if (per_cu <= 0) {                                                                             \
+        int n = 0;                                                                                   \
+        const hipError_t oe = hipOccupancyMaxActiveBlocksPerMultiprocessor(                          \
+            &n, reinterpret_cast<const void*>(kern), 64 * WW, lds);                                  \
+        if (oe != hipSuccess) return oe;                                                             \
+        per_cu = n > 0 ? n : 1;                                                                      \
+      }                                                                                              \
+      const int64_t n_items = (int64_t)items.x * items.y * items.z;                                  \
+      grid = dim3((unsigned)std::min<int64_t>(n_items, (int64_t)cus * per_cu));                      \
+    }                                                                                                \
+    if (grid.x * grid.y * grid.z == 0) return hipSuccess;                                            \
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WW), lds, stream, args);                                \
+    return hipGetLastError();                                                                        \
   }
   PDA_PCASE(128, 4)
   PDA_PCASE(128, 8)

@@ -301,3 +301,57 @@ def test_prefill_pair_handshake_never_takes_old_scores(pattern):
     assert all(a is None for a in pair_exchange_reads(active, lambda k, step: k & 1))
     wrong = pair_exchange_reads(active, lambda k, step: step & 1)
     assert all(a is None for a in wrong) == (pattern == "all")
+
+
+# ---- prefill at D=128: persistent workgroups' item order ----
+
+def persistent_slots(P, n):
+    """The slots workgroup b of a grid of P takes, round by round, as the
+    prefill kernel's item loop computes them (snake order within each XCD's
+    workgroups when P is a multiple of 8, else one slot per workgroup)."""
+    per = P >> 3
+    out = {}
+    for blk in range(P):
+        x8, j8 = blk & 7, blk >> 3
+        r, mine = 0, []
+        while True:
+            v = blk + r * P if (P & 7) else 8 * (r * per + ((per - 1 - j8) if (r & 1) else j8)) + x8
+            if v >= n:
+                break
+            mine.append(v)
+            r += 1
+        out[blk] = mine
+    return out
+
+
+def slot_item(v, n):
+    xcd, k = v & 7, v >> 3
+    return xcd * (n >> 3) + min(xcd, n & 7) + k
+
+
+@pytest.mark.parametrize("P,n", [(256, 1024), (256, 512), (256, 1568), (512, 1024), (256, 300),
+                                 (8, 8), (5, 5), (256, 256), (512, 513)])
+def test_prefill_persistent_slots_cover_every_item_once(P, n):
+    """Every item is taken exactly once; a multiple-of-8 grid keeps each
+    workgroup's slots on its own XCD (slot % 8 == workgroup % 8); and the
+    slot -> item map is a bijection on [0, n)."""
+    slots = persistent_slots(P, n)
+    taken = sorted(v for s in slots.values() for v in s)
+    assert taken == list(range(n))
+    if P % 8 == 0:
+        assert all(v % 8 == blk % 8 for blk, s in slots.items() for v in s)
+    assert sorted(slot_item(v, n) for v in range(n)) == list(range(n))
+
+
+def test_prefill_persistent_order_evens_out_causal_blocks():
+    """A fresh prefill's 32 token blocks per (sequence, KV head) come longest
+    first (block j of the reversed order has 32 - j steps); with 256
+    workgroups and 1024 items every workgroup gets the same number of steps
+    in the snake order, while plain round robin would give the first XCD
+    slots four of the longest."""
+    P, n = 256, 1024
+    steps = lambda lg: 32 - (lg % 32)  # items of one (sequence, KV head) are consecutive
+    snake = [sum(steps(slot_item(v, n)) for v in s) for s in persistent_slots(P, n).values()]
+    assert max(snake) == min(snake) == sum(steps(i) for i in range(n)) // P
+    plain = [sum(steps(slot_item(b + r * P, n)) for r in range(n // P)) for b in range(P)]
+    assert max(plain) > 1.5 * min(plain)
