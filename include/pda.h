@@ -41,6 +41,10 @@
  *    entries of the first ceil(seq_lens[b] / page_size) columns of row b are
  *    in [0, num_pages). Other table entries, and page slots past a
  *    sequence's length, are never read and may hold anything (NaN included).
+ *  - The environment variable PDA_PREFILL_CUS, read at each call, set to a
+ *    positive count below the device's CU count sizes the long-query
+ *    kernel's persistent grid for that many CUs instead (a small problem then
+ *    runs many work items per workgroup in turn); results do not depend on it.
  */
 #ifndef PDA_H_
 #define PDA_H_

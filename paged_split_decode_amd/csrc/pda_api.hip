@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -388,13 +389,27 @@ pda_status check_pointers(const void* q, const void* k, const void* v, const int
   return PDA_OK;
 }
 
+// CUs the persistent prefill grid is sized for: the device's, or fewer when
+// the environment variable PDA_PREFILL_CUS holds a smaller positive count (a
+// small problem then runs many items per workgroup in turn, as a large one
+// does on the whole device).
+int prefill_grid_cus() {
+  const int cus = device_cu_count();
+  const char* e = std::getenv("PDA_PREFILL_CUS");
+  if (cus > 0 && e != nullptr) {
+    const long n = std::strtol(e, nullptr, 10);
+    if (n > 0 && n < cus) return (int)n;
+  }
+  return cus;
+}
+
 pda_status launch_decode(const Plan& p, const pda_decode_dims* d, pda::DecodeArgs& args,
                          hipStream_t stream) {
   hipError_t e;
   if (p.prefill) {
     // (items: token blocks x KV heads x sequences; the launcher sizes the grid)
     const dim3 items(p.row_tiles, d->num_kv_heads, d->batch);
-    const int cus = device_cu_count();
+    const int cus = prefill_grid_cus();
     if (cus <= 0) return fail(PDA_ERR_DEVICE, "cannot read the device's CU count");
     const int waves = p.threads / 64;
     switch (kv_kind(d->kv_dtype)) {

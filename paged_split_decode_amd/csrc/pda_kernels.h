@@ -177,15 +177,16 @@ constexpr int prefill_buffers(int head_dim, int kv_kind, int waves) {
   return kv_kind == kKvF16 && head_dim == 128 && waves == 8 ? PDA_PREFILL_NBUF8 : 2;
 }
 // LDS the output tiles take after the loop: 32 rows per wave of the dims it
-// writes (half of D in the 8-wave D=256 pairs), each row 16 bytes longer.
+// writes (half of D in the 8-wave D=256 pairs), unpadded (the 16-byte pieces
+// of a row are stored in an order that depends on the row).
 constexpr size_t prefill_out_lds_bytes(int head_dim, int waves) {
-  return (size_t)waves * 32 * (2 * ((head_dim == 256 && waves == 8) ? head_dim / 2 : head_dim) + 16);
+  return (size_t)waves * 32 * 2 * ((head_dim == 256 && waves == 8) ? head_dim / 2 : head_dim);
 }
 // The score exchange of the D=256 pairs: 16 floats per lane and wave.
 constexpr size_t prefill_xchg_bytes(int head_dim, int waves) {
   return head_dim == 256 && waves == 8 ? (size_t)waves * 64 * 16 * 4 : 0;
 }
-inline size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
+constexpr size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
   const size_t steps = (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim) +
                        prefill_xchg_bytes(head_dim, waves);
   const size_t out = prefill_out_lds_bytes(head_dim, waves);

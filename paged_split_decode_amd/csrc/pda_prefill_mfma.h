@@ -777,9 +777,13 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     // Bring o, l to the row maximum, add the two lane halves' l, and write
     // fp16 out (a row that sees no key is 0), one division per row: o times
     // alpha * v_scale / l. Lane l holds dims 32 dt + 8 j + 4 hh .. + 3 of row
-    // rr; the rows go through a wave-private LDS tile (row stride DW + 8
-    // halves, 16-byte aligned) so that the global stores are whole rows, 16
-    // lanes x 16 bytes each, instead of 8-byte pieces of 32 rows.
+    // rr; the rows go through a wave-private LDS tile so that the global
+    // stores are whole rows, 16 lanes x 16 bytes each, instead of 8-byte
+    // pieces of 32 rows. In the tile (rows of 256 bytes, no padding), 16-byte
+    // piece c of row r sits at piece c ^ (r % 16) of the row, with its two
+    // 8-byte halves swapped in rows 16 .. 31: the 32 lanes of a write pass
+    // (32 rows, one half each) then fill all 64 banks once, and so do the 16
+    // lanes of a read pass (the 16 pieces of a row).
     const float alpha = __builtin_amdgcn_exp2f(m - mx);
     lsum *= alpha;
     {
@@ -790,8 +794,10 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     const float vs = a.v_scale ? ((scale_ptr_t)a.v_scale)[g] : 1.0f;
     const float f = lsum > 0.0f ? (alpha * vs) / lsum : 0.0f;
     constexpr int DW = PAIR ? D / 2 : D;  // dims this wave writes
-    constexpr int RS = 2 * DW + 16;      // LDS bytes per row
-    static_assert(WAVES * 32 * RS <= (int)prefill_out_lds_bytes(D, WAVES), "out tile fits");
+    constexpr int RS = 2 * DW;           // LDS bytes per row
+    constexpr int PPR = DW / 8;          // 16-byte pieces of a row
+    static_assert(PPR == 16, "the piece order assumes 16 pieces per row");
+    static_assert(WAVES * 32 * RS == (int)prefill_out_lds_bytes(D, WAVES), "out tile size");
     // Every wave has left the last step's LDS reads before any tile is written.
     __syncthreads();
     uint8_t* const tile = lds_raw + wave * 32 * RS;
@@ -802,20 +808,27 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
         h4_t y;
   #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = (_Float16)(o[dt][4 * j + e] * f);
-        *reinterpret_cast<h4_t*>(tile + rr * RS + 2 * (32 * dt + 8 * j + 4 * hh)) = y;
+        *reinterpret_cast<h4_t*>(tile + rr * RS + 16 * ((4 * dt + j) ^ (rr & 15)) + 8 * (hh ^ (rr >> 4))) = y;
       }
     }
-    constexpr int PPR = DW / 8;  // 16-byte pieces of a row
+    // (all of a lane's pieces read first, then stored; row (64 p + lane) / 16
+    // is at least 16 exactly when p >= 4)
+    constexpr int NP = 32 * PPR / 64;
+    u32x4 pv[NP];
   #pragma unroll
-    for (int it = 0; it < 32 * PPR / 64; ++it) {
-      const int idx = 64 * it + lane;
-      const int r = idx / PPR, pc = idx % PPR;
+    for (int p = 0; p < NP; ++p) {
+      const int r = (64 * p + lane) / PPR, pc = lane % PPR;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(tile + r * RS + 16 * (pc ^ (r & 15)));
+      pv[p] = p >= NP / 2 ? u32x4{w[2], w[3], w[0], w[1]} : w;
+    }
+  #pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = (64 * p + lane) / PPR, pc = lane % PPR;
       const int wr = 32 * rg + r;  // the workgroup row
       const int i = i0 + wr / G;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + 16 * pc);
       if (wr < a.rows && i < Qb) {
         const size_t hrow = (size_t)(off + i) * Hq + g * G + (wr - (wr / G) * G);
-        *reinterpret_cast<u32x4*>(a.out + hrow * D + dcol + 8 * pc) = v;
+        *reinterpret_cast<u32x4*>(a.out + hrow * D + dcol + 8 * pc) = pv[p];
       }
     }
   };

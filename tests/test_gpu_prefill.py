@@ -93,6 +93,46 @@ def test_prefill_kernel_on_short_queries_matches_decode(kv):
     assert (a.float() - b.float()).abs().max().item() <= 2 * TOL[kv]
 
 
+def _with_seq_lens(c, lens):
+    """The case with fewer keys per sequence than its block table holds, so
+    that the first new tokens of a sequence may sit at negative positions and
+    see no key."""
+    import dataclasses
+    L = np.array(lens, np.int32)
+    return dataclasses.replace(c, seq_lens=torch.from_numpy(L).to(DEV), seq_lens_host=L)
+
+
+@pytest.mark.parametrize("cus", [1, 3, 8])
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+@pytest.mark.parametrize("shape", ["wide", "narrow", "negative", "window"])
+def test_prefill_many_items_per_workgroup(shape, kv, cus, monkeypatch):
+    """The persistent grid sized for 1, 3 or 8 CUs (PDA_PREFILL_CUS), so that
+    each workgroup takes many (token block, KV head, sequence) items in turn,
+    as on the whole device at full size: items of other sequences and KV heads
+    follow each other, token blocks past a short sequence's new tokens are
+    skipped, some items have one 64-key step, and (negative) some have tokens
+    that all precede the sequence's keys, hence no step at all; 8-wave (wide,
+    negative, window) and 4-wave (narrow) workgroups, fp16 KV (direct loads
+    into LDS) and fp8 (staged through registers). The output equals the
+    oracle's, and bit for bit the output of the grid sized for the device."""
+    if shape == "narrow":
+        # 4-wave workgroups: 4 x 100 new tokens exceed the table's capacity,
+        # and a KV head has 4 x 100 < 512 rows
+        c = _ragged(300 + cus, q_lens=[100, 3, 40, 77], ctx=[20, 0, 90, 30], kv_dtype=kv)
+    else:
+        # 8-wave workgroups: a KV head has 4 x 300 >= 512 rows
+        c = _ragged(310 + cus, q_lens=[300, 1, 17, 130, 64], ctx=[200, 0, 5, 700, 64], kv_dtype=kv,
+                    window=40 if shape == "window" else 0)
+        if shape == "negative":
+            c = _with_seq_lens(c, [150, 1, 10, 830, 20])
+    monkeypatch.delenv("PDA_PREFILL_CUS", raising=False)
+    full = run_gpu(c, num_splits=1)
+    monkeypatch.setenv("PDA_PREFILL_CUS", str(cus))
+    got = run_gpu(c, num_splits=1)
+    assert_parity(got, oracle_full(c), kv, f"prefill {shape} {kv} on {cus} CUs")
+    assert torch.equal(got, full), "the output depends on the grid size"
+
+
 def test_prefill_rejects_splits():
     import paged_split_decode_amd as pda
     c = _ragged(5, q_lens=[100], ctx=[10])

@@ -217,6 +217,38 @@ def test_prefill_pipeline_model_catches_planted_mistakes(mistake):
         assert allowed + per > (n_issued - last_of_s) * per
 
 
+def test_prefill_out_tile_swizzle():
+    """The output tile of a wave: 32 rows of 256 bytes; lane l's 8-byte
+    piece (dims 32 dt + 8 j + 4 hh .. + 3 of row rr = l % 32, hh = l / 32)
+    goes to piece (4 dt + j) ^ (rr % 16) of the row, half hh ^ (rr / 16); the
+    reads take 16-byte piece pc = l % 16 of row r = (64 p + l) / 16 from piece
+    pc ^ (r % 16), halves swapped back when r >= 16 (p >= 4). Every byte is
+    written once, each read returns the 8 dims it names in order, and the
+    writes (32 lanes a pass) and reads (16 a pass) are conflict-free."""
+    RS = 256
+    slot = {}
+    for dt in range(4):
+        for j in range(4):
+            addrs = []
+            for lane in range(64):
+                rr, hh = lane % 32, lane // 32
+                a = rr * RS + 16 * ((4 * dt + j) ^ (rr % 16)) + 8 * (hh ^ (rr // 16))
+                addrs.append(a)
+                assert a not in slot
+                slot[a] = (rr, 32 * dt + 8 * j + 4 * hh)
+            assert conflict_free(addrs, 8, 32)
+    assert sorted(slot) == list(range(0, 32 * RS, 8))
+    for p in range(8):
+        addrs = []
+        for lane in range(64):
+            r, pc = (64 * p + lane) // 16, lane % 16
+            a = r * RS + 16 * (pc ^ (r % 16))
+            addrs.append(a)
+            lo, hi = (a + 8, a) if p >= 4 else (a, a + 8)
+            assert slot[lo] == (r, 8 * pc) and slot[hi] == (r, 8 * pc + 4)
+        assert conflict_free(addrs, 16, 16)
+
+
 # ---- decode kernel: the wave-private V tile and its transposing reads ----
 
 @pytest.mark.parametrize("D", [128, 256])
