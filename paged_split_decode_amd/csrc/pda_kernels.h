@@ -186,11 +186,17 @@ constexpr size_t prefill_out_lds_bytes(int head_dim, int waves) {
 constexpr size_t prefill_xchg_bytes(int head_dim, int waves) {
   return head_dim == 256 && waves == 8 ? (size_t)waves * 64 * 16 * 4 : 0;
 }
+// fp16 KV stages Q through LDS: at D=128 with 8 waves in 64 KB of its own
+// after the three step buffers (160 KB in all; the output tiles go there
+// too), else in step buffer 1.
+constexpr bool prefill_q_own(int head_dim, int kv_kind, int waves) {
+  return kv_kind == kKvF16 && head_dim == 128 && waves == 8 && prefill_buffers(head_dim, kv_kind, waves) == 3;
+}
 constexpr size_t prefill_lds_bytes(int head_dim, int kv_kind, int waves) {
   const size_t steps = (size_t)prefill_buffers(head_dim, kv_kind, waves) * prefill_step_bytes(head_dim) +
                        prefill_xchg_bytes(head_dim, waves);
   const size_t out = prefill_out_lds_bytes(head_dim, waves);
-  return steps > out ? steps : out;
+  return prefill_q_own(head_dim, kv_kind, waves) ? steps + out : (steps > out ? steps : out);
 }
 hipError_t launch_prefill_f16(int head_dim, int waves, dim3 items, int cus, size_t lds, hipStream_t stream,
                               const DecodeArgs& args);

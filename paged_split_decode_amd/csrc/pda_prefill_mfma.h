@@ -99,6 +99,14 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   // Persistent workgroups at D=128 (below); at D=256 one item per workgroup
   // measured faster.
   constexpr bool PERSIST = !PAIR;
+  // Q through LDS (fp16 KV): in 64 KB of its own after the three step
+  // buffers at D=128 with 8 waves (where the output tiles then go too),
+  // else in step buffer 1, which no load reaches before the first step.
+  constexpr bool QLDS = DMA;
+  constexpr bool Q_OWN = QLDS && prefill_q_own(D, KV, WAVES);
+  constexpr int QS_AT = Q_OWN ? NBUF * BUF_BYTES : BUF_BYTES;
+  static_assert(!QLDS || Q_OWN || NBUF == 2, "Q in step buffer 1: only step 0 loads before the first step");
+  static_assert(!QLDS || (PAIR ? WAVES / 2 : WAVES) * 32 * 2 * D <= (Q_OWN ? 65536 : BUF_BYTES), "Q fits");
   const int rg = PAIR ? (wave >> 1) : wave;  // row block
   const int dh = PAIR ? (wave & 1) : 0;      // key half of the scores, output dim half
   // One item (token block, KV head, sequence) per call of `item`, by its
@@ -401,11 +409,38 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     constexpr int NDT = (PAIR ? D / 2 : D) / 32;  // 32-dim output tiles of this wave
     // The Q loads go out before the first steps' cache loads, and Q is first
     // read after the wait for those: the two latencies overlap, and the cache
-    // loads stay the youngest, as the explicit waits below count on. (A lane
-    // without a row reads its token clamped into the sequence, in bounds, and
-    // keeps zeros.)
+    // loads stay the youngest, as the explicit waits below count on. (A row
+    // without a token reads its token clamped into the sequence, in bounds,
+    // and keeps zeros.)
+    //   fp16 KV: Q goes through LDS by direct loads of whole rows (a 1 KB load
+    //   covers 1024 / (2 D) rows, instead of 16-byte pieces of 32 rows, four
+    //   times the cache lines per load); the wave's 32 rows (at D=256, half
+    //   of its pair's 32 rows each) are stored row after row, 16-byte piece c
+    //   of row r at piece c ^ (r % 16), so that the reads of 16 rows' piece c
+    //   (one pass) fall on 16 distinct piece slots. 1-byte KV: Q goes to
+    //   registers directly.
     u32x4 qx[NK];
-    {
+    uint8_t* const qs = lds_raw + QS_AT + rg * 32 * (2 * D);  // this row block's Q rows
+    // (only with a step to wait for: the wait for step 0 covers these loads,
+    // and an item without steps writes its zero rows through the same LDS)
+    if (QLDS && n_steps > 0) {
+      constexpr int RB = 2 * D;          // bytes per row
+      constexpr int RPL = 1024 / RB;     // rows per 1 KB load
+      constexpr int SPR = RB / 16;       // 16-byte pieces per row
+      constexpr int NQL = 8;             // loads per wave
+      static_assert(NQL * RPL == (PAIR ? 16 : 32), "a wave loads its share of its 32 rows");
+      const int r0 = PAIR ? 16 * dh : 0;
+  #pragma unroll
+      for (int k = 0; k < NQL; ++k) {
+        const int r = r0 + k * RPL + lane / SPR;  // row in the row block
+        const int sl = lane % SPR;                 // its piece slot
+        const int wr = 32 * rg + r;                // the workgroup row
+        const int qi = min(i0 + wr / G, Qb - 1);
+        const uint8_t* src = a.q + ((size_t)(off + qi) * Hq + g * G + (wr - (wr / G) * G)) * RB +
+                             16 * (sl ^ (r & 15));
+        lds_load16(src, lds_u32 + (uint32_t)(QS_AT + rg * 32 * RB + (r0 + k * RPL) * RB));
+      }
+    } else if (!QLDS) {
       const uint8_t* qrow =
           a.q + ((size_t)(off + min(my_i, Qb - 1)) * Hq + g * G + (myr - (myr / G) * G)) * (D * 2);
   #pragma unroll
@@ -419,13 +454,25 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       if (n_steps > 0) stage_load(0, IntC<0>{});
     }
     h8_t qb[NK];
+    // After the barrier that follows the wait for the first step (and Q).
     auto q_ready = [&]() __attribute__((always_inline)) {
+      if constexpr (QLDS) {
+  #pragma unroll
+        for (int t = 0; t < NK; ++t)
+          qx[t] = *reinterpret_cast<const u32x4*>(qs + rr * (2 * D) + 16 * ((2 * t + hh) ^ (rr & 15)));
+      }
       const uint32_t keep = my_row ? 0xFFFFFFFFu : 0u;
   #pragma unroll
       for (int t = 0; t < NK; ++t) {
   #pragma unroll
         for (int e = 0; e < 4; ++e) qx[t][e] = (qx[t][e] & keep) ^ qflip;
         qb[t] = __builtin_bit_cast(h8_t, qx[t]);
+      }
+      // Q staged in step buffer 1: every wave has read it before the first
+      // step's loads go there.
+      if constexpr (QLDS && !Q_OWN) {
+        wait_vm(IntC<63>{});
+        barrier();
       }
     };
 
@@ -798,9 +845,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     constexpr int PPR = DW / 8;          // 16-byte pieces of a row
     static_assert(PPR == 16, "the piece order assumes 16 pieces per row");
     static_assert(WAVES * 32 * RS == (int)prefill_out_lds_bytes(D, WAVES), "out tile size");
-    // Every wave has left the last step's LDS reads before any tile is written.
-    __syncthreads();
-    uint8_t* const tile = lds_raw + wave * 32 * RS;
+    // The tiles: in the Q region where it is the wave's own (its Q rows were
+    // read at the start), else over the step buffers, once every wave has
+    // left the last step's LDS reads.
+    if constexpr (!Q_OWN) __syncthreads();
+    uint8_t* const tile = lds_raw + (Q_OWN ? QS_AT : 0) + wave * 32 * RS;
   #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
   #pragma unroll

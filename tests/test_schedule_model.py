@@ -217,6 +217,40 @@ def test_prefill_pipeline_model_catches_planted_mistakes(mistake):
         assert allowed + per > (n_issued - last_of_s) * per
 
 
+@pytest.mark.parametrize("D,pair", [(128, False), (256, True)])
+def test_prefill_q_staging(D, pair):
+    """Q through LDS (fp16 KV): a row block's 32 rows of 2 D bytes, row after
+    row; 1 KB direct load k of a wave (lane l lands at 16 l) covers rows r0 +
+    k * RPL + l / SPR, piece slot l % SPR, and fetches the row's 16-byte piece
+    slot ^ (row % 16) (r0 = 0, or 16 dh for the D=256 pairs, whose two waves
+    load half the rows each). Every piece of every row is staged exactly once,
+    lane (rr = l % 32, hh = l / 32) reads back the B operand of k-step t
+    (row rr, dims 16 t + 8 hh ..) from slot (2 t + hh) ^ (rr % 16), and a
+    16-lane read pass is conflict-free."""
+    RB = 2 * D
+    RPL, SPR = 1024 // RB, RB // 16
+    waves = (0, 1) if pair else (0,)
+    held = {}  # LDS byte offset in the row block -> (row, piece)
+    for dh in waves:
+        r0 = 16 * dh if pair else 0
+        for k in range(8):
+            for lane in range(64):
+                r, sl = r0 + k * RPL + lane // SPR, lane % SPR
+                dst = (r0 + k * RPL) * RB + 16 * lane
+                assert dst == r * RB + 16 * sl
+                assert dst not in held
+                held[dst] = (r, sl ^ (r % 16))
+    assert sorted(held.values()) == [(r, c) for r in range(32) for c in range(SPR)]
+    for t in range(D // 16):
+        addrs = []
+        for lane in range(64):
+            rr, hh = lane % 32, lane // 32
+            a = rr * RB + 16 * ((2 * t + hh) ^ (rr % 16))
+            assert held[a] == (rr, 2 * t + hh)
+            addrs.append(a)
+        assert conflict_free(addrs, 16, 16)
+
+
 def test_prefill_out_tile_swizzle():
     """The output tile of a wave: 32 rows of 256 bytes; lane l's 8-byte
     piece (dims 32 dt + 8 j + 4 hh .. + 3 of row rr = l % 32, hh = l / 32)
