@@ -900,7 +900,9 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       const uint32_t v = (P & 7u) ? blockIdx.x + r * P : 8u * (r * per + ((r & 1u) ? per - 1u - j8 : j8)) + x8;
       if (v >= n_items) break;
       item(slot_item(v, n_items));
-      // (the next item's loads go to LDS that this one's output tile used)
+      // (the next item's first loads go to step buffers 0 and 1, which a
+      // slower wave may still read for this item's last step or, where the
+      // output tiles lie over the step buffers, for its output)
       __syncthreads();
     }
   } else {
