@@ -104,7 +104,7 @@ def _with_seq_lens(c, lens):
 
 @pytest.mark.parametrize("cus", [1, 3, 8])
 @pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
-@pytest.mark.parametrize("shape", ["wide", "narrow", "negative", "window"])
+@pytest.mark.parametrize("shape", ["wide", "narrow", "negative", "window", "negative_d256"])
 def test_prefill_many_items_per_workgroup(shape, kv, cus, monkeypatch):
     """The persistent grid sized for 1, 3 or 8 CUs (PDA_PREFILL_CUS), so that
     each workgroup takes many (token block, KV head, sequence) items in turn,
@@ -113,17 +113,21 @@ def test_prefill_many_items_per_workgroup(shape, kv, cus, monkeypatch):
     skipped, some items have one 64-key step, and (negative) some have tokens
     that all precede the sequence's keys, hence no step at all; 8-wave (wide,
     negative, window) and 4-wave (narrow) workgroups, fp16 KV (direct loads
-    into LDS) and fp8 (staged through registers). The output equals the
-    oracle's, and bit for bit the output of the grid sized for the device."""
+    into LDS) and fp8 (staged through registers). D=256 (one item per
+    workgroup, whatever the CU count) takes the negative case as well. The
+    output equals the oracle's, and bit for bit the output of the grid sized
+    for the device."""
     if shape == "narrow":
         # 4-wave workgroups: 4 x 100 new tokens exceed the table's capacity,
         # and a KV head has 4 x 100 < 512 rows
         c = _ragged(300 + cus, q_lens=[100, 3, 40, 77], ctx=[20, 0, 90, 30], kv_dtype=kv)
     else:
         # 8-wave workgroups: a KV head has 4 x 300 >= 512 rows
+        d256 = shape == "negative_d256"
         c = _ragged(310 + cus, q_lens=[300, 1, 17, 130, 64], ctx=[200, 0, 5, 700, 64], kv_dtype=kv,
-                    window=40 if shape == "window" else 0)
-        if shape == "negative":
+                    window=40 if shape == "window" else 0, head_dim=256 if d256 else 128,
+                    num_q_heads=12 if d256 else 8)
+        if shape.startswith("negative"):
             c = _with_seq_lens(c, [150, 1, 10, 830, 20])
     monkeypatch.delenv("PDA_PREFILL_CUS", raising=False)
     full = run_gpu(c, num_splits=1)
