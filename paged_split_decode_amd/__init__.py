@@ -91,17 +91,21 @@ _SIGNATURES = {
 
 
 def library_path() -> str:
-    return _LIB_PATH
+    """The library this process loads: libpda.so beside this file, or the
+    build the environment variable PDA_LIBRARY names (read at the first
+    load), such as the diagnostic timeline build."""
+    return os.environ.get("PDA_LIBRARY") or _LIB_PATH
 
 
 def load_library() -> ctypes.CDLL:
     """Load libpda.so (once). Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = library_path()
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"{_LIB_PATH} is missing: build it with `python -m paged_split_decode_amd.build`")
-        lib = ctypes.CDLL(_LIB_PATH)
+                f"{path} is missing: build it with `python -m paged_split_decode_amd.build`")
+        lib = ctypes.CDLL(path)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype, fn.argtypes = res, args

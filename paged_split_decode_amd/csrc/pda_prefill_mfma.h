@@ -27,6 +27,17 @@
 
 #include "pda_decode_mfma.h"
 
+// Diagnostic builds only (-DPDA_PREFILL_TIMELINE=1; the library is otherwise
+// unchanged): per item, wave 0 reads the 100 MHz clock at the end of each
+// phase of its start and end, and the shader clock at the item's start and
+// end, waiting for each reading at once (so that its latency is not charged
+// to a later phase), and writes them over the first values of the item's
+// first output row. paged_split_decode_amd/timeline.py builds, runs and reads
+// them.
+#ifndef PDA_PREFILL_TIMELINE
+#define PDA_PREFILL_TIMELINE 0
+#endif
+
 namespace pda {
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
@@ -121,6 +132,20 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     // kept in registers through every item)
     int lane = lane0;
     asm volatile("" : "+v"(lane));
+    // (diagnostic builds: stamp k ends phase k - 1; 0 at the item's start)
+    uint32_t tl[7] = {0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint64_t tl_cycles = 0;
+    auto stamp = [&](int k) __attribute__((always_inline)) {
+      if constexpr (PDA_PREFILL_TIMELINE) {
+        __builtin_amdgcn_sched_barrier(0);
+        tl[k] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+        if (k == 0) tl_cycles = __builtin_amdgcn_s_memtime();
+        if (k == 6) tl_cycles = __builtin_amdgcn_s_memtime() - tl_cycles;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    stamp(0);
     // Item lg -> (token block, KV head, sequence): token block fastest, the
     // blocks with the most keys first.
     int g, b, blk;
@@ -382,6 +407,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       for (int i = lane; i < b; i += 64) sum += a.q_lens[i];
       off = wave_sum_i(sum);
     }
+    stamp(1);
 
     // 32 x 32 x 16 MFMA lane layouts (A: lane l holds row l % 32, k = 8 h + 0..7
     // with h = l / 32; B: column l % 32, same k; C: column l % 32, rows
@@ -453,6 +479,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     } else {
       if (n_steps > 0) stage_load(0, IntC<0>{});
     }
+    stamp(2);
     h8_t qb[NK];
     // After the barrier that follows the wait for the first step (and Q).
     auto q_ready = [&]() __attribute__((always_inline)) {
@@ -766,9 +793,11 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       if (n_steps > 0) {
         // (steps 0 .. NBUF - 2 were issued above; Q loads may follow them)
         wait_step(0, NBUF - 2);
+        stamp(3);
         dma_zero_tail(0, 0);
         wait_vm(IntC<63>{});
         barrier();
+        stamp(4);
         q_ready();
         int buf = 0;
         size_t nb0 = tile_at(NBUF - 1, ta), nb1 = tile_at(NBUF - 1, ta + 1);
@@ -821,6 +850,7 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       }
     }
 
+    stamp(5);
     // Bring o, l to the row maximum, add the two lane halves' l, and write
     // fp16 out (a row that sees no key is 0), one division per row: o times
     // alpha * v_scale / l. Lane l holds dims 32 dt + 8 j + 4 hh .. + 3 of row
@@ -878,6 +908,18 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
       if (wr < a.rows && i < Qb) {
         const size_t hrow = (size_t)(off + i) * Hq + g * G + (wr - (wr / G) * G);
         *reinterpret_cast<u32x4*>(a.out + hrow * D + dcol + 8 * pc) = pv[p];
+      }
+    }
+    stamp(6);
+    if constexpr (PDA_PREFILL_TIMELINE) {
+      // (the item's first row: workgroup row 0, written by wave 0 above)
+      if (wave == 0 && lane == 0) {
+        uint32_t* const tp = reinterpret_cast<uint32_t*>(a.out + ((size_t)(off + i0) * Hq + g * G) * D);
+        for (int k = 0; k < 7; ++k) tp[k] = tl[k];
+        tp[7] = (uint32_t)tl_cycles;
+        tp[8] = (uint32_t)n_steps;
+        tp[9] = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));   // HW_ID: CU, SH, SE
+        tp[10] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));  // XCC_ID
       }
     }
   };
