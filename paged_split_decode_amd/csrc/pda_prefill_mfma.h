@@ -117,7 +117,9 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
   constexpr bool Q_OWN = QLDS && prefill_q_own(D, KV, WAVES);
   constexpr int QS_AT = Q_OWN ? NBUF * BUF_BYTES : BUF_BYTES;
   static_assert(!QLDS || Q_OWN || NBUF == 2, "Q in step buffer 1: only step 0 loads before the first step");
-  static_assert(!QLDS || (PAIR ? WAVES / 2 : WAVES) * 32 * 2 * D <= (Q_OWN ? 65536 : BUF_BYTES), "Q fits");
+  static_assert(!QLDS || (PAIR ? WAVES / 2 : WAVES) * 32 * 2 * D <=
+                             (Q_OWN ? (int)prefill_out_lds_bytes(D, WAVES) : BUF_BYTES),
+                "Q fits its region");
   const int rg = PAIR ? (wave >> 1) : wave;  // row block
   const int dh = PAIR ? (wave & 1) : 0;      // key half of the scores, output dim half
   // One item (token block, KV head, sequence) per call of `item`, by its
@@ -267,9 +269,6 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
           for (int dg = 0; dg < NDV; ++dg) lds_load16(src + 64 * dg, dst + 1024u * dg);
         }
       }
-    };
-    auto dma_step = [&](int step, int buf) __attribute__((always_inline)) {
-      dma_bases(tile_at(step, ta), tile_at(step, ta + 1), buf);
     };
     // After a V wave's loads of a step have landed: V slots of keys at or past
     // the sequence's end hold whatever the page has there (a weight 0 times a
