@@ -12,9 +12,9 @@ hipError_t launch_decode_f16(int head_dim, int rows_per_wave, dim3 grid,
   return launch_kv<kKvF16>(head_dim, rows_per_wave, grid, threads, lds, stream, args);
 }
 
-hipError_t launch_decode_mfma_f16(int head_dim, int row_tiles, dim3 grid, int threads,
-                               size_t lds, hipStream_t stream, const DecodeArgs& args) {
-  return launch_mfma_kv<kKvF16>(head_dim, row_tiles, grid, threads, lds, stream, args);
+hipError_t launch_decode_mfma_f16(int head_dim, int row_tiles, bool stream_kv, dim3 grid,
+                               int threads, size_t lds, hipStream_t stream, const DecodeArgs& args) {
+  return launch_mfma_kv<kKvF16>(head_dim, row_tiles, stream_kv, grid, threads, lds, stream, args);
 }
 
 }  // namespace pda

@@ -160,22 +160,32 @@ __device__ __forceinline__ uint32_t lane_piece_offset(int c) {
   return (uint32_t)(Geom<D, KV>::kLaneBytes == 8 ? 8 * c : 16 * c);
 }
 
+// A global load, non-temporal when NTL (the data is read once: streaming
+// loads then keep it from displacing other lines in the caches).
+template <bool NTL, typename T>
+__device__ __forceinline__ T ld_global(const uint8_t* p) {
+  if constexpr (NTL)
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else
+    return *reinterpret_cast<const T*>(p);
+}
+
 // Load this lane's slice of one key row (K or V); `p` points at its first piece.
-template <int D, int KV, int N>
+template <int D, int KV, int N, bool NTL = false>
 __device__ __forceinline__ void load_slice(uint32_t (&dst)[N], const uint8_t* p) {
   using Gm = Geom<D, KV>;
   static_assert(N == Gm::kRawDwords, "slice size");
   if constexpr (Gm::kLaneBytes == 32) {  // fp16, D=256: two 256-byte halves
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 256);
+    const u32x4 a = ld_global<NTL, u32x4>(p);
+    const u32x4 b = ld_global<NTL, u32x4>(p + 256);
 #pragma unroll
     for (int j = 0; j < 4; ++j) { dst[j] = a[j]; dst[4 + j] = b[j]; }
   } else if constexpr (Gm::kLaneBytes == 16) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 a = ld_global<NTL, u32x4>(p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) dst[j] = a[j];
   } else {  // 1-byte, D=128
-    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 a = ld_global<NTL, u32x2>(p);
     dst[0] = a[0];
     dst[1] = a[1];
   }

@@ -277,7 +277,9 @@ __device__ __forceinline__ BalancedChunk balanced_chunk(const DecodeArgs& a, int
   return r;
 }
 
-template <int D, int KV, int NRT>
+// STREAM: K and V by non-temporal loads (calls whose K and V exceed the
+// last-level cache; see the launcher's caller).
+template <int D, int KV, int NRT, bool STREAM>
 __global__ void __launch_bounds__(256 * mfma_waves_per_simd(D, KV, NRT),
                                   mfma_waves_per_simd(D, KV, NRT))
 pda_decode_mfma_kernel(const DecodeArgs a) {
@@ -484,12 +486,12 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
     const uint8_t* vp = a.v + base;
 #pragma unroll
     for (int t = 0; t < NKL; ++t) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(kp + koff + 64 * t);
+      const u32x4 x = ld_global<STREAM, u32x4>(kp + koff + 64 * t);
 #pragma unroll
       for (int e = 0; e < 4; ++e) kr[t][e] = x[e];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_slice<D, KV>(vr[i], vp + voff[i]);
+    for (int i = 0; i < 4; ++i) load_slice<D, KV, VR, STREAM>(vr[i], vp + voff[i]);
   };
 
   uint32_t kb[NB][NKL][4], vb[NB][4][VR];
@@ -843,18 +845,22 @@ pda_decode_mfma_kernel(const DecodeArgs a) {
 }
 
 template <int KV>
-hipError_t launch_mfma_kv(int head_dim, int row_tiles, dim3 grid, int threads, size_t lds,
+hipError_t launch_mfma_kv(int head_dim, int row_tiles, bool stream_kv, dim3 grid, int threads, size_t lds,
                           hipStream_t stream, const DecodeArgs& args) {
-#define PDA_MCASE(DD, NT)                                                              \
-  if (head_dim == DD && row_tiles == NT) {                                             \
-    hipLaunchKernelGGL((pda_decode_mfma_kernel<DD, KV, NT>), grid, dim3(threads), lds, \
-                       stream, args);                                                  \
-    return hipGetLastError();                                                          \
+#define PDA_MCASE(DD, NT, ST)                                                              \
+  if (head_dim == DD && row_tiles == NT && stream_kv == ST) {                              \
+    hipLaunchKernelGGL((pda_decode_mfma_kernel<DD, KV, NT, ST>), grid, dim3(threads), lds, \
+                       stream, args);                                                      \
+    return hipGetLastError();                                                              \
   }
-  PDA_MCASE(128, 1)
-  PDA_MCASE(128, 2)
-  PDA_MCASE(256, 1)
-  PDA_MCASE(256, 2)
+  PDA_MCASE(128, 1, false)
+  PDA_MCASE(128, 2, false)
+  PDA_MCASE(256, 1, false)
+  PDA_MCASE(256, 2, false)
+  PDA_MCASE(128, 1, true)
+  PDA_MCASE(128, 2, true)
+  PDA_MCASE(256, 1, true)
+  PDA_MCASE(256, 2, true)
 #undef PDA_MCASE
   return hipErrorInvalidValue;
 }

@@ -110,12 +110,13 @@ hipError_t launch_decode_i8(int head_dim, int rows_per_wave, dim3 grid,
                             const DecodeArgs& args);
 
 // Matrix-core (MFMA) decode kernel for (head_dim, kv_kind, row_tiles of 16
-// query rows), grid (num_splits, Hkv, B), `threads` / 64 waves per workgroup.
-hipError_t launch_decode_mfma_f16(int head_dim, int row_tiles, dim3 grid, int threads,
+// query rows), grid (num_splits, Hkv, B), `threads` / 64 waves per workgroup;
+// stream_kv: K and V by non-temporal loads.
+hipError_t launch_decode_mfma_f16(int head_dim, int row_tiles, bool stream_kv, dim3 grid, int threads,
                                   size_t lds, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_mfma_fp8(int head_dim, int row_tiles, dim3 grid, int threads,
+hipError_t launch_decode_mfma_fp8(int head_dim, int row_tiles, bool stream_kv, dim3 grid, int threads,
                                   size_t lds, hipStream_t stream, const DecodeArgs& args);
-hipError_t launch_decode_mfma_i8(int head_dim, int row_tiles, dim3 grid, int threads,
+hipError_t launch_decode_mfma_i8(int head_dim, int row_tiles, bool stream_kv, dim3 grid, int threads,
                                  size_t lds, hipStream_t stream, const DecodeArgs& args);
 // Waves per SIMD the matrix kernel's register allocation leaves room for:
 // two wherever the working set fits in 256 registers (a second wave hides the
