@@ -141,9 +141,12 @@ pda_write_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict
   const int64_t t = (int64_t)blockIdx.x * tokens_per_wg + tt;
   if (tt >= tokens_per_wg || rem >= per_token || t >= num_tokens) return;
   // The row loads do not depend on the slot: they go out with its load.
+  // Rows are read once and cache slots written once, by non-temporal loads
+  // and stores (they then displace no other lines in the caches; 2-6%
+  // faster at 32768 tokens, equal at 64).
   const size_t src = ((size_t)t * num_kv_heads + h) * head_dim + 8 * c;  // elements
-  const u32x4_w kx = *reinterpret_cast<const u32x4_w*>(key + src);
-  const u32x4_w vx = *reinterpret_cast<const u32x4_w*>(value + src);
+  const u32x4_w kx = __builtin_nontemporal_load(reinterpret_cast<const u32x4_w*>(key + src));
+  const u32x4_w vx = __builtin_nontemporal_load(reinterpret_cast<const u32x4_w*>(value + src));
   const int64_t slot = slot_mapping[t];
   float ks = 1.0f, vs = 1.0f;
   if constexpr (KV != kKvF16) {
@@ -158,11 +161,13 @@ pda_write_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict
           : (size_t)slot * num_kv_heads + h;
   const size_t dst = dst_row * head_dim + 8 * c;  // elements
   if constexpr (KV == kKvF16) {
-    *reinterpret_cast<u32x4_w*>(k_cache + 2 * dst) = kx;
-    *reinterpret_cast<u32x4_w*>(v_cache + 2 * dst) = vx;
+    __builtin_nontemporal_store(kx, reinterpret_cast<u32x4_w*>(k_cache + 2 * dst));
+    __builtin_nontemporal_store(vx, reinterpret_cast<u32x4_w*>(v_cache + 2 * dst));
   } else {
-    *reinterpret_cast<u32x2*>(k_cache + dst) = quantize8<KV>(kx, ks, __builtin_amdgcn_rcpf(ks));
-    *reinterpret_cast<u32x2*>(v_cache + dst) = quantize8<KV>(vx, vs, __builtin_amdgcn_rcpf(vs));
+    __builtin_nontemporal_store(quantize8<KV>(kx, ks, __builtin_amdgcn_rcpf(ks)),
+                                reinterpret_cast<u32x2*>(k_cache + dst));
+    __builtin_nontemporal_store(quantize8<KV>(vx, vs, __builtin_amdgcn_rcpf(vs)),
+                                reinterpret_cast<u32x2*>(v_cache + dst));
   }
 }
 
