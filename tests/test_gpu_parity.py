@@ -140,6 +140,32 @@ def test_kv_head_groups(Hkv, D, kv, G, Q, splits):
     assert_parity(run_gpu(c, kernel="matrix"), oracle_full(c), kv, repr(w))
 
 
+@pytest.mark.parametrize("D,kv,G,Q", [(128, "f16", 4, 1), (256, "f16", 6, 1),
+                                      (256, "fp8_e4m3", 4, 2), (128, "int8", 7, 3)])
+@pytest.mark.parametrize("splits", [1, 4, 0])
+def test_streaming_loads_give_the_same_output(D, kv, G, Q, splits):
+    """The matrix kernel streams K and V (non-temporal loads) when the K/V a
+    call can read, judged from the block table's capacity, exceed the
+    last-level cache. The same small case with its table padded by unused
+    columns (never read: past every sequence's pages) takes that variant;
+    both outputs equal the oracle's. (Not bit for bit each other's: the
+    capacity also sets the split and key-wave plan, hence the order of the
+    fp32 sums. No window: a window bounds the keys a call can read whatever
+    the table.)"""
+    import dataclasses
+    w = small(29, head_dim=D, kv_dtype=kv, num_q_heads=G * 2, num_kv_heads=2, q_len=Q,
+              seq_lens=(0, 45, 700, 129), num_splits=splits)
+    c = case_on_gpu(w)
+    elem = 2 if kv == "f16" else 1
+    cols = (256 << 20) // (c.workload.page_size * 4 * 2 * D * elem * 2) + 16  # capacity past the cache
+    bt = torch.zeros((c.block_table.shape[0], cols), dtype=c.block_table.dtype, device=DEV)
+    bt[:, :c.block_table.shape[1]] = c.block_table
+    want = oracle_full(c)
+    assert_parity(run_gpu(c, kernel="matrix"), want, kv, repr(w))
+    assert_parity(run_gpu(dataclasses.replace(c, block_table=bt), kernel="matrix"), want, kv,
+                  f"{w!r}, table of {cols} columns")
+
+
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
 @pytest.mark.parametrize("P", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("D,kv,G,Q,W", [(128, "f16", 4, 1, 0), (256, "fp8_e4m3", 6, 2, 100),
