@@ -176,6 +176,12 @@ typedef struct pda_decode_dims {
  * or a batch as large as one round) the automatic count is
  * pda_decode_resolve_splits's, the same for every sequence. The result does
  * not depend on the split choice beyond fp32 rounding.
+ *
+ * Cache reads: when the K and V bytes a call can touch (every page its block
+ * table can name, or its window) exceed 256 MB, more than MI355X's last-level
+ * cache holds, the matrix kernel reads them with non-temporal loads; below
+ * that, with ordinary loads, so that repeated calls find them in that cache.
+ * The values read, and the result, are the same either way.
  */
 pda_status pda_paged_decode_attention(
     const void* q, const void* k_cache, const void* v_cache,
