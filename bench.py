@@ -323,7 +323,7 @@ def prefill_record(name, case, m):
             "us_per_call": round(us, 2), "per_call_us": m["per_call_us"], "TFLOP_s": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)},
+                         "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic_for(name)},
             "flops": flops, "GB_s": round(m["bytes"] / (us * 1e-6) / 1e9, 1),
             "algorithmic_bytes": m["bytes"]}
 
