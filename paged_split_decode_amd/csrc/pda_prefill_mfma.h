@@ -875,10 +875,16 @@ pda_prefill_mfma_kernel(const DecodeArgs a) {
     static_assert(PPR == 16, "the piece order assumes 16 pieces per row");
     static_assert(WAVES * 32 * RS == (int)prefill_out_lds_bytes(D, WAVES), "out tile size");
     // The tiles: in the Q region where it is the wave's own (its Q rows were
-    // read at the start), else over the step buffers, once every wave has
-    // left the last step's LDS reads.
-    if constexpr (!Q_OWN) __syncthreads();
-    uint8_t* const tile = lds_raw + (Q_OWN ? QS_AT : 0) + wave * 32 * RS;
+    // read at the start). With two step buffers and tiles that fit in one,
+    // in the buffer the last step did not use: no load goes there after the
+    // last step, and every wave read it last before the barrier this wave
+    // passed ahead of the last step (with one step, it held Q, which every
+    // wave read before the barrier after Q), so no barrier is needed. Else
+    // over the step buffers, once every wave has left the last step's reads.
+    constexpr bool FREE_BUF = !Q_OWN && NBUF == 2 && WAVES * 32 * RS <= BUF_BYTES;
+    if constexpr (!Q_OWN && !FREE_BUF) __syncthreads();
+    uint8_t* const tile =
+        lds_raw + (Q_OWN ? QS_AT : FREE_BUF ? (n_steps & 1) * BUF_BYTES : 0) + wave * 32 * RS;
   #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
   #pragma unroll
